@@ -1,0 +1,141 @@
+"""Seeded synthetic inputs for the tensor-parallel MLP shard.
+
+This module only draws numbers: shapes, seeds and value distributions of the
+workloads.  It holds none of the method's arithmetic, so both the GPU path and
+the CPU oracle can be fed from it without sharing any computation.
+
+bf16 inputs are drawn in fp32 and rounded to bf16 (round to nearest even) by
+torch; the GPU receives those bf16 values and the oracle receives the very same
+values widened exactly to fp64.
+
+Workload shapes come from the pages' worked examples:
+  * the Day 41 post's fp32 check (x [4,512], W [512,2048], p = 4, seed 42);
+  * a GPT-style d = 4096, d_ff = 16384 MLP split four ways ("Transformer math:
+    tensor parallel", section "A worked example"; "Building GPT from Scratch,
+    Part 9", section "Splitting the FFN Layer");
+  * Llama 3.1 70B at TP = 8: hidden 8192, feed-forward 28672, 3584 feed-forward
+    columns per GPU ("What is Tensor Parallelism?", section "Worked example:
+    Llama 3.1 70B on 8 GPUs"), with the gated SwiGLU feed-forward ("Tensor
+    Parallelism Explained", section 2.B).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+WEIGHT_STD = 0.02
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int          # tokens
+    d: int          # model width
+    k: int          # full hidden width (d_ff)
+    p: int          # tensor-parallel degree
+    act: str        # "gelu_tanh" or "swiglu"
+    dtype: str      # "f32" or "bf16"
+    bias: bool      # column bias b1 present
+    note: str = ""
+    Ts: tuple = field(default_factory=tuple)  # decode: several token counts
+
+    @property
+    def s(self) -> int:
+        return self.k // self.p
+
+    @property
+    def n_gemm(self) -> int:
+        return 3 if self.act == "swiglu" else 2
+
+    def shard_flops(self, T: int | None = None) -> float:
+        """Algorithmic flops of one shard forward: 2*T*d*(k/p) per GEMM."""
+        T = self.T if T is None else T
+        return 2.0 * T * self.d * self.s * self.n_gemm
+
+
+WORKLOADS = {
+    "tiny_f32_p4": Workload("tiny_f32_p4", 4, 512, 2048, 4, "gelu_tanh", "f32", True,
+                            "Day 41 post fp32 check shape, GeLU(tanh), p=4 simulated"),
+    "gpt_gelu_p4": Workload("gpt_gelu_p4", 2048, 4096, 16384, 4, "gelu_tanh", "bf16", True,
+                            "GPT-style GeLU MLP shard, p=4, zero bias"),
+    "llama70b_prefill_tp8": Workload("llama70b_prefill_tp8", 4096, 8192, 28672, 8, "swiglu",
+                                     "bf16", False, "Llama-70B SwiGLU shard, TP=8, prefill"),
+    "llama70b_decode_tp8": Workload("llama70b_decode_tp8", 64, 8192, 28672, 8, "swiglu", "bf16",
+                                    False, "Llama-70B SwiGLU shard, TP=8, decode",
+                                    Ts=(1, 8, 64)),
+    "llama70b_block_sim_tp8": Workload("llama70b_block_sim_tp8", 512, 8192, 28672, 8, "swiglu",
+                                       "bf16", False,
+                                       "all 8 shards of a TP=8 Llama-70B MLP on one GPU"),
+}
+
+
+def gaussian_f32(shape, seed: int, std: float = 1.0) -> np.ndarray:
+    """N(0, std^2) fp32 array from numpy's default_rng(seed)."""
+    a = np.random.default_rng(seed).standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return a
+
+
+def gaussian_bf16(shape, seed: int, std: float = 1.0):
+    """N(0, std^2) drawn in fp32, rounded to bf16 (RNE) by torch; a CPU torch tensor."""
+    import torch
+
+    return torch.from_numpy(gaussian_f32(shape, seed, std)).to(torch.bfloat16)
+
+
+def tiny_f32_inputs():
+    """The Day 41 post's check: legacy RandomState(42), drawn in the order x, W, b (all
+    N(0,1) fp32), then a down-projection W2 [2048, 512] ~ N(0,1)/sqrt(2048)."""
+    rs = np.random.RandomState(42)
+    X = rs.randn(4, 512).astype(np.float32)
+    W1 = rs.randn(512, 2048).astype(np.float32)
+    b1 = rs.randn(2048).astype(np.float32)
+    W2 = (rs.randn(2048, 512) / np.sqrt(2048.0)).astype(np.float32)
+    return X, W1, b1, W2
+
+
+def gpt_gelu_shard_inputs(T: int = 2048, d: int = 4096, s: int = 4096):
+    """Compact shard of the GPT-style GeLU MLP: X seed 42, W1_i seed 43, W2_i seed 44
+    (bf16), b1_i = 0.  W1_i is [d, s], W2_i is [s, d]."""
+    import torch
+
+    X = gaussian_bf16((T, d), 42)
+    W1 = gaussian_bf16((d, s), 43, WEIGHT_STD)
+    W2 = gaussian_bf16((s, d), 44, WEIGHT_STD)
+    b1 = torch.zeros(s, dtype=torch.bfloat16)
+    return X, W1, b1, W2
+
+
+def llama_shard_weights(d: int = 8192, s: int = 3584):
+    """Compact TP=8 Llama-70B weight shard: W_gate seed 43, W_up seed 44 ([d, s]),
+    W_down seed 45 ([s, d]); bf16 N(0, 0.02^2)."""
+    Wg = gaussian_bf16((d, s), 43, WEIGHT_STD)
+    Wu = gaussian_bf16((d, s), 44, WEIGHT_STD)
+    W2 = gaussian_bf16((s, d), 45, WEIGHT_STD)
+    return Wg, Wu, W2
+
+
+def llama_tokens(T: int, d: int = 8192):
+    """X [T, d] bf16 from seed 42; a smaller T gives the first rows of a larger draw."""
+    return gaussian_bf16((T, d), 42)
+
+
+def llama_full_weights(d: int = 8192, k: int = 28672):
+    """Full (unsharded) Llama-70B MLP weights: Wg, Wu [d, k] seeds 43, 44; W2 [k, d] seed 45."""
+    Wg = gaussian_bf16((d, k), 43, WEIGHT_STD)
+    Wu = gaussian_bf16((d, k), 44, WEIGHT_STD)
+    W2 = gaussian_bf16((k, d), 45, WEIGHT_STD)
+    return Wg, Wu, W2
+
+
+def small_case(T: int, d: int, k: int, seed: int, swiglu: bool, bias: bool, x_std: float = 1.0,
+               w_std: float = WEIGHT_STD):
+    """Generic small bf16 case: X, W1 (gate), Wu (or None), b1 (or None), W2 (full matrices)."""
+    X = gaussian_bf16((T, d), seed, x_std)
+    W1 = gaussian_bf16((d, k), seed + 1, w_std)
+    Wu = gaussian_bf16((d, k), seed + 2, w_std) if swiglu else None
+    b1 = gaussian_bf16((k,), seed + 3, 0.5) if bias else None
+    W2 = gaussian_bf16((k, d), seed + 4, w_std)
+    return X, W1, Wu, b1, W2

@@ -1,0 +1,201 @@
+"""CPU oracle for one tensor-parallel MLP shard -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports it and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain fp64 loops, fp32 instances for the
+Day 41 post's printed fp32 check); this module only builds that file with gcc
+and marshals numpy arrays to it.  See the header of ``oracle.c`` for what each
+function computes and which page passage it follows.
+
+Parity unpinned: nothing here.  Every function is pinned by the CPU tests in
+``tests/test_oracle_pins.py`` (printed value, identities, closed forms,
+brute force with exact rationals, library routines).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# The oracle's own activation numbering (see oracle.c).
+ACT_NONE, ACT_RELU, ACT_GELU_TANH, ACT_GELU_ERF, ACT_SWIGLU = 0, 1, 2, 3, 4
+ACT_SILU = ACT_SWIGLU  # scalar helper: kind 4 is SiLU
+ACT_BY_NAME = {
+    "none": ACT_NONE,
+    "relu": ACT_RELU,
+    "gelu_tanh": ACT_GELU_TANH,
+    "gelu_erf": ACT_GELU_ERF,
+    "swiglu": ACT_SWIGLU,
+}
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-std=c11", "-D_DEFAULT_SOURCE", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        i64, i32, ci = ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+        vp = ctypes.c_void_p
+        lib.oracle_col_shard_f64.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, vp, ci, vp]
+        lib.oracle_row_shard_f64.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp]
+        lib.oracle_partial_sum_f64.argtypes = [i64, i64, i32, vp, vp, vp]
+        lib.oracle_mlp_unsharded_f64.argtypes = [i64, i64, i64, vp, vp, vp, vp, ci, vp, vp, vp]
+        lib.oracle_activation_f64.argtypes = [ci, i64, vp, vp]
+        lib.oracle_activation_f64.restype = None
+        lib.oracle_linear_f32.argtypes = [i64, i64, i64, vp, vp, vp, ci, vp]
+        lib.oracle_col_shard_f32.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, vp, ci, vp]
+        lib.oracle_partial_sum_f32.argtypes = [i64, i64, i32, vp, vp, vp]
+        lib.oracle_num_threads.argtypes = []
+        for name in ("oracle_col_shard_f64", "oracle_row_shard_f64", "oracle_partial_sum_f64",
+                     "oracle_mlp_unsharded_f64", "oracle_linear_f32", "oracle_col_shard_f32",
+                     "oracle_partial_sum_f32", "oracle_num_threads"):
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _c(a, dtype):
+    """Contiguous array of the given dtype (the conversion is exact for bf16/fp32 -> fp64)."""
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _act(act):
+    return ACT_BY_NAME[act] if isinstance(act, str) else int(act)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: invalid shard arguments")
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def col_shard(X, W1, i, p, act, b1=None, Wu=None):
+    """Y_i [T, k/p] in fp64 for shard i of p (W1, Wu are the full [d, k] matrices)."""
+    lib = _load()
+    X, W1, Wu, b1 = _c(X, np.float64), _c(W1, np.float64), _c(Wu, np.float64), _c(b1, np.float64)
+    T, d = X.shape
+    k = W1.shape[1]
+    if k % p:
+        raise ValueError("k not divisible by p")
+    Y = np.empty((T, k // p), dtype=np.float64)
+    _check(lib.oracle_col_shard_f64(T, d, k, i, p, _p(X), _p(W1), _p(Wu), _p(b1), _act(act), _p(Y)),
+           "col_shard")
+    return Y
+
+
+def row_shard(Y, W2, i, p):
+    """Z_i [T, d] in fp64: shard i's hidden slice times its row block of the full W2 [k, d]."""
+    lib = _load()
+    Y, W2 = _c(Y, np.float64), _c(W2, np.float64)
+    k, d = W2.shape
+    T = Y.shape[0]
+    if k % p or Y.shape[1] != k // p:
+        raise ValueError("shape mismatch")
+    Z = np.empty((T, d), dtype=np.float64)
+    _check(lib.oracle_row_shard_f64(T, d, k, i, p, _p(Y), _p(W2), _p(Z)), "row_shard")
+    return Z
+
+
+def partial_sum(parts, b2=None):
+    """Z = ((parts[0] + parts[1]) + ...) (+ b2), fp64; parts is a sequence of [T, d]."""
+    lib = _load()
+    P = _c(np.stack([np.asarray(q) for q in parts]), np.float64)
+    p, T, d = P.shape
+    b2 = _c(b2, np.float64)
+    Z = np.empty((T, d), dtype=np.float64)
+    _check(lib.oracle_partial_sum_f64(T, d, p, _p(P), _p(b2), _p(Z)), "partial_sum")
+    return Z
+
+
+def mlp_unsharded(X, W1, W2, act, b1=None, Wu=None, b2=None):
+    """Z = act(X W1 + b1) W2 + b2 (or SiLU(X Wg) * (X Wu) for swiglu), fp64, computed unsharded."""
+    lib = _load()
+    X, W1, W2 = _c(X, np.float64), _c(W1, np.float64), _c(W2, np.float64)
+    Wu, b1, b2 = _c(Wu, np.float64), _c(b1, np.float64), _c(b2, np.float64)
+    T, d = X.shape
+    k = W1.shape[1]
+    Z = np.empty((T, W2.shape[1]), dtype=np.float64)
+    _check(lib.oracle_mlp_unsharded_f64(T, d, k, _p(X), _p(W1), _p(Wu), _p(b1), _act(act),
+                                        _p(W2), _p(b2), _p(Z)), "mlp_unsharded")
+    return Z
+
+
+def mlp_shard(X, W1, W2, i, p, act, b1=None, Wu=None):
+    """(Y_i, Z_i) for shard i of p, fp64 (column step, then row step)."""
+    Y = col_shard(X, W1, i, p, act, b1=b1, Wu=Wu)
+    return Y, row_shard(Y, W2, i, p)
+
+
+def activation(act, x):
+    """Element-wise activation in fp64 (kind 'swiglu' / 4 means SiLU here)."""
+    lib = _load()
+    x = _c(x, np.float64)
+    y = np.empty_like(x)
+    lib.oracle_activation_f64(_act(act), x.size, _p(x), _p(y))
+    return y
+
+
+def linear_f32(X, W, b=None, act="none"):
+    """fp32 unsharded X W + b (then act), summed in fp32 with the index ascending."""
+    lib = _load()
+    X, W, b = _c(X, np.float32), _c(W, np.float32), _c(b, np.float32)
+    T, d = X.shape
+    k = W.shape[1]
+    Y = np.empty((T, k), dtype=np.float32)
+    _check(lib.oracle_linear_f32(T, d, k, _p(X), _p(W), _p(b), _act(act), _p(Y)), "linear_f32")
+    return Y
+
+
+def col_shard_f32(X, W1, i, p, act="none", b1=None, Wu=None):
+    """fp32 column step of shard i of p."""
+    lib = _load()
+    X, W1, Wu, b1 = _c(X, np.float32), _c(W1, np.float32), _c(Wu, np.float32), _c(b1, np.float32)
+    T, d = X.shape
+    k = W1.shape[1]
+    if k % p:
+        raise ValueError("k not divisible by p")
+    Y = np.empty((T, k // p), dtype=np.float32)
+    _check(lib.oracle_col_shard_f32(T, d, k, i, p, _p(X), _p(W1), _p(Wu), _p(b1), _act(act), _p(Y)),
+           "col_shard_f32")
+    return Y
+
+
+def partial_sum_f32(parts, b2=None):
+    """fp32 Z = ((parts[0] + parts[1]) + ...) (+ b2)."""
+    lib = _load()
+    P = _c(np.stack([np.asarray(q) for q in parts]), np.float32)
+    p, T, d = P.shape
+    b2 = _c(b2, np.float32)
+    Z = np.empty((T, d), dtype=np.float32)
+    _check(lib.oracle_partial_sum_f32(T, d, p, _p(P), _p(b2), _p(Z)), "partial_sum_f32")
+    return Z

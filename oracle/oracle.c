@@ -1,0 +1,317 @@
+/*
+ * CPU oracle for one tensor-parallel MLP shard.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain reference that the
+ * GPU library is checked against.  Only the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg may load it.  It shares no code, header,
+ * table or helper with the HIP library, and it includes nothing from it.
+ *
+ * What it computes (the plain definition, written out):
+ *
+ *   Shard i of p owns the contiguous block of s = k/p hidden units starting
+ *   at c0 = i*s.
+ *     - Column-parallel linear: each shard multiplies the full, replicated
+ *       input X [T,d] by its own column block of A [d,k] and keeps a [T,s]
+ *       slice of the hidden activation ("Transformer math: tensor parallel",
+ *       section "Column-parallel: split the weight by output columns";
+ *       "Tensor Parallelism Explained", section 1.A).  The column bias is cut
+ *       the same way as the columns (Day 41 post, "Simulating column parallel
+ *       linear").
+ *     - The activation is element-wise, so it is applied to the shard alone
+ *       ("Transformer math: tensor parallel", section "The MLP block: column
+ *       then row, one all-reduce").  For the gated variant both the gate and
+ *       the up projection are column-split the same way and the shard forms
+ *       Swish(gate) times up ("Tensor Parallelism Explained", section 2.B).
+ *     - Row-parallel linear: the shard multiplies its hidden slice by its row
+ *       block of B [k,d] and gets a full-shape [T,d] partial ("Transformer
+ *       math: tensor parallel", section "Row-parallel: split the weight by
+ *       input rows").
+ *     - The reduction adds the p partials element by element, shard 0 first,
+ *       then adds the row bias once (Day 41 post, "Simulating row parallel
+ *       linear").
+ *
+ * Every dot product is summed with its index ascending, in the precision of
+ * the function (fp64, or fp32 for the *_f32 functions that pin the printed
+ * fp32 result of the Day 41 post).  There is no blocking, no reordering and
+ * no intermediate rounding.  Rows of the output are spread over OpenMP
+ * threads; that does not change any sum.  Build with -ffp-contract=off so
+ * that a multiply followed by an add is never fused into one rounding.
+ *
+ * Activations follow their published definitions; the pages only name them:
+ *   GeLU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+ *                    (Hendrycks and Gimpel, 2016)
+ *   GeLU, erf form:  0.5 x (1 + erf(x / sqrt 2))
+ *   SiLU (Swish with beta = 1): x / (1 + exp(-x))
+ *   ReLU: max(0, x)  (Day 41 post, "Pairing them: the Megatron-LM MLP")
+ * They call the host C library (tanh, erf, exp).
+ *
+ * Matrices are dense row-major with no padding.  All pointers are host
+ * memory owned by the caller.  Functions return 0, or -1 on an argument that
+ * breaks the shard rule (k not divisible by p, i outside [0,p)).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Activation kinds understood by this oracle (its own numbering). */
+#define OR_ACT_NONE 0
+#define OR_ACT_RELU 1
+#define OR_ACT_GELU_TANH 2
+#define OR_ACT_GELU_ERF 3
+#define OR_ACT_SWIGLU 4 /* column step: SiLU(gate) * up; scalar helper: SiLU */
+
+static double act_scalar_f64(int kind, double x) {
+  switch (kind) {
+    case OR_ACT_NONE:
+      return x;
+    case OR_ACT_RELU:
+      return x > 0.0 ? x : 0.0;
+    case OR_ACT_GELU_TANH: {
+      const double c = sqrt(2.0 / M_PI);
+      return 0.5 * x * (1.0 + tanh(c * (x + 0.044715 * x * x * x)));
+    }
+    case OR_ACT_GELU_ERF:
+      return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));
+    case OR_ACT_SWIGLU:
+      return x / (1.0 + exp(-x));
+  }
+  return NAN;
+}
+
+static float act_scalar_f32(int kind, float x) {
+  switch (kind) {
+    case OR_ACT_NONE:
+      return x;
+    case OR_ACT_RELU:
+      return x > 0.0f ? x : 0.0f;
+    case OR_ACT_GELU_TANH: {
+      const float c = (float)sqrt(2.0 / M_PI);
+      return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
+    }
+    case OR_ACT_GELU_ERF:
+      return 0.5f * x * (1.0f + erff(x / sqrtf(2.0f)));
+    case OR_ACT_SWIGLU:
+      return x / (1.0f + expf(-x));
+  }
+  return NAN;
+}
+
+static int shard_ok(int64_t k, int32_t i, int32_t p) {
+  return p >= 1 && i >= 0 && i < p && k % p == 0;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* y[n] = act(x[n]) for the scalar activations (kind 4 is SiLU here). */
+void oracle_activation_f64(int kind, int64_t n, const double *x, double *y) {
+  for (int64_t e = 0; e < n; ++e) y[e] = act_scalar_f64(kind, x[e]);
+}
+
+/*
+ * Column-parallel step of shard i of p, fp64.
+ *   X  [T,d]; W1 [d,k] (the full matrix, the gate for SwiGLU); Wu [d,k] (up,
+ *   SwiGLU only, else NULL); b1 [k] or NULL (not used with SwiGLU).
+ *   Y  [T,k/p] receives act(X W1[:, c0:c0+s] + b1[c0:c0+s]), or
+ *   SiLU(X Wg[:, c0:c0+s]) * (X Wu[:, c0:c0+s]).
+ */
+int oracle_col_shard_f64(int64_t T, int64_t d, int64_t k, int32_t i, int32_t p,
+                         const double *X, const double *W1, const double *Wu,
+                         const double *b1, int act, double *Y) {
+  if (!shard_ok(k, i, p)) return -1;
+  if (act == OR_ACT_SWIGLU && Wu == NULL) return -1;
+  const int64_t s = k / p, c0 = (int64_t)i * s;
+#pragma omp parallel
+  {
+    double *u = (double *)malloc(sizeof(double) * (size_t)(s > 0 ? s : 1));
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      double *h = Y + t * s;
+      for (int64_t j = 0; j < s; ++j) h[j] = 0.0;
+      for (int64_t j = 0; j < s; ++j) u[j] = 0.0;
+      for (int64_t c = 0; c < d; ++c) {
+        const double xv = X[t * d + c];
+        const double *w = W1 + c * k + c0;
+        for (int64_t j = 0; j < s; ++j) h[j] += xv * w[j];
+        if (act == OR_ACT_SWIGLU) {
+          const double *wu = Wu + c * k + c0;
+          for (int64_t j = 0; j < s; ++j) u[j] += xv * wu[j];
+        }
+      }
+      if (act == OR_ACT_SWIGLU) {
+        for (int64_t j = 0; j < s; ++j) h[j] = act_scalar_f64(OR_ACT_SWIGLU, h[j]) * u[j];
+      } else {
+        for (int64_t j = 0; j < s; ++j) {
+          const double v = b1 ? h[j] + b1[c0 + j] : h[j];
+          h[j] = act_scalar_f64(act, v);
+        }
+      }
+    }
+    free(u);
+  }
+  return 0;
+}
+
+/*
+ * Row-parallel step of shard i of p, fp64.
+ *   Y [T,k/p] (this shard's hidden slice); W2 [k,d] (the full matrix).
+ *   Z [T,d] receives Y W2[c0:c0+s, :], the shard's partial (no bias).
+ */
+int oracle_row_shard_f64(int64_t T, int64_t d, int64_t k, int32_t i, int32_t p,
+                         const double *Y, const double *W2, double *Z) {
+  if (!shard_ok(k, i, p)) return -1;
+  const int64_t s = k / p, c0 = (int64_t)i * s;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double *z = Z + t * d;
+    for (int64_t n = 0; n < d; ++n) z[n] = 0.0;
+    for (int64_t j = 0; j < s; ++j) {
+      const double yv = Y[t * s + j];
+      const double *w = W2 + (c0 + j) * d;
+      for (int64_t n = 0; n < d; ++n) z[n] += yv * w[n];
+    }
+  }
+  return 0;
+}
+
+/*
+ * The reduction that replaces the all-reduce, fp64:
+ *   Z = ((parts[0] + parts[1]) + ...) + parts[p-1], then + b2 (if given).
+ *   parts is p consecutive [T,d] blocks.
+ */
+int oracle_partial_sum_f64(int64_t T, int64_t d, int32_t p, const double *parts,
+                           const double *b2, double *Z) {
+  if (p < 1) return -1;
+  const int64_t n = T * d;
+#pragma omp parallel for schedule(static)
+  for (int64_t e = 0; e < n; ++e) {
+    double acc = parts[e];
+    for (int32_t q = 1; q < p; ++q) acc += parts[(int64_t)q * n + e];
+    if (b2) acc += b2[e % d];
+    Z[e] = acc;
+  }
+  return 0;
+}
+
+/*
+ * The unsharded MLP, fp64, written directly from its definition (it does not
+ * call the shard functions): H = X W1 (+ b1), Y = act(H) (or SiLU(X Wg) *
+ * (X Wu)), Z = Y W2 (+ b2).  X [T,d], W1 and Wu [d,k], W2 [k,d], Z [T,d].
+ */
+int oracle_mlp_unsharded_f64(int64_t T, int64_t d, int64_t k, const double *X,
+                             const double *W1, const double *Wu, const double *b1,
+                             int act, const double *W2, const double *b2, double *Z) {
+  if (act == OR_ACT_SWIGLU && Wu == NULL) return -1;
+#pragma omp parallel
+  {
+    double *h = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+    double *u = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      for (int64_t j = 0; j < k; ++j) h[j] = 0.0;
+      for (int64_t j = 0; j < k; ++j) u[j] = 0.0;
+      for (int64_t c = 0; c < d; ++c) {
+        const double xv = X[t * d + c];
+        for (int64_t j = 0; j < k; ++j) h[j] += xv * W1[c * k + j];
+        if (act == OR_ACT_SWIGLU)
+          for (int64_t j = 0; j < k; ++j) u[j] += xv * Wu[c * k + j];
+      }
+      for (int64_t j = 0; j < k; ++j) {
+        if (act == OR_ACT_SWIGLU)
+          h[j] = act_scalar_f64(OR_ACT_SWIGLU, h[j]) * u[j];
+        else
+          h[j] = act_scalar_f64(act, b1 ? h[j] + b1[j] : h[j]);
+      }
+      double *z = Z + t * d;
+      for (int64_t n = 0; n < d; ++n) z[n] = 0.0;
+      for (int64_t j = 0; j < k; ++j) {
+        const double yv = h[j];
+        for (int64_t n = 0; n < d; ++n) z[n] += yv * W2[j * d + n];
+      }
+      if (b2)
+        for (int64_t n = 0; n < d; ++n) z[n] += b2[n];
+    }
+    free(h);
+    free(u);
+  }
+  return 0;
+}
+
+/* ---- fp32 instances: the Day 41 post prints its check in fp32 ---------- */
+
+/* Full (unsharded) fp32 linear: Y [T,k] = act(X W + b). */
+int oracle_linear_f32(int64_t T, int64_t d, int64_t k, const float *X, const float *W,
+                      const float *b, int act, float *Y) {
+  if (act == OR_ACT_SWIGLU) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    float *h = Y + t * k;
+    for (int64_t j = 0; j < k; ++j) h[j] = 0.0f;
+    for (int64_t c = 0; c < d; ++c) {
+      const float xv = X[t * d + c];
+      for (int64_t j = 0; j < k; ++j) h[j] += xv * W[c * k + j];
+    }
+    for (int64_t j = 0; j < k; ++j) h[j] = act_scalar_f32(act, b ? h[j] + b[j] : h[j]);
+  }
+  return 0;
+}
+
+/* fp32 column-parallel step of shard i of p (same contract as the fp64 one). */
+int oracle_col_shard_f32(int64_t T, int64_t d, int64_t k, int32_t i, int32_t p,
+                         const float *X, const float *W1, const float *Wu,
+                         const float *b1, int act, float *Y) {
+  if (!shard_ok(k, i, p)) return -1;
+  if (act == OR_ACT_SWIGLU && Wu == NULL) return -1;
+  const int64_t s = k / p, c0 = (int64_t)i * s;
+#pragma omp parallel
+  {
+    float *u = (float *)malloc(sizeof(float) * (size_t)(s > 0 ? s : 1));
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      float *h = Y + t * s;
+      for (int64_t j = 0; j < s; ++j) h[j] = 0.0f;
+      for (int64_t j = 0; j < s; ++j) u[j] = 0.0f;
+      for (int64_t c = 0; c < d; ++c) {
+        const float xv = X[t * d + c];
+        const float *w = W1 + c * k + c0;
+        for (int64_t j = 0; j < s; ++j) h[j] += xv * w[j];
+        if (act == OR_ACT_SWIGLU) {
+          const float *wu = Wu + c * k + c0;
+          for (int64_t j = 0; j < s; ++j) u[j] += xv * wu[j];
+        }
+      }
+      if (act == OR_ACT_SWIGLU) {
+        for (int64_t j = 0; j < s; ++j) h[j] = act_scalar_f32(OR_ACT_SWIGLU, h[j]) * u[j];
+      } else {
+        for (int64_t j = 0; j < s; ++j)
+          h[j] = act_scalar_f32(act, b1 ? h[j] + b1[c0 + j] : h[j]);
+      }
+    }
+    free(u);
+  }
+  return 0;
+}
+
+/* fp32 reduction of p partials, shard 0 first, then + b2 (if given). */
+int oracle_partial_sum_f32(int64_t T, int64_t d, int32_t p, const float *parts,
+                           const float *b2, float *Z) {
+  if (p < 1) return -1;
+  const int64_t n = T * d;
+#pragma omp parallel for schedule(static)
+  for (int64_t e = 0; e < n; ++e) {
+    float acc = parts[e];
+    for (int32_t q = 1; q < p; ++q) acc += parts[(int64_t)q * n + e];
+    if (b2) acc += b2[e % d];
+    Z[e] = acc;
+  }
+  return 0;
+}

@@ -1,0 +1,357 @@
+"""Pins of the CPU oracle to what the pages and the mathematics fix.
+
+None of these tests re-types the oracle's formulas: each compares it with a
+value the pages print, an identity, a closed form, a special case, brute force
+with exact rationals, or an independent library routine.
+"""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from megatron_tensor_mlp_amd import synth
+
+
+def rel_fro(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+# ---------------------------------------------------------------- P-1 --------
+def test_day41_printed_concat_error_fp32(golden):
+    """Day 41 post, 'Simulating column parallel linear': concatenating the column
+    shards reproduces x @ W + b with a printed max error of 0.00e+00 (fp32)."""
+    g = golden("day41_column_concat.txt")
+    assert g["dtype"] == "float32"
+    rs = np.random.RandomState(int(g["seed"]))
+    T, d, k, p = (int(g[n]) for n in ("batch", "in_features", "out_features", "num_gpus"))
+    x = rs.randn(T, d).astype(np.float32)
+    W = rs.randn(d, k).astype(np.float32)
+    b = rs.randn(k).astype(np.float32)
+    full = oracle.linear_f32(x, W, b)
+    shards = [oracle.col_shard_f32(x, W, i, p, "none", b1=b) for i in range(p)]
+    concat = np.concatenate(shards, axis=1)
+    assert concat.shape == full.shape == (T, k)
+    max_err = float(np.max(np.abs(full - concat)))
+    assert max_err == float(g["max_error"]) == 0.0
+    # the same holds after a local element-wise activation
+    for act in ("gelu_tanh", "gelu_erf", "relu"):
+        full_a = oracle.linear_f32(x, W, b, act)
+        cat_a = np.concatenate([oracle.col_shard_f32(x, W, i, p, act, b1=b) for i in range(p)], 1)
+        assert np.array_equal(full_a, cat_a)
+    # and the fp32 result is a genuine fp32 matmul (not something else that is
+    # trivially equal): it agrees with fp64 numpy to fp32 rounding
+    ref = x.astype(np.float64) @ W.astype(np.float64) + b
+    assert rel_fro(full, ref) < 1e-6
+
+
+def test_tiny_workload_generator_matches_day41_draw():
+    """The tiny fp32 workload draws x, W, b exactly as the Day 41 post does."""
+    X, W1, b1, W2 = synth.tiny_f32_inputs()
+    rs = np.random.RandomState(42)
+    assert np.array_equal(X, rs.randn(4, 512).astype(np.float32))
+    assert np.array_equal(W1, rs.randn(512, 2048).astype(np.float32))
+    assert np.array_equal(b1, rs.randn(2048).astype(np.float32))
+    assert W2.shape == (2048, 512) and W2.dtype == np.float32
+    assert 0.8 / math.sqrt(2048) < W2.std() < 1.2 / math.sqrt(2048)
+
+
+def test_fp64_concat_bit_exact_all_acts():
+    """Column concat equals the unsharded column step bit-for-bit in fp64 too."""
+    X, W1, b1, W2 = synth.tiny_f32_inputs()
+    for act in ("none", "relu", "gelu_tanh", "gelu_erf"):
+        full = oracle.col_shard(X, W1, 0, 1, act, b1=b1)
+        cat = np.concatenate([oracle.col_shard(X, W1, i, 4, act, b1=b1) for i in range(4)], 1)
+        assert np.array_equal(full, cat), act
+    Wu = synth.gaussian_f32((512, 2048), 7)
+    full = oracle.col_shard(X, W1, 0, 1, "swiglu", Wu=Wu)
+    cat = np.concatenate([oracle.col_shard(X, W1, i, 4, "swiglu", Wu=Wu) for i in range(4)], 1)
+    assert np.array_equal(full, cat)
+
+
+# ---------------------------------------------------------------- P-2 --------
+@pytest.mark.parametrize("act", ["gelu_tanh", "gelu_erf", "relu", "swiglu"])
+@pytest.mark.parametrize("p", [1, 2, 4, 8])
+def test_sum_of_row_partials_equals_unsharded(act, p):
+    """'Transformer math: tensor parallel', row-parallel and MLP sections: the p
+    partial outputs sum to the unsharded MLP output (up to reassociation)."""
+    T, d, k = 5, 24, 64
+    X, W1, Wu, b1, W2 = (None if a is None else a.to(torch.float64).numpy()
+                         for a in synth.small_case(T, d, k, 11, act == "swiglu",
+                                                   act != "swiglu", w_std=0.3))
+    b2 = synth.gaussian_f32((d,), 99).astype(np.float64)
+    parts = [oracle.mlp_shard(X, W1, W2, i, p, act, b1=b1, Wu=Wu)[1] for i in range(p)]
+    Z = oracle.partial_sum(parts, b2)
+    Zfull = oracle.mlp_unsharded(X, W1, W2, act, b1=b1, Wu=Wu, b2=b2)
+    assert rel_fro(Z, Zfull) <= 1e-12
+
+
+# ---------------------------------------------------------------- P-3 --------
+@pytest.mark.parametrize("p", [1, 3, 4])
+def test_linear_closed_form(p):
+    """'Tensor Parallelism Explained', section 1.B: with no activation the
+    reduced result is X (W W'), a closed form computed here with numpy."""
+    rng = np.random.default_rng(5)
+    T, d, k = 6, 20, 36
+    X = rng.standard_normal((T, d))
+    W1 = rng.standard_normal((d, k))
+    W2 = rng.standard_normal((k, d))
+    parts = [oracle.mlp_shard(X, W1, W2, i, p, "none")[1] for i in range(p)]
+    closed = X @ (W1 @ W2)
+    assert rel_fro(oracle.partial_sum(parts), closed) <= 1e-12
+    assert rel_fro(oracle.mlp_unsharded(X, W1, W2, "none"), closed) <= 1e-12
+
+
+# ---------------------------------------------------------------- P-4 --------
+@pytest.mark.parametrize("act", ["gelu_tanh", "relu", "swiglu", "gelu_erf"])
+def test_p1_is_bit_identical_to_unsharded(act):
+    """'Building GPT from Scratch, Part 9', section 'Running This On Your
+    MacBook?': TP=1 is the original model.  One shard of one is bit-identical."""
+    X, W1, Wu, b1, W2 = (None if a is None else a.to(torch.float64).numpy()
+                         for a in synth.small_case(7, 40, 48, 3, act == "swiglu", act != "swiglu"))
+    b2 = np.linspace(-1, 1, 40)
+    Y, Zi = oracle.mlp_shard(X, W1, W2, 0, 1, act, b1=b1, Wu=Wu)
+    Z = oracle.partial_sum([Zi], b2)
+    assert np.array_equal(Z, oracle.mlp_unsharded(X, W1, W2, act, b1=b1, Wu=Wu, b2=b2))
+
+
+# ---------------------------------------------------------------- P-5 --------
+def test_negative_control_activation_on_partial_sums():
+    """'Transformer math: tensor parallel', MLP section: putting the nonlinearity
+    on partial sums (splitting the first weight by rows) is wrong, while with no
+    nonlinearity the two orders agree.  The oracle must show both."""
+    rng = np.random.default_rng(1)
+    T, d, k = 8, 32, 16
+    X = rng.standard_normal((T, d))
+    W = rng.standard_normal((d, k)) / math.sqrt(d)
+    h = d // 2
+    for act, should_match in (("none", True), ("gelu_tanh", False), ("gelu_erf", False)):
+        right = oracle.col_shard(X, W, 0, 1, act)
+        wrong = (oracle.col_shard(X[:, :h], W[:h], 0, 1, act)
+                 + oracle.col_shard(X[:, h:], W[h:], 0, 1, act))
+        err = rel_fro(wrong, right)
+        if should_match:
+            assert err <= 1e-12
+        else:
+            assert err > 0.1, (act, err)
+
+
+# ---------------------------------------------------------------- P-6 --------
+def _brute_force(X, W1, b1, W2, b2, p, relu):
+    """Exact rational evaluation of the sharded MLP straight from the block
+    formulas: Y_i = act(X A_i + b_i), Z = sum_i Y_i B_i + b2."""
+    T, d = len(X), len(X[0])
+    k = len(W1[0])
+    s = k // p
+    Z = [[Fraction(0)] * len(W2[0]) for _ in range(T)]
+    for i in range(p):
+        for t in range(T):
+            y = []
+            for j in range(s):
+                v = sum((Fraction(X[t][c]) * Fraction(W1[c][i * s + j]) for c in range(d)),
+                        Fraction(0)) + Fraction(b1[i * s + j])
+                y.append(max(v, Fraction(0)) if relu else v)
+            for n in range(len(W2[0])):
+                Z[t][n] += sum((y[j] * Fraction(W2[i * s + j][n]) for j in range(s)), Fraction(0))
+    return [[Z[t][n] + Fraction(b2[n]) for n in range(len(W2[0]))] for t in range(T)]
+
+
+@pytest.mark.parametrize("T,d,s,p", [(1, 1, 1, 1), (2, 3, 1, 4), (3, 5, 3, 2), (3, 4, 2, 3),
+                                     (2, 5, 3, 4), (1, 2, 3, 1)])
+@pytest.mark.parametrize("relu", [False, True])
+def test_brute_force_exact_rationals(T, d, s, p, relu):
+    """Brute force on tiny shapes with small integers: the oracle is exact."""
+    rng = np.random.default_rng(T * 100 + d * 10 + s + p)
+    k = s * p
+    X = rng.integers(-4, 5, (T, d)).astype(np.float64)
+    W1 = rng.integers(-3, 4, (d, k)).astype(np.float64)
+    b1 = rng.integers(-5, 6, (k,)).astype(np.float64)
+    W2 = rng.integers(-3, 4, (k, d)).astype(np.float64)
+    b2 = rng.integers(-5, 6, (d,)).astype(np.float64)
+    act = "relu" if relu else "none"
+    expect = _brute_force(X.tolist(), W1.tolist(), b1.tolist(), W2.tolist(), b2.tolist(), p, relu)
+    parts = [oracle.mlp_shard(X, W1, W2, i, p, act, b1=b1)[1] for i in range(p)]
+    got = oracle.partial_sum(parts, b2)
+    assert [[Fraction(v) for v in row] for row in got.tolist()] == expect
+    got_u = oracle.mlp_unsharded(X, W1, W2, act, b1=b1, b2=b2)
+    assert [[Fraction(v) for v in row] for row in got_u.tolist()] == expect
+
+
+def test_brute_force_swiglu_small():
+    """SwiGLU ('Tensor Parallelism Explained', section 2.B): Swish(X Wg_i) times
+    (X Wu_i), evaluated here term by term with Python's math.exp."""
+    rng = np.random.default_rng(8)
+    T, d, k, p = 2, 3, 4, 2
+    X = rng.integers(-3, 4, (T, d)).astype(np.float64)
+    Wg = rng.integers(-2, 3, (d, k)).astype(np.float64)
+    Wu = rng.integers(-2, 3, (d, k)).astype(np.float64)
+    W2 = rng.integers(-2, 3, (k, d)).astype(np.float64)
+    s = k // p
+    for i in range(p):
+        Y, Zi = oracle.mlp_shard(X, Wg, W2, i, p, "swiglu", Wu=Wu)
+        for t in range(T):
+            for j in range(s):
+                g = sum(X[t][c] * Wg[c][i * s + j] for c in range(d))
+                u = sum(X[t][c] * Wu[c][i * s + j] for c in range(d))
+                assert Y[t][j] == pytest.approx(g / (1 + math.exp(-g)) * u, rel=1e-14, abs=1e-14)
+
+
+# ---------------------------------------------------------------- P-7 --------
+def test_matmul_against_numpy():
+    rng = np.random.default_rng(2)
+    T, d, k, p = 9, 70, 96, 4
+    X = rng.standard_normal((T, d))
+    W1 = rng.standard_normal((d, k))
+    W2 = rng.standard_normal((k, d))
+    s = k // p
+    for i in range(p):
+        Y = oracle.col_shard(X, W1, i, p, "none")
+        assert rel_fro(Y, X @ W1[:, i * s:(i + 1) * s]) <= 1e-13
+        Z = oracle.row_shard(Y, W2, i, p)
+        assert rel_fro(Z, Y @ W2[i * s:(i + 1) * s, :]) <= 1e-13
+
+
+GRID = np.array([0.0, 1e-8, -1e-8, 1.0, -1.0, 3.0, -3.0, 10.0, -10.0, 30.0, -30.0, 0.5, -0.5,
+                 2.25, -7.75, 1e-3, -1e-3])
+
+
+def test_activations_against_library_routines():
+    x = np.concatenate([GRID, np.linspace(-12, 12, 1001)])
+    xt = torch.from_numpy(x)
+    ref_tanh = torch.nn.functional.gelu(xt, approximate="tanh").numpy()
+    ref_erf = torch.nn.functional.gelu(xt, approximate="none").numpy()
+    ref_silu = torch.nn.functional.silu(xt).numpy()
+    np.testing.assert_allclose(oracle.activation("gelu_tanh", x), ref_tanh, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(oracle.activation("gelu_erf", x), ref_erf, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(oracle.activation("swiglu", x), ref_silu, rtol=1e-13, atol=1e-15)
+    assert np.array_equal(oracle.activation("relu", x), np.maximum(x, 0.0))
+    assert np.array_equal(oracle.activation("none", x), x)
+    # scalar spot checks against Python's math module
+    for v in GRID:
+        assert oracle.activation("gelu_erf", np.array([v]))[0] == pytest.approx(
+            0.5 * v * math.erfc(-v / math.sqrt(2)), rel=1e-13, abs=1e-15)
+        assert oracle.activation("swiglu", np.array([v]))[0] == pytest.approx(
+            v * 0.5 * (1 + math.tanh(v / 2)), rel=1e-13, abs=1e-15)
+
+
+def test_activation_odd_part_identities():
+    """act(x) - act(-x) = x for both GeLU forms and SiLU (each is x times a
+    function F with F(x) + F(-x) = 1); GeLU(0) = SiLU(0) = 0; large |x| limits."""
+    x = np.linspace(-9, 9, 721)
+    for act in ("gelu_tanh", "gelu_erf", "swiglu"):
+        y, ym = oracle.activation(act, x), oracle.activation(act, -x)
+        np.testing.assert_allclose(y - ym, x, rtol=1e-13, atol=1e-14)
+        assert oracle.activation(act, np.array([0.0]))[0] == 0.0
+        big = oracle.activation(act, np.array([40.0, -40.0]))
+        assert big[0] == pytest.approx(40.0, rel=1e-12) and abs(big[1]) < 1e-12
+
+
+# ---------------------------------------------------------------- P-8 --------
+def one_hot_case(T, d, k, seed):
+    """Integer one-hot weights: W1 column g has a single +-1 at row (7g+3) mod d,
+    W2 row g has a single +-1 at column (5g+1) mod d; X small integers."""
+    rng = np.random.default_rng(seed)
+    X = rng.integers(-256, 257, (T, d)).astype(np.float64)
+    W1 = np.zeros((d, k))
+    W2 = np.zeros((k, d))
+    sg1 = rng.choice([-1.0, 1.0], k)
+    sg2 = rng.choice([-1.0, 1.0], k)
+    for g in range(k):
+        W1[(7 * g + 3) % d, g] = sg1[g]
+        W2[g, (5 * g + 1) % d] = sg2[g]
+    b1 = rng.integers(-8, 9, (k,)).astype(np.float64)
+    return X, W1, W2, b1, sg1, sg2
+
+
+@pytest.mark.parametrize("p", [1, 2, 4, 8])
+def test_bookkeeping_one_hot(p):
+    """Day 41 post: shard i owns columns [i*s, (i+1)*s) of the first weight and
+    the same rows of the second.  With one-hot integer weights every output is a
+    known integer, so an off-by-shard or transposed index fails exactly."""
+    T, d, k = 5, 24, 64
+    X, W1, W2, b1, sg1, sg2 = one_hot_case(T, d, k, p)
+    s = k // p
+    for i in range(p):
+        Y, Zi = oracle.mlp_shard(X, W1, W2, i, p, "relu", b1=b1)
+        expY = np.zeros((T, s))
+        for j in range(s):
+            g = i * s + j
+            expY[:, j] = np.maximum(sg1[g] * X[:, (7 * g + 3) % d] + b1[g], 0)
+        assert np.array_equal(Y, expY)
+        expZ = np.zeros((T, d))
+        for j in range(s):
+            g = i * s + j
+            expZ[:, (5 * g + 1) % d] += sg2[g] * expY[:, j]
+        assert np.array_equal(Zi, expZ)
+
+
+def test_shard_rule_errors():
+    """The shard rule: k must be divisible by p, 0 <= i < p ('Tensor Parallelism
+    Explained', section 4: a non-dividing degree fails at startup)."""
+    X = np.zeros((2, 4))
+    W = np.zeros((4, 10))
+    with pytest.raises(ValueError):
+        oracle.col_shard(X, W, 0, 4, "none")
+    with pytest.raises(ValueError):
+        oracle.col_shard(X, W, 2, 2, "none")
+    with pytest.raises(ValueError):
+        oracle.col_shard(X, W, -1, 2, "none")
+
+
+def test_llama_shard_width(golden):
+    """'What is Tensor Parallelism?', Llama 3.1 70B worked example: 28672 / 8 = 3584
+    feed-forward columns per GPU; the oracle's shard of a [d, 28672] weight has
+    that many columns and its partial has the full [T, 8192] shape."""
+    g = golden("llama70b_tp8_shapes.txt")
+    k, p, s = int(g["ffn_size"]), int(g["tp"]), int(g["ffn_columns_per_gpu"])
+    d = 8
+    X = np.ones((1, d))
+    W1 = np.zeros((d, k))
+    Y = oracle.col_shard(X, W1, p - 1, p, "none")
+    assert Y.shape == (1, s)
+    hidden = int(g["hidden_size"])
+    W2 = np.zeros((k, hidden))
+    Z = oracle.row_shard(Y, W2, p - 1, p)
+    assert Z.shape == (1, hidden)
+    tokens = int(g["prompt_tokens"])
+    assert tokens * hidden * 2 == pytest.approx(float(g["allreduce_tensor_bytes_bf16"]), rel=1e-3)
+    assert hidden * 2 == pytest.approx(float(g["decode_tensor_bytes_bf16"]), rel=0.05)
+
+
+def test_gpt_ffn_shard_shapes(golden):
+    """'Transformer math: tensor parallel', worked example: four [4096, 4096]
+    column shards of a [4096, 16384] weight; a [4096, 4096] partial of 33.5 MB."""
+    g = golden("gpt_ffn_p4_shapes.txt")
+    d, dff, p = int(g["d"]), int(g["d_ff"]), int(g["p"])
+    assert (d, dff // p) == (int(g["column_shard_rows"]), int(g["column_shard_cols"]))
+    assert (dff // p, d) == (int(g["row_shard_rows"]), int(g["row_shard_cols"]))
+    assert int(g["tokens"]) * d * 2 == pytest.approx(float(g["partial_bytes_16bit"]), rel=2e-3)
+    # the oracle's shards of a (narrow) [8, 16384] weight have 4096 columns
+    Y = oracle.col_shard(np.ones((1, 8)), np.zeros((8, dff)), 3, p, "none")
+    assert Y.shape == (1, dff // p)
+
+
+# ---------------------------------------------------------------- P-9 --------
+def test_bf16_inputs_round_trip_exactly():
+    """Inputs are rounded to bf16 once (RNE); widening them to fp64 for the
+    oracle is exact, and the RNE ties go to even."""
+    a = synth.gaussian_bf16((1000,), 3)
+    assert torch.equal(a.to(torch.float64).to(torch.bfloat16), a)
+    ties = torch.tensor([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8)],
+                        dtype=torch.float32).to(torch.bfloat16).to(torch.float64)
+    assert ties.tolist() == [1.0, 1.0 + 2.0 ** -6, -1.0]
+
+
+def test_partial_sum_order_fp32():
+    """fp32 reduction adds shard 0 first, then 1, ...; the order is observable."""
+    parts = [np.array([[1e8]], np.float32), np.array([[1.0]], np.float32),
+             np.array([[-1e8]], np.float32)]
+    assert oracle.partial_sum_f32(parts)[0, 0] == np.float32(0.0)  # (1e8 + 1) - 1e8 in fp32
+    parts2 = [parts[0], parts[2], parts[1]]
+    assert oracle.partial_sum_f32(parts2)[0, 0] == np.float32(1.0)
+    b2 = np.array([0.5], np.float32)
+    assert oracle.partial_sum_f32(parts2, b2)[0, 0] == np.float32(1.5)
