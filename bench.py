@@ -1,0 +1,292 @@
+"""Benchmark of one MI355X's tensor-parallel MLP shard.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+
+A step is one forward of one GPU's shard of the Llama-70B SwiGLU MLP at TP = 8
+(T = 4096 tokens, d = 8192, k/p = 3584): the column step (X Wg_i, X Wu_i,
+SiLU(g) * u -> bf16 Y_i) then the row step (Y_i W2_i -> fp32 partial Z_i),
+i.e. the two launches tp_mlp_shard makes, issued one by one so HIP events can
+bracket each kernel on the stream it runs on.  Inputs are seeded synthetic
+bf16 tensors already resident in HBM.
+
+Prints ONE JSON line.  `value` is the step's algorithmic TFLOP/s (2*T*d*(k/p)
+flops per GEMM, three GEMMs).  Secondary fields report the few-token (decode)
+shard in GB/s of weights streamed, the on-device partial sum in GB/s, the
+simulated TP = 8 block and the GPT-style GeLU shard.  `roofline` covers the
+dominant kernel (the SwiGLU column GEMM), `cpu_baseline` the CPU oracle timed
+on a bounded row sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("MLP-shard TFLOP/s & % bf16 MFMA peak (prefill); GB/s & % HBM peak (decode)")
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+TILED_SOURCES = ["megatron_tensor_mlp_amd/csrc/gemm_tiled.hip",
+                 "megatron_tensor_mlp_amd/csrc/device_common.hpp",
+                 "megatron_tensor_mlp_amd/csrc/kernels.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel_tag):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(PROFILES, f"{kernel_tag}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    h = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or not h or h.group(1) != source_hash(TILED_SOURCES):
+        return None
+    return float(m.group(1))
+
+
+def time_events(torch, fn_list, steps, warmup):
+    """Run `steps` iterations of the launches in fn_list (after `warmup`), with
+    an event before and after each launch on the current stream.  Returns
+    (total seconds, per-launch mean seconds list)."""
+    for _ in range(warmup):
+        for fn in fn_list:
+            fn()
+    torch.cuda.synchronize()
+    n = len(fn_list)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for j in range(steps):
+        evs[j][0].record()
+        for q, fn in enumerate(fn_list):
+            fn()
+            evs[j][q + 1].record()
+    end.record()
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end) / 1e3
+    per = [sum(evs[j][q].elapsed_time(evs[j][q + 1]) for j in range(steps)) / steps / 1e3
+           for q in range(n)]
+    return total, per
+
+
+def headline(torch, tp, synth, steps, warmup):
+    W = synth.WORKLOADS["llama70b_prefill_tp8"]
+    dev = "cuda:0"
+    Wg, Wu, W2 = (t.to(dev) for t in synth.llama_shard_weights(W.d, W.s))
+    X = synth.llama_tokens(W.T, W.d).to(dev)
+    Y = torch.empty(W.T, W.s, dtype=torch.bfloat16, device=dev)
+    Z = torch.empty(W.T, W.d, dtype=torch.float32, device=dev)
+    col = lambda: tp.tp_col_linear(X, Wg, 0, 1, Y, act="swiglu", Wu=Wu)  # noqa: E731
+    row = lambda: tp.tp_row_linear(Y, W2, 0, 1, Z)  # noqa: E731
+    total, (t_col, t_row) = time_events(torch, [col, row], steps, warmup)
+    flops_col = 2.0 * W.T * W.d * W.s * 2
+    flops_row = 2.0 * W.T * W.d * W.s
+    return dict(W=W, total=total, t_col=t_col, t_row=t_row, flops_col=flops_col,
+                flops_row=flops_row, step_flops=flops_col + flops_row)
+
+
+def decode_bench(torch, tp, synth, steps, warmup, copies=3):
+    """Few-token shard; weights rotate over `copies` copies (>= 528 MB) so the
+    256 MB Infinity Cache cannot hold them."""
+    W = synth.WORKLOADS["llama70b_decode_tp8"]
+    dev = "cuda:0"
+    base = [t.to(dev) for t in synth.llama_shard_weights(W.d, W.s)]
+    sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+    out = {}
+    wbytes = sum(t.numel() * t.element_size() for t in base)
+    for T in W.Ts:
+        X = synth.llama_tokens(T, W.d).to(dev)
+        Y = torch.empty(T, W.s, dtype=torch.bfloat16, device=dev)
+        Z = torch.empty(T, W.d, dtype=torch.float32, device=dev)
+        ws = tp.workspace(tp.tp_workspace_bytes(torch.bfloat16, "swiglu", T, W.d, W.s, 1), dev)
+        fns = []
+        for (Wg, Wu, W2) in sets:
+            fns.append(lambda Wg=Wg, Wu=Wu: tp.tp_col_linear(X, Wg, 0, 1, Y, act="swiglu", Wu=Wu,
+                                                              ws=ws))
+            fns.append(lambda W2=W2: tp.tp_row_linear(Y, W2, 0, 1, Z, ws=ws))
+        reps = max(1, steps)
+        total, per = time_events(torch, fns, reps, warmup)
+        step = total / (reps * copies)
+        alg_bytes = wbytes + T * W.d * 2 + 2 * T * W.s * 2 + T * W.d * 4
+        t_col = sum(per[0::2]) / copies
+        t_row = sum(per[1::2]) / copies
+        out[f"T{T}"] = {
+            "us_per_step": round(step * 1e6, 2),
+            "GBps": round(alg_bytes / step / 1e9, 1),
+            "frac_hbm": round(alg_bytes / step / 1e9 / PEAK_HBM_GBS, 4),
+            "col_us": round(t_col * 1e6, 2), "row_us": round(t_row * 1e6, 2),
+            "col_GBps": round((2 * W.d * W.s * 2) / t_col / 1e9, 1),
+            "row_GBps": round((W.s * W.d * 2) / t_row / 1e9, 1),
+        }
+    out["weight_bytes"] = wbytes
+    out["rotation_copies"] = copies
+    return out
+
+
+def partial_sum_bench(torch, tp, steps, warmup, copies=3):
+    """C5's reduction: 8 fp32 [512, 8192] partials -> Z, rotating over copies."""
+    dev = "cuda:0"
+    p, T, d = 8, 512, 8192
+    bufs = [torch.randn(p, T, d, device=dev) for _ in range(copies)]
+    Zs = [torch.empty(T, d, device=dev) for _ in range(copies)]
+    fns = [lambda b=b, z=z: tp.tp_partial_sum([b[q] for q in range(p)], z) for b, z in
+           zip(bufs, Zs)]
+    total, per = time_events(torch, fns, max(1, steps), warmup)
+    t = sum(per) / copies
+    nbytes = (p + 1) * T * d * 4
+    return {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+            "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4), "bytes": nbytes,
+            "rotation_copies": copies}
+
+
+def simulated_block_bench(torch, tp, synth, steps, warmup):
+    W = synth.WORKLOADS["llama70b_block_sim_tp8"]
+    dev = "cuda:0"
+    Wg, Wu, W2 = (t.to(dev) for t in synth.llama_full_weights(W.d, W.k))
+    X = synth.llama_tokens(W.T, W.d).to(dev)
+    Y = torch.empty(W.p, W.T, W.s, dtype=torch.bfloat16, device=dev)
+    Zp = torch.empty(W.p, W.T, W.d, device=dev)
+    Z = torch.empty(W.T, W.d, device=dev)
+    fn = lambda: tp.tp_mlp_simulated(X, Wg, W2, W.p, Y, Zp, Z, act="swiglu", Wu=Wu)  # noqa: E731
+    total, (t,) = time_events(torch, [fn], max(1, steps), warmup)
+    flops = 2.0 * W.T * W.d * W.k * 3
+    return {"us": round(t * 1e6, 1), "TFLOPs": round(flops / t / 1e12, 1),
+            "frac_mfma": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def gpt_bench(torch, tp, synth, steps, warmup):
+    W = synth.WORKLOADS["gpt_gelu_p4"]
+    dev = "cuda:0"
+    X, W1, b1, W2 = (t.to(dev) for t in synth.gpt_gelu_shard_inputs(W.T, W.d, W.s))
+    Y = torch.empty(W.T, W.s, dtype=torch.bfloat16, device=dev)
+    Z = torch.empty(W.T, W.d, device=dev)
+    col = lambda: tp.tp_col_linear(X, W1, 0, 1, Y, act="gelu_tanh", b1=b1)  # noqa: E731
+    row = lambda: tp.tp_row_linear(Y, W2, 0, 1, Z)  # noqa: E731
+    total, (tc, tr) = time_events(torch, [col, row], max(1, steps), warmup)
+    flops = 2.0 * W.T * W.d * W.s * 2
+    t = tc + tr
+    return {"us": round(t * 1e6, 1), "TFLOPs": round(flops / t / 1e12, 1),
+            "frac_mfma": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "col_us": round(tc * 1e6, 1), "row_us": round(tr * 1e6, 1)}
+
+
+def cpu_baseline(synth, target_s=12.0):
+    """The CPU oracle, untuned, on a bounded sample of the headline workload:
+    the first R token rows of one shard forward (rows are independent)."""
+    import oracle
+    import numpy as np
+    import torch
+
+    W = synth.WORKLOADS["llama70b_prefill_tp8"]
+    Wg, Wu, W2 = synth.llama_shard_weights(W.d, W.s)
+    f = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+    Wg, Wu, W2 = f(Wg), f(Wu), f(W2)
+    X = f(synth.llama_tokens(W.T, W.d))
+    threads = oracle.num_threads()
+    # calibrate on one row per thread, then size the sample to ~target_s
+    r0 = max(1, threads)
+    t0 = time.perf_counter()
+    oracle.mlp_shard(X[:r0], Wg, W2, 0, 1, "swiglu", Wu=Wu)
+    dt0 = time.perf_counter() - t0
+    rows = int(min(W.T, max(r0, r0 * target_s / max(dt0, 1e-6))))
+    rows = max(threads, rows - rows % threads)
+    t0 = time.perf_counter()
+    oracle.mlp_shard(X[:rows], Wg, W2, 0, 1, "swiglu", Wu=Wu)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * W.d * W.s * 3
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {rows} of {W.T} token rows of one llama70b_prefill_tp8 shard "
+                      f"forward (fp64 loops), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="headline only")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's shard; runs on more than one GPU are not part of "
+              "this build (the cross-GPU reduction is out of scope).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import megatron_tensor_mlp_amd as tp
+    from megatron_tensor_mlp_amd import synth
+
+    tp.library()
+    log("bench: headline llama70b_prefill_tp8")
+    h = headline(torch, tp, synth, args.steps, args.warmup)
+    W = h["W"]
+    ms = h["total"] / args.steps * 1e3
+    value = h["step_flops"] * args.steps / h["total"] / 1e12
+    achieved = h["flops_col"] / h["t_col"] / 1e12
+    traffic = recorded_traffic("gemm_bf16_tiled_swiglu_llama70b_prefill_tp8")
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": W.name, "T": W.T, "d": W.d, "k": W.k, "p": W.p, "k_per_shard": W.s,
+                   "act": W.act, "frac_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "gemm_bf16_tiled_kernel<EPI_SWIGLU>",
+                     "kernel_us": round(h["t_col"] * 1e6, 2),
+                     "flops_per_launch": h["flops_col"]},
+        "row_gemm": {"us": round(h["t_row"] * 1e6, 2),
+                     "TFLOPs": round(h["flops_row"] / h["t_row"] / 1e12, 2)},
+    }
+    if not args.quick:
+        log("bench: decode")
+        result["decode"] = decode_bench(torch, tp, synth, max(5, args.steps // 2), 3)
+        log("bench: partial sum")
+        result["partial_sum"] = partial_sum_bench(torch, tp, max(5, args.steps), 3)
+        log("bench: simulated block")
+        result["simulated_block"] = simulated_block_bench(torch, tp, synth, max(3, args.steps // 4),
+                                                          2)
+        log("bench: gpt gelu shard")
+        result["gpt_gelu_shard"] = gpt_bench(torch, tp, synth, max(5, args.steps // 2), 3)
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(synth)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

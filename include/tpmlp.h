@@ -1,0 +1,199 @@
+/*
+ * tpmlp.h -- C ABI of one GPU's shard of a tensor-parallel transformer MLP,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (Megatron-style tensor parallelism of the feed-forward block):
+ *   Y_i = act(X A_i + b1_i)           column-parallel linear, local activation
+ *   Z_i = Y_i B_i                     row-parallel linear, full-shape partial
+ *   Z   = Z_0 + Z_1 + ... + Z_{p-1}   the reduction (an all-reduce across GPUs;
+ *                                     here an on-device sum of p partials)
+ * with X [T,d] replicated on every shard, A = W1 [d,k] split by columns,
+ * B = W2 [k,d] split by rows, and shard i of p owning hidden units
+ * [i*k/p, (i+1)*k/p).  Sources: "Transformer math: tensor parallel"
+ * (aicassindra.com), sections "Column-parallel: split the weight by output
+ * columns", "Row-parallel: split the weight by input rows" and "The MLP block:
+ * column then row, one all-reduce"; "Tensor Parallelism Explained"
+ * (initnode.dev), section 1 (equations for Y_i, Z_i and Z) and section 2.B (the
+ * SwiGLU variant); the Day 41 post (skandtandon.pages.dev), sections
+ * "Simulating column parallel linear", "Simulating row parallel linear" and
+ * "Pairing them: the Megatron-LM MLP".
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major; a leading dimension (ld*) is the distance in
+ *     elements between consecutive rows and must be >= the row width.
+ *   - Weights are passed as the FULL logical matrices plus (i, p); the library
+ *     takes the shard's column block of W1/Wu/b1 and row block of W2 itself.
+ *     A GPU that stores only its compact shard passes it with k = k/p, i = 0,
+ *     p = 1 (a column block of a [d,k] matrix is itself a [d,k/p] matrix).
+ *   - i is 0-based, 0 <= i < p, 1 <= p <= 64, and k must be divisible by p
+ *     ("Tensor Parallelism Explained", section 4: a degree that does not divide
+ *     the sharded dimension is a startup error).
+ *   - Element types: TP_BF16 means bf16 X, weights, bias and hidden Y with fp32
+ *     accumulation; TP_F32 means fp32 throughout.  Partials Z_i and the reduced
+ *     Z are always fp32.
+ *   - Alignment: every data pointer must be 16-byte aligned, and d, k/p and
+ *     every leading dimension must be a multiple of 8 elements (bf16) or
+ *     4 elements (fp32); otherwise TP_ERR_MISALIGNED.
+ *   - T = 0 is valid and launches nothing.
+ *   - Memory: all tensors are device memory owned by the caller.  The library
+ *     allocates nothing and keeps no pointer after a call returns.  Some shapes
+ *     need a caller-provided workspace (see tp_workspace_bytes).
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued on it and the call returns without waiting; inputs must stay
+ *     alive, and outputs must not be read, until the stream reaches the work.
+ *   - Errors: arguments are checked on the host before anything is launched.
+ *     On any status other than TP_OK nothing was launched and no output was
+ *     touched; tp_last_error_message() gives a detail string (per thread).
+ *     TP_ERR_HIP means a launch failed; faults during execution surface at the
+ *     caller's next synchronisation of the stream.
+ *   - Calls on different streams that share a workspace buffer race.
+ */
+#ifndef TPMLP_H
+#define TPMLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TPMLP_ABI_VERSION 1
+#define TP_MAX_SHARDS 64
+
+typedef enum {
+  TP_OK = 0,
+  TP_ERR_NULL_POINTER = 1, /* a required pointer is NULL                         */
+  TP_ERR_BAD_SHAPE = 2,    /* T < 0, d < 1, k < 1, or an ld below the row width  */
+  TP_ERR_NOT_DIVISIBLE = 3,/* k % p != 0                                          */
+  TP_ERR_BAD_SHARD = 4,    /* i outside [0,p), p < 1 or p > TP_MAX_SHARDS         */
+  TP_ERR_MISALIGNED = 5,   /* pointer not 16-byte aligned or width/ld not a
+                              multiple of 8 (bf16) / 4 (fp32) elements            */
+  TP_ERR_BAD_DTYPE = 6,    /* unknown tp_dtype                                    */
+  TP_ERR_BAD_ACT = 7,      /* unknown tp_act, or a bias given with TP_ACT_SWIGLU  */
+  TP_ERR_WORKSPACE = 8,    /* workspace missing or smaller than required          */
+  TP_ERR_HIP = 9           /* a HIP launch failed                                 */
+} tp_status;
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* Local activation of the column step.  GeLU is named by every page without a
+ * formula; both published forms are offered: tanh form 0.5x(1+tanh(sqrt(2/pi)
+ * (x+0.044715x^3))) and erf form 0.5x(1+erf(x/sqrt2)).  ReLU is the Day 41
+ * post's simplification.  TP_ACT_SWIGLU is Swish(X Wg_i) * (X Wu_i) with the
+ * Swish slope 1, i.e. SiLU(x) = x/(1+exp(-x)) ("Tensor Parallelism Explained",
+ * section 2.B); W1 is then the gate matrix and Wu the up matrix. */
+typedef enum {
+  TP_ACT_NONE = 0,
+  TP_ACT_RELU = 1,
+  TP_ACT_GELU_TANH = 2,
+  TP_ACT_GELU_ERF = 3,
+  TP_ACT_SWIGLU = 4
+} tp_act;
+
+/*
+ * Column-parallel step of shard i of p (the first linear of the MLP plus its
+ * local activation).  With s = k/p and c0 = i*s:
+ *   Y[t, j] = act( sum_c X[t,c] * W1[c, c0+j]  +  b1[c0+j] )        (0 <= j < s)
+ * or, for TP_ACT_SWIGLU,
+ *   Y[t, j] = SiLU( sum_c X[t,c] * W1[c, c0+j] ) * ( sum_c X[t,c] * Wu[c, c0+j] )
+ * Source: "Transformer math: tensor parallel", section "Column-parallel: split
+ * the weight by output columns" (Y_i = X A_i); the bias slice follows the Day
+ * 41 post, "Simulating column parallel linear".
+ *   X  [T, d], ldx     input, dtype dt (replicated on every shard)
+ *   W1 [d, k], ldw1    full first weight (gate for SwiGLU), dtype dt
+ *   Wu [d, k], ldwu    full up weight, SwiGLU only (else NULL, ldwu ignored)
+ *   b1 [k] or NULL     full column bias, dtype dt; must be NULL for SwiGLU
+ *   Y  [T, s], ldy     output hidden shard, dtype dt, overwritten
+ * fp32 accumulation; the activation is applied in fp32 and Y is rounded once
+ * (to nearest even) to dt.
+ */
+tp_status tp_col_linear(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t i,
+                        int32_t p, const void *X, int64_t ldx, const void *W1, int64_t ldw1,
+                        const void *Wu, int64_t ldwu, const void *b1, void *Y, int64_t ldy,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Row-parallel step of shard i of p (the second linear, without its bias):
+ *   Z[t, n] = sum_j Y[t, j] * W2[c0+j, n]                         (0 <= n < d)
+ * Source: "Transformer math: tensor parallel", section "Row-parallel: split
+ * the weight by input rows" (Z_i = Y_i B_i, a full-shape partial); "Tensor
+ * Parallelism Explained", section 1.B.
+ *   Y  [T, s], ldy     hidden shard, dtype dt
+ *   W2 [k, d], ldw2    full second weight, dtype dt
+ *   Z  [T, d], ldz     fp32 partial, overwritten; the row bias is NOT added
+ *                      here (it is added once after the reduction)
+ */
+tp_status tp_row_linear(tp_dtype dt, int64_t T, int64_t d, int64_t k, int32_t i, int32_t p,
+                        const void *Y, int64_t ldy, const void *W2, int64_t ldw2, float *Z,
+                        int64_t ldz, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The whole shard: tp_col_linear into the caller's Y, then tp_row_linear from
+ * it into Z, on one stream.  Y is an output too (the hidden shard, written once
+ * in dt).  Source: "Transformer math: tensor parallel", section "The MLP block:
+ * column then row, one all-reduce"; Day 41 post, "Pairing them: the
+ * Megatron-LM MLP".
+ */
+tp_status tp_mlp_shard(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t i,
+                       int32_t p, const void *X, int64_t ldx, const void *W1, int64_t ldw1,
+                       const void *Wu, int64_t ldwu, const void *b1, const void *W2,
+                       int64_t ldw2, void *Y, int64_t ldy, float *Z, int64_t ldz, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/*
+ * The reduction of p partials (what the all-reduce computes), on one device:
+ *   Z = ((parts[0] + parts[1]) + ...) + parts[p-1]   (+ b2, added once)
+ * in fp32, element by element, shard 0 first.  Source: Day 41 post,
+ * "Simulating row parallel linear" (sum of the partials, then the bias);
+ * "Building GPT from Scratch, Part 9", "Implementation Sketch" (the row bias is
+ * added after the all-reduce).
+ *   parts  HOST array of p device pointers, each to an fp32 [T, d] matrix
+ *          with leading dimension ldp
+ *   b2     fp32 [d] or NULL
+ *   Z      fp32 [T, d], ldz, overwritten.  Z may be exactly parts[0] (in
+ *          place); any other overlap with an input is undefined.
+ */
+tp_status tp_partial_sum(int64_t T, int64_t d, int32_t p, const float *const *parts, int64_t ldp,
+                         const float *b2, float *Z, int64_t ldz, void *stream);
+
+/*
+ * Simulated-p mode: all p shards of the MLP on this one device, then the
+ * on-device reduction.  Equivalent to tp_mlp_shard for i = 0..p-1 followed by
+ * tp_partial_sum, but the shards of each step run as one grouped launch.
+ * It lets one GPU check the identity sum_i Z_i = act(X W1) W2 ("Tensor
+ * Parallelism Explained", section 1.B, the equation for Z).
+ *   Y      p consecutive [T, k/p] blocks (dense), dtype dt: Y_0, Y_1, ...
+ *   Zp     p consecutive fp32 [T, d] blocks (dense): the partials Z_0, ...
+ *   b2     fp32 [d] or NULL (added once, after the sum)
+ *   Z      fp32 [T, d], ldz: the reduced output
+ */
+tp_status tp_mlp_simulated(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t p,
+                           const void *X, int64_t ldx, const void *W1, int64_t ldw1,
+                           const void *Wu, int64_t ldwu, const void *b1, const void *W2,
+                           int64_t ldw2, const float *b2, void *Y, float *Zp, float *Z,
+                           int64_t ldz, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Bytes of workspace that tp_col_linear / tp_row_linear / tp_mlp_shard /
+ * tp_mlp_simulated need for these sizes (0 if none).  The workspace holds
+ * split-K partial sums and arrival counters of the few-token (T <= 64) path.
+ * It must be zero-filled before its first use; every call leaves its counters
+ * zero again, so one zeroed buffer can be reused by any later call on the same
+ * stream.  Returns 0 for invalid arguments.
+ */
+size_t tp_workspace_bytes(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t p);
+
+/* Shard bookkeeping on the host: shard i of p of a dimension of size k owns
+ * [*c0, *c0 + *s) with s = k/p and c0 = i*s (Day 41 post, "Simulating column
+ * parallel linear").  No GPU is touched. */
+tp_status tp_shard_bounds(int64_t k, int32_t i, int32_t p, int64_t *c0, int64_t *s);
+
+const char *tp_status_string(tp_status s);
+const char *tp_last_error_message(void); /* detail of this thread's last non-OK status */
+int32_t tp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TPMLP_H */

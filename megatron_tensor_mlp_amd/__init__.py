@@ -1,0 +1,33 @@
+"""MI355X-native tensor-parallel MLP shard (column-parallel linear + local
+GeLU/SwiGLU, row-parallel linear to an fp32 partial, on-device partial sum).
+
+This package is a thin ctypes binding over ``libtpmlp.so`` (declared in
+``include/tpmlp.h``): it turns torch tensors into pointers, sizes and leading
+dimensions, and the current torch stream into a ``hipStream_t``.  Every step of
+the computation runs in the library's HIP kernels; if the library is missing,
+every call raises.  torch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+from ._binding import (  # noqa: F401
+    ACT,
+    DTYPE,
+    TpError,
+    library,
+    library_path,
+    tp_abi_version,
+    tp_col_linear,
+    tp_mlp_shard,
+    tp_mlp_simulated,
+    tp_partial_sum,
+    tp_row_linear,
+    tp_shard_bounds,
+    tp_workspace_bytes,
+    workspace,
+)
+
+__all__ = [
+    "ACT", "DTYPE", "TpError", "library", "library_path", "tp_abi_version", "tp_col_linear",
+    "tp_mlp_shard", "tp_mlp_simulated", "tp_partial_sum", "tp_row_linear", "tp_shard_bounds",
+    "tp_workspace_bytes", "workspace",
+]

@@ -1,0 +1,253 @@
+"""ctypes binding of libtpmlp (argument marshalling only).
+
+Each ``tp_*`` function here has the name of the C entry point it calls.  It
+reads sizes and leading dimensions off the torch tensors, checks that the
+buffers are large enough for those sizes (the C library cannot see buffer
+extents), and passes raw device pointers plus the current torch HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded before libtpmlp so the process uses one HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libtpmlp.so")
+
+DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+ACT = {"none": 0, "relu": 1, "gelu_tanh": 2, "gelu_erf": 3, "swiglu": 4}
+STATUS = ["TP_OK", "TP_ERR_NULL_POINTER", "TP_ERR_BAD_SHAPE", "TP_ERR_NOT_DIVISIBLE",
+          "TP_ERR_BAD_SHARD", "TP_ERR_MISALIGNED", "TP_ERR_BAD_DTYPE", "TP_ERR_BAD_ACT",
+          "TP_ERR_WORKSPACE", "TP_ERR_HIP"]
+
+
+class TpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        name = STATUS[status] if 0 <= status < len(STATUS) else f"status {status}"
+        super().__init__(f"{name}: {message}")
+        self.status = status
+        self.name = name
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library():
+    """Load libtpmlp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m megatron_tensor_mlp_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    ci = ctypes.c_int
+    lib.tp_col_linear.argtypes = [ci, ci, i64, i64, i64, i32, i32, vp, i64, vp, i64, vp, i64, vp,
+                                  vp, i64, vp, sz, vp]
+    lib.tp_row_linear.argtypes = [ci, i64, i64, i64, i32, i32, vp, i64, vp, i64, vp, i64, vp, sz,
+                                  vp]
+    lib.tp_mlp_shard.argtypes = [ci, ci, i64, i64, i64, i32, i32, vp, i64, vp, i64, vp, i64, vp,
+                                 vp, i64, vp, i64, vp, i64, vp, sz, vp]
+    lib.tp_partial_sum.argtypes = [i64, i64, i32, ctypes.POINTER(vp), i64, vp, vp, i64, vp]
+    lib.tp_mlp_simulated.argtypes = [ci, ci, i64, i64, i64, i32, vp, i64, vp, i64, vp, i64, vp,
+                                     vp, i64, vp, vp, vp, vp, i64, vp, sz, vp]
+    lib.tp_workspace_bytes.argtypes = [ci, ci, i64, i64, i64, i32]
+    lib.tp_workspace_bytes.restype = sz
+    lib.tp_shard_bounds.argtypes = [i64, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.tp_status_string.argtypes = [ci]
+    lib.tp_status_string.restype = ctypes.c_char_p
+    lib.tp_last_error_message.argtypes = []
+    lib.tp_last_error_message.restype = ctypes.c_char_p
+    lib.tp_abi_version.argtypes = []
+    lib.tp_abi_version.restype = i32
+    for name in ("tp_col_linear", "tp_row_linear", "tp_mlp_shard", "tp_partial_sum",
+                 "tp_mlp_simulated", "tp_shard_bounds"):
+        getattr(lib, name).restype = ci
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = library().tp_last_error_message().decode()
+        raise TpError(status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ld(t, rows: int, cols: int, name: str) -> int:
+    """Leading dimension of a row-major 2-D view, after checking it spans rows x cols."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{name} is {tuple(t.shape)}, needs at least ({rows}, {cols})")
+    if rows > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} rows must be contiguous")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], cols)
+
+
+def _dt(t) -> int:
+    if t.dtype not in DTYPE:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return DTYPE[t.dtype]
+
+
+def _act(act) -> int:
+    return ACT[act] if isinstance(act, str) else int(act)
+
+
+def tp_abi_version() -> int:
+    return library().tp_abi_version()
+
+
+def tp_shard_bounds(k: int, i: int, p: int):
+    """(c0, s): the block [c0, c0 + s) that shard i of p owns of a dimension of size k."""
+    c0, s = ctypes.c_int64(), ctypes.c_int64()
+    _check(library().tp_shard_bounds(k, i, p, ctypes.byref(c0), ctypes.byref(s)))
+    return c0.value, s.value
+
+
+def tp_workspace_bytes(dtype, act, T: int, d: int, k: int, p: int) -> int:
+    dt = DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return library().tp_workspace_bytes(dt, _act(act), T, d, k, p)
+
+
+_ws_cache: dict = {}
+
+
+def workspace(nbytes: int, device) -> torch.Tensor | None:
+    """A zero-filled device buffer of at least nbytes, cached per device.  The
+    library leaves its counters zero after every call, so the buffer can be
+    reused by later calls on the same stream."""
+    if nbytes <= 0:
+        return None
+    dev = torch.device(device)
+    buf = _ws_cache.get(dev)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _ws_cache[dev] = buf
+    return buf
+
+
+def _ws_args(ws, need, device):
+    if ws is None:
+        ws = workspace(need, device)
+    if ws is None:
+        return None, 0
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def tp_col_linear(X, W1, i: int, p: int, Y, act="gelu_tanh", Wu=None, b1=None, ws=None,
+                  stream=None):
+    """Y <- act(X W1[:, i*s:(i+1)*s] + b1[i*s:(i+1)*s]) (or the SwiGLU pair), s = k/p."""
+    T, d = X.shape
+    k = W1.shape[1]
+    s = k // p if p > 0 else 0
+    a = _act(act)
+    ldx = _ld(X, T, d, "X")
+    ldw1 = _ld(W1, d, k, "W1")
+    ldwu = _ld(Wu, d, k, "Wu") if Wu is not None else 0
+    ldy = _ld(Y, T, s, "Y")
+    if b1 is not None and b1.numel() < k:
+        raise ValueError("b1 is shorter than k")
+    need = tp_workspace_bytes(X.dtype, a, T, d, k, p)
+    wsp, wsn = _ws_args(ws, need, X.device)
+    _check(library().tp_col_linear(_dt(X), a, T, d, k, i, p, _ptr(X), ldx, _ptr(W1), ldw1,
+                                   _ptr(Wu), ldwu, _ptr(b1), _ptr(Y), ldy, wsp, wsn,
+                                   _stream(stream)))
+    return Y
+
+
+def tp_row_linear(Y, W2, i: int, p: int, Z, ws=None, stream=None):
+    """Z <- Y W2[i*s:(i+1)*s, :] (fp32 partial, no bias), s = k/p."""
+    k, d = W2.shape
+    T = Y.shape[0]
+    s = k // p if p > 0 else 0
+    ldy = _ld(Y, T, s, "Y")
+    ldw2 = _ld(W2, k, d, "W2")
+    ldz = _ld(Z, T, d, "Z")
+    need = tp_workspace_bytes(Y.dtype, 0, T, d, k, p)
+    wsp, wsn = _ws_args(ws, need, Y.device)
+    _check(library().tp_row_linear(_dt(Y), T, d, k, i, p, _ptr(Y), ldy, _ptr(W2), ldw2, _ptr(Z),
+                                   ldz, wsp, wsn, _stream(stream)))
+    return Z
+
+
+def tp_mlp_shard(X, W1, W2, i: int, p: int, Y, Z, act="gelu_tanh", Wu=None, b1=None, ws=None,
+                 stream=None):
+    """Y <- column step of shard i, Z <- row step (fp32 partial)."""
+    T, d = X.shape
+    k = W1.shape[1]
+    s = k // p if p > 0 else 0
+    a = _act(act)
+    ldx = _ld(X, T, d, "X")
+    ldw1 = _ld(W1, d, k, "W1")
+    ldwu = _ld(Wu, d, k, "Wu") if Wu is not None else 0
+    ldw2 = _ld(W2, k, d, "W2")
+    ldy = _ld(Y, T, s, "Y")
+    ldz = _ld(Z, T, d, "Z")
+    if b1 is not None and b1.numel() < k:
+        raise ValueError("b1 is shorter than k")
+    need = tp_workspace_bytes(X.dtype, a, T, d, k, p)
+    wsp, wsn = _ws_args(ws, need, X.device)
+    _check(library().tp_mlp_shard(_dt(X), a, T, d, k, i, p, _ptr(X), ldx, _ptr(W1), ldw1,
+                                  _ptr(Wu), ldwu, _ptr(b1), _ptr(W2), ldw2, _ptr(Y), ldy,
+                                  _ptr(Z), ldz, wsp, wsn, _stream(stream)))
+    return Y, Z
+
+
+def tp_partial_sum(parts, Z, b2=None, stream=None):
+    """Z <- ((parts[0] + parts[1]) + ...) (+ b2); parts are fp32 [T, d] views with one ld."""
+    p = len(parts)
+    T, d = Z.shape
+    ldp = _ld(parts[0], T, d, "parts[0]") if p else d
+    for q, t in enumerate(parts):
+        if _ld(t, T, d, f"parts[{q}]") != ldp:
+            raise ValueError("all partials must share one leading dimension")
+    ldz = _ld(Z, T, d, "Z")
+    if b2 is not None and b2.numel() < d:
+        raise ValueError("b2 is shorter than d")
+    arr = (ctypes.c_void_p * max(p, 1))(*[t.data_ptr() for t in parts])
+    _check(library().tp_partial_sum(T, d, p, arr, ldp, _ptr(b2), _ptr(Z), ldz, _stream(stream)))
+    return Z
+
+
+def tp_mlp_simulated(X, W1, W2, p: int, Y, Zp, Z, act="gelu_tanh", Wu=None, b1=None, b2=None,
+                     ws=None, stream=None):
+    """All p shards on this device: Y [p, T, k/p], Zp [p, T, d] fp32, Z [T, d] fp32."""
+    T, d = X.shape
+    k = W1.shape[1]
+    s = k // p if p > 0 else 0
+    a = _act(act)
+    ldx = _ld(X, T, d, "X")
+    ldw1 = _ld(W1, d, k, "W1")
+    ldwu = _ld(Wu, d, k, "Wu") if Wu is not None else 0
+    ldw2 = _ld(W2, k, d, "W2")
+    if not Y.is_contiguous() or Y.numel() < p * T * s:
+        raise ValueError("Y must be a contiguous [p, T, k/p] buffer")
+    if not Zp.is_contiguous() or Zp.numel() < p * T * d or Zp.dtype != torch.float32:
+        raise ValueError("Zp must be a contiguous fp32 [p, T, d] buffer")
+    ldz = _ld(Z, T, d, "Z")
+    if b1 is not None and b1.numel() < k:
+        raise ValueError("b1 is shorter than k")
+    need = tp_workspace_bytes(X.dtype, a, T, d, k, p)
+    wsp, wsn = _ws_args(ws, need, X.device)
+    _check(library().tp_mlp_simulated(_dt(X), a, T, d, k, p, _ptr(X), ldx, _ptr(W1), ldw1,
+                                      _ptr(Wu), ldwu, _ptr(b1), _ptr(W2), ldw2, _ptr(b2),
+                                      _ptr(Y), _ptr(Zp), _ptr(Z), ldz, wsp, wsn,
+                                      _stream(stream)))
+    return Z

@@ -1,0 +1,427 @@
+// Host side of libtpmlp: argument checks, shard bookkeeping, path choice and
+// launches on the caller's stream.  Every check happens before any launch, so
+// an error status means nothing was enqueued and no output was touched.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/tpmlp.h"
+#include "kernels.h"
+
+using namespace tpmlp;
+
+namespace {
+
+thread_local std::string g_msg;
+
+tp_status fail(tp_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_msg = buf;
+  return s;
+}
+
+tp_status ok() {
+  g_msg.clear();
+  return TP_OK;
+}
+
+// Few-token path threshold: at or below this many tokens the shard is a
+// weight-streaming problem (HBM-bound), above it a tiled MFMA problem.
+constexpr int64_t kDecodeMaxT = 64;
+
+size_t elem_size(tp_dtype dt) { return dt == TP_BF16 ? 2 : 4; }
+int64_t elem_align(tp_dtype dt) { return dt == TP_BF16 ? 8 : 4; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+tp_status check_dtype_act(tp_dtype dt, int act) {
+  if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_BAD_DTYPE, "unknown dtype %d", (int)dt);
+  if (act < TP_ACT_NONE || act > TP_ACT_SWIGLU)
+    return fail(TP_ERR_BAD_ACT, "unknown activation %d", act);
+  return TP_OK;
+}
+
+// Shape and shard rule shared by every shard entry point.
+tp_status check_shard(int64_t T, int64_t d, int64_t k, int32_t i, int32_t p) {
+  if (T < 0) return fail(TP_ERR_BAD_SHAPE, "T = %lld < 0", (long long)T);
+  if (d < 1) return fail(TP_ERR_BAD_SHAPE, "d = %lld < 1", (long long)d);
+  if (k < 1) return fail(TP_ERR_BAD_SHAPE, "k = %lld < 1", (long long)k);
+  if (p < 1 || p > TP_MAX_SHARDS)
+    return fail(TP_ERR_BAD_SHARD, "p = %d outside [1, %d]", p, TP_MAX_SHARDS);
+  if (i < 0 || i >= p) return fail(TP_ERR_BAD_SHARD, "shard index i = %d outside [0, %d)", i, p);
+  if (k % p != 0)
+    return fail(TP_ERR_NOT_DIVISIBLE, "k = %lld is not divisible by p = %d", (long long)k, p);
+  return TP_OK;
+}
+
+tp_status check_ld(const char *name, int64_t ld, int64_t width, tp_dtype dt) {
+  if (ld < width)
+    return fail(TP_ERR_BAD_SHAPE, "%s = %lld is below the row width %lld", name, (long long)ld,
+                (long long)width);
+  if (ld % elem_align(dt) != 0)
+    return fail(TP_ERR_MISALIGNED, "%s = %lld is not a multiple of %lld elements", name,
+                (long long)ld, (long long)elem_align(dt));
+  return TP_OK;
+}
+
+tp_status check_ptr(const char *name, const void *ptr) {
+  if (!ptr) return fail(TP_ERR_NULL_POINTER, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(TP_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
+  return TP_OK;
+}
+
+#define TRY(expr)                   \
+  do {                              \
+    const tp_status st_ = (expr);   \
+    if (st_ != TP_OK) return st_;   \
+  } while (0)
+
+struct ColCall {
+  tp_dtype dt;
+  int act;
+  int64_t T, d, k;
+  int32_t i, p;
+  const void *X, *W1, *Wu, *b1;
+  int64_t ldx, ldw1, ldwu, ldy;
+  void *Y;
+};
+
+tp_status validate_col(const ColCall &c) {
+  TRY(check_dtype_act(c.dt, c.act));
+  TRY(check_shard(c.T, c.d, c.k, c.i, c.p));
+  const int64_t s = c.k / c.p;
+  if (c.d % elem_align(c.dt) || s % elem_align(c.dt))
+    return fail(TP_ERR_MISALIGNED, "d = %lld and k/p = %lld must be multiples of %lld",
+                (long long)c.d, (long long)s, (long long)elem_align(c.dt));
+  TRY(check_ptr("X", c.X));
+  TRY(check_ptr("W1", c.W1));
+  TRY(check_ptr("Y", c.Y));
+  TRY(check_ld("ldx", c.ldx, c.d, c.dt));
+  TRY(check_ld("ldw1", c.ldw1, c.k, c.dt));
+  TRY(check_ld("ldy", c.ldy, s, c.dt));
+  if (c.act == TP_ACT_SWIGLU) {
+    TRY(check_ptr("Wu", c.Wu));
+    TRY(check_ld("ldwu", c.ldwu, c.k, c.dt));
+    if (c.b1) return fail(TP_ERR_BAD_ACT, "a column bias is not supported with SWIGLU");
+  } else if (c.b1) {
+    TRY(check_ptr("b1", c.b1));
+  }
+  return TP_OK;
+}
+
+struct RowCall {
+  tp_dtype dt;
+  int64_t T, d, k;
+  int32_t i, p;
+  const void *Y, *W2;
+  int64_t ldy, ldw2, ldz;
+  float *Z;
+};
+
+tp_status validate_row(const RowCall &r) {
+  TRY(check_dtype_act(r.dt, TP_ACT_NONE));
+  TRY(check_shard(r.T, r.d, r.k, r.i, r.p));
+  const int64_t s = r.k / r.p;
+  if (r.d % elem_align(r.dt) || s % elem_align(r.dt))
+    return fail(TP_ERR_MISALIGNED, "d = %lld and k/p = %lld must be multiples of %lld",
+                (long long)r.d, (long long)s, (long long)elem_align(r.dt));
+  TRY(check_ptr("Y", r.Y));
+  TRY(check_ptr("W2", r.W2));
+  TRY(check_ptr("Z", r.Z));
+  TRY(check_ld("ldy", r.ldy, s, r.dt));
+  TRY(check_ld("ldw2", r.ldw2, r.d, r.dt));
+  TRY(check_ld("ldz", r.ldz, r.d, TP_F32));
+  return TP_OK;
+}
+
+// GEMM descriptors of one shard (or of all p shards, grouped).  The column
+// block of W1/Wu/b1 of shard i starts at column i*s, the row block of W2 at
+// row i*s (Day 41 post, "Simulating column parallel linear" and "Simulating
+// row parallel linear").
+GemmArgs col_gemm(const ColCall &c, int groups, int64_t ystride) {
+  const int64_t s = c.k / c.p, c0 = (int64_t)c.i * s;
+  const size_t es = elem_size(c.dt);
+  GemmArgs a{};
+  a.A = c.X;
+  a.lda = c.ldx;
+  a.B = (const char *)c.W1 + c0 * es;
+  a.ldb = c.ldw1;
+  a.B2 = c.Wu ? (const void *)((const char *)c.Wu + c0 * es) : nullptr;
+  a.ldb2 = c.ldwu;
+  a.bias = c.b1 ? (const void *)((const char *)c.b1 + c0 * es) : nullptr;
+  a.C = c.Y;
+  a.ldc = c.ldy;
+  a.M = c.T;
+  a.N = s;
+  a.K = c.d;
+  a.epi = c.act == TP_ACT_SWIGLU ? EPI_SWIGLU : EPI_ACT;
+  a.act = c.act;
+  a.groups = groups;
+  a.sA = 0;
+  a.sB = s;
+  a.sB2 = s;
+  a.sBias = s;
+  a.sC = ystride;
+  return a;
+}
+
+GemmArgs row_gemm(const RowCall &r, int groups, int64_t ystride, int64_t zstride) {
+  const int64_t s = r.k / r.p, c0 = (int64_t)r.i * s;
+  GemmArgs a{};
+  a.A = r.Y;
+  a.lda = r.ldy;
+  a.B = (const char *)r.W2 + c0 * r.ldw2 * elem_size(r.dt);
+  a.ldb = r.ldw2;
+  a.C = r.Z;
+  a.ldc = r.ldz;
+  a.M = r.T;
+  a.N = r.d;
+  a.K = s;
+  a.epi = EPI_F32;
+  a.act = TP_ACT_NONE;
+  a.groups = groups;
+  a.sA = ystride;
+  a.sB = s * r.ldw2;
+  a.sC = zstride;
+  return a;
+}
+
+size_t gemm_ws_bytes(tp_dtype dt, const GemmArgs &a) {
+  if (dt != TP_BF16 || a.M > kDecodeMaxT || a.M <= 0) return 0;
+  return decode_workspace_bytes(a);
+}
+
+tp_status run_gemm(tp_dtype dt, const GemmArgs &a, void *ws, hipStream_t st) {
+  hipError_t e;
+  if (dt == TP_F32)
+    e = launch_gemm_f32(a, st);
+  else if (a.M <= kDecodeMaxT)
+    e = launch_gemm_bf16_decode(a, ws, st);
+  else
+    e = launch_gemm_bf16_tiled(a, st);
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return TP_OK;
+}
+
+tp_status check_ws(size_t need, void *ws, size_t ws_bytes) {
+  if (need == 0) return TP_OK;
+  if (!ws || ws_bytes < need)
+    return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need,
+                ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(TP_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  return TP_OK;
+}
+
+ColCall make_col(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t i, int32_t p,
+                 const void *X, int64_t ldx, const void *W1, int64_t ldw1, const void *Wu,
+                 int64_t ldwu, const void *b1, void *Y, int64_t ldy) {
+  ColCall c;
+  c.dt = dt;
+  c.act = (int)act;
+  c.T = T;
+  c.d = d;
+  c.k = k;
+  c.i = i;
+  c.p = p;
+  c.X = X;
+  c.W1 = W1;
+  c.Wu = (act == TP_ACT_SWIGLU) ? Wu : nullptr;
+  c.b1 = b1;
+  c.ldx = ldx;
+  c.ldw1 = ldw1;
+  c.ldwu = ldwu;
+  c.ldy = ldy;
+  c.Y = Y;
+  return c;
+}
+
+RowCall make_row(tp_dtype dt, int64_t T, int64_t d, int64_t k, int32_t i, int32_t p,
+                 const void *Y, int64_t ldy, const void *W2, int64_t ldw2, float *Z, int64_t ldz) {
+  RowCall r;
+  r.dt = dt;
+  r.T = T;
+  r.d = d;
+  r.k = k;
+  r.i = i;
+  r.p = p;
+  r.Y = Y;
+  r.W2 = W2;
+  r.ldy = ldy;
+  r.ldw2 = ldw2;
+  r.ldz = ldz;
+  r.Z = Z;
+  return r;
+}
+
+size_t max_sz(size_t a, size_t b) { return a > b ? a : b; }
+
+}  // namespace
+
+extern "C" {
+
+tp_status tp_col_linear(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t i,
+                        int32_t p, const void *X, int64_t ldx, const void *W1, int64_t ldw1,
+                        const void *Wu, int64_t ldwu, const void *b1, void *Y, int64_t ldy,
+                        void *ws, size_t ws_bytes, void *stream) {
+  const ColCall c = make_col(dt, act, T, d, k, i, p, X, ldx, W1, ldw1, Wu, ldwu, b1, Y, ldy);
+  TRY(validate_col(c));
+  if (T == 0) return ok();
+  const GemmArgs a = col_gemm(c, 1, 0);
+  TRY(check_ws(gemm_ws_bytes(dt, a), ws, ws_bytes));
+  TRY(run_gemm(dt, a, ws, (hipStream_t)stream));
+  return ok();
+}
+
+tp_status tp_row_linear(tp_dtype dt, int64_t T, int64_t d, int64_t k, int32_t i, int32_t p,
+                        const void *Y, int64_t ldy, const void *W2, int64_t ldw2, float *Z,
+                        int64_t ldz, void *ws, size_t ws_bytes, void *stream) {
+  const RowCall r = make_row(dt, T, d, k, i, p, Y, ldy, W2, ldw2, Z, ldz);
+  TRY(validate_row(r));
+  if (T == 0) return ok();
+  const GemmArgs a = row_gemm(r, 1, 0, 0);
+  TRY(check_ws(gemm_ws_bytes(dt, a), ws, ws_bytes));
+  TRY(run_gemm(dt, a, ws, (hipStream_t)stream));
+  return ok();
+}
+
+tp_status tp_mlp_shard(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t i,
+                       int32_t p, const void *X, int64_t ldx, const void *W1, int64_t ldw1,
+                       const void *Wu, int64_t ldwu, const void *b1, const void *W2,
+                       int64_t ldw2, void *Y, int64_t ldy, float *Z, int64_t ldz, void *ws,
+                       size_t ws_bytes, void *stream) {
+  const ColCall c = make_col(dt, act, T, d, k, i, p, X, ldx, W1, ldw1, Wu, ldwu, b1, Y, ldy);
+  TRY(validate_col(c));
+  const RowCall r = make_row(dt, T, d, k, i, p, Y, ldy, W2, ldw2, Z, ldz);
+  TRY(validate_row(r));
+  if (T == 0) return ok();
+  const GemmArgs ac = col_gemm(c, 1, 0), ar = row_gemm(r, 1, 0, 0);
+  TRY(check_ws(max_sz(gemm_ws_bytes(dt, ac), gemm_ws_bytes(dt, ar)), ws, ws_bytes));
+  TRY(run_gemm(dt, ac, ws, (hipStream_t)stream));
+  TRY(run_gemm(dt, ar, ws, (hipStream_t)stream));
+  return ok();
+}
+
+tp_status tp_partial_sum(int64_t T, int64_t d, int32_t p, const float *const *parts, int64_t ldp,
+                         const float *b2, float *Z, int64_t ldz, void *stream) {
+  if (T < 0) return fail(TP_ERR_BAD_SHAPE, "T = %lld < 0", (long long)T);
+  if (d < 1) return fail(TP_ERR_BAD_SHAPE, "d = %lld < 1", (long long)d);
+  if (p < 1 || p > TP_MAX_SHARDS)
+    return fail(TP_ERR_BAD_SHARD, "p = %d outside [1, %d]", p, TP_MAX_SHARDS);
+  if (d % 4) return fail(TP_ERR_MISALIGNED, "d = %lld is not a multiple of 4", (long long)d);
+  if (!parts) return fail(TP_ERR_NULL_POINTER, "parts is NULL");
+  TRY(check_ld("ldp", ldp, d, TP_F32));
+  TRY(check_ld("ldz", ldz, d, TP_F32));
+  PartSumArgs a{};
+  for (int q = 0; q < p; ++q) {
+    char name[32];
+    snprintf(name, sizeof name, "parts[%d]", q);
+    TRY(check_ptr(name, parts[q]));
+    a.parts[q] = parts[q];
+  }
+  TRY(check_ptr("Z", Z));
+  if (b2) TRY(check_ptr("b2", b2));
+  if (T == 0) return ok();
+  a.p = p;
+  a.T = T;
+  a.d = d;
+  a.ldp = ldp;
+  a.ldz = ldz;
+  a.b2 = b2;
+  a.Z = Z;
+  const hipError_t e = launch_partial_sum(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+tp_status tp_mlp_simulated(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t p,
+                           const void *X, int64_t ldx, const void *W1, int64_t ldw1,
+                           const void *Wu, int64_t ldwu, const void *b1, const void *W2,
+                           int64_t ldw2, const float *b2, void *Y, float *Zp, float *Z,
+                           int64_t ldz, void *ws, size_t ws_bytes, void *stream) {
+  if (p < 1 || p > TP_MAX_SHARDS)
+    return fail(TP_ERR_BAD_SHARD, "p = %d outside [1, %d]", p, TP_MAX_SHARDS);
+  const int64_t s = (p > 0 && k % p == 0) ? k / p : 0;
+  // Shard 0 stands for all: the others differ only by the block offsets.
+  const ColCall c = make_col(dt, act, T, d, k, 0, p, X, ldx, W1, ldw1, Wu, ldwu, b1, Y, s);
+  TRY(validate_col(c));
+  const RowCall r = make_row(dt, T, d, k, 0, p, Y, s, W2, ldw2, Zp, d);
+  TRY(validate_row(r));
+  TRY(check_ptr("Z", Z));
+  TRY(check_ld("ldz", ldz, d, TP_F32));
+  if (b2) TRY(check_ptr("b2", b2));
+  if (T == 0) return ok();
+  const GemmArgs ac = col_gemm(c, p, T * s), ar = row_gemm(r, p, T * s, T * d);
+  TRY(check_ws(max_sz(gemm_ws_bytes(dt, ac), gemm_ws_bytes(dt, ar)), ws, ws_bytes));
+  TRY(run_gemm(dt, ac, ws, (hipStream_t)stream));
+  TRY(run_gemm(dt, ar, ws, (hipStream_t)stream));
+  PartSumArgs ps{};
+  for (int q = 0; q < p; ++q) ps.parts[q] = Zp + (int64_t)q * T * d;
+  ps.p = p;
+  ps.T = T;
+  ps.d = d;
+  ps.ldp = d;
+  ps.ldz = ldz;
+  ps.b2 = b2;
+  ps.Z = Z;
+  const hipError_t e = launch_partial_sum(ps, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t tp_workspace_bytes(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t p) {
+  if (dt != TP_F32 && dt != TP_BF16) return 0;
+  if ((int)act < TP_ACT_NONE || (int)act > TP_ACT_SWIGLU) return 0;
+  if (T < 1 || d < 1 || k < 1 || p < 1 || p > TP_MAX_SHARDS || k % p) return 0;
+  const int64_t s = k / p;
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  ColCall c = make_col(dt, act, T, d, k, 0, p, dummy, d, dummy, k, dummy, k, nullptr,
+                       (void *)dummy, s);
+  RowCall r = make_row(dt, T, d, k, 0, p, dummy, s, dummy, d, (float *)dummy, d);
+  return max_sz(gemm_ws_bytes(dt, col_gemm(c, 1, 0)), gemm_ws_bytes(dt, row_gemm(r, 1, 0, 0)));
+}
+
+tp_status tp_shard_bounds(int64_t k, int32_t i, int32_t p, int64_t *c0, int64_t *s) {
+  if (!c0 || !s) return fail(TP_ERR_NULL_POINTER, "output pointer is NULL");
+  TRY(check_shard(0, 1, k, i, p));
+  *s = k / p;
+  *c0 = (int64_t)i * (k / p);
+  return ok();
+}
+
+const char *tp_status_string(tp_status s) {
+  switch (s) {
+    case TP_OK:
+      return "TP_OK";
+    case TP_ERR_NULL_POINTER:
+      return "TP_ERR_NULL_POINTER";
+    case TP_ERR_BAD_SHAPE:
+      return "TP_ERR_BAD_SHAPE";
+    case TP_ERR_NOT_DIVISIBLE:
+      return "TP_ERR_NOT_DIVISIBLE";
+    case TP_ERR_BAD_SHARD:
+      return "TP_ERR_BAD_SHARD";
+    case TP_ERR_MISALIGNED:
+      return "TP_ERR_MISALIGNED";
+    case TP_ERR_BAD_DTYPE:
+      return "TP_ERR_BAD_DTYPE";
+    case TP_ERR_BAD_ACT:
+      return "TP_ERR_BAD_ACT";
+    case TP_ERR_WORKSPACE:
+      return "TP_ERR_WORKSPACE";
+    case TP_ERR_HIP:
+      return "TP_ERR_HIP";
+  }
+  return "TP_UNKNOWN_STATUS";
+}
+
+const char *tp_last_error_message(void) { return g_msg.c_str(); }
+
+int32_t tp_abi_version(void) { return TPMLP_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Device-side types and element-wise functions shared by the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpmlp {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Activation codes, equal to tp_act in tpmlp.h.
+enum : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2, ACT_GELU_ERF = 3, ACT_SWIGLU = 4 };
+
+// Element-wise activations in fp32.  The pages name GeLU and Swish without a
+// formula; the published definitions are used, evaluated with the device math
+// library (tanhf, erff, expf).
+//   GeLU tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+//   GeLU erf form:  0.5 x (1 + erf(x / sqrt 2))
+//   SiLU (Swish, slope 1): x / (1 + exp(-x))
+template <int ACT>
+__device__ __forceinline__ float activate(float x) {
+  if constexpr (ACT == ACT_RELU) {
+    return x > 0.0f ? x : 0.0f;
+  } else if constexpr (ACT == ACT_GELU_TANH) {
+    const float c = 0.7978845608028654f;  // sqrt(2/pi)
+    return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
+  } else if constexpr (ACT == ACT_GELU_ERF) {
+    return 0.5f * x * (1.0f + erff(x * 0.7071067811865476f));
+  } else if constexpr (ACT == ACT_SWIGLU) {  // the SiLU half of SwiGLU
+    return x / (1.0f + expf(-x));
+  } else {
+    return x;
+  }
+}
+
+__device__ __forceinline__ float silu(float x) { return activate<ACT_SWIGLU>(x); }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t lo16) {
+  return __uint_as_float(lo16 << 16);
+}
+
+// Combine the low (or high) 16-bit halves of two dwords into one dword:
+// result = lo_half(a) | lo_half(b) << 16   (or the high halves).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+}  // namespace tpmlp

@@ -1,0 +1,57 @@
+// Host-side launch interface of the gfx950 kernels (internal to libtpmlp).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tpmlp {
+
+// What a GEMM does with its fp32 accumulator tile.
+enum Epilogue : int {
+  EPI_ACT = 0,     // C = act(acc + bias) in the element type  (column step, GeLU/ReLU/none)
+  EPI_SWIGLU = 1,  // C = SiLU(acc_gate) * acc_up              (column step, SwiGLU)
+  EPI_F32 = 2,          // C = acc, fp32                           (row step partial)
+};
+
+// C[M,N] = epilogue(A[M,K] * B[K,N]) for `groups` independent problems that
+// share M, N, K and leading dimensions; problem g uses base pointers offset by
+// g * s* elements (the simulated-p grouped launch).  bf16 operands.
+struct GemmArgs {
+  const void *A;
+  int64_t lda;
+  const void *B;   // gate matrix for SwiGLU
+  int64_t ldb;
+  const void *B2;  // up matrix (SwiGLU only)
+  int64_t ldb2;
+  const void *bias;  // [N] or null (EPI_ACT only)
+  void *C;
+  int64_t ldc;
+  int64_t M, N, K;
+  int epi, act;
+  int groups;
+  int64_t sA, sB, sB2, sBias, sC;
+};
+
+// Large-T path: MFMA tiles staged through LDS.
+hipError_t launch_gemm_bf16_tiled(const GemmArgs &a, hipStream_t s);
+
+// Few-token path (M <= 64): weight-streaming split-K GEMM.  `ws` must hold
+// decode_workspace_bytes(a) zero-initialised bytes (or 0 bytes if that is 0).
+size_t decode_workspace_bytes(const GemmArgs &a);
+hipError_t launch_gemm_bf16_decode(const GemmArgs &a, void *ws, hipStream_t s);
+
+// fp32 path (correctness-first): one output per thread, k ascending.
+hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s);
+
+// Z = ((P0 + P1) + ...) + P_{p-1} (+ b2), fp32.
+constexpr int kMaxParts = 64;
+struct PartSumArgs {
+  const float *parts[kMaxParts];
+  int p;
+  int64_t T, d, ldp, ldz;
+  const float *b2;
+  float *Z;
+};
+hipError_t launch_partial_sum(const PartSumArgs &a, hipStream_t s);
+
+}  // namespace tpmlp

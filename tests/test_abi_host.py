@@ -1,0 +1,207 @@
+"""Host-side tests of the C ABI: the library loads, exports what include/tpmlp.h
+declares, does its shard bookkeeping, and rejects bad arguments before any
+launch.  No GPU is used: the error-path cases pass fake (never dereferenced)
+pointers and are skipped whenever a GPU is visible, so no kernel can ever see
+them."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import megatron_tensor_mlp_amd as tp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpmlp.h")
+
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="fake-pointer error paths run only where no GPU is visible")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("tp_col_linear", "tp_row_linear", "tp_mlp_shard", "tp_partial_sum",
+              "tp_mlp_simulated", "tp_workspace_bytes", "tp_shard_bounds", "tp_status_string",
+              "tp_last_error_message", "tp_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tp.library()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", tp.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (tp_\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_library_is_gfx950():
+    """The fat binary carries gfx950 code objects (the offload bundle's target id)."""
+    blob = open(tp.library_path(), "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define TPMLP_ABI_VERSION (\d+)", open(HEADER).read())
+    assert tp.tp_abi_version() == int(m.group(1))
+
+
+def test_status_strings():
+    lib = tp.library()
+    for code, name in enumerate(tp._binding.STATUS):
+        assert lib.tp_status_string(code).decode() == name
+    assert lib.tp_status_string(99).decode() == "TP_UNKNOWN_STATUS"
+
+
+def test_shard_bounds_llama_tp8(golden):
+    """'What is Tensor Parallelism?', Llama 3.1 70B worked example: 3584 columns per GPU."""
+    g = golden("llama70b_tp8_shapes.txt")
+    k, p, s = int(g["ffn_size"]), int(g["tp"]), int(g["ffn_columns_per_gpu"])
+    for i in range(p):
+        assert tp.tp_shard_bounds(k, i, p) == (i * s, s)
+
+
+def test_shard_bounds_errors():
+    """'Tensor Parallelism Explained', section 4: 64 heads over TP = 5 fails at startup;
+    the same divisibility rule applies to the sharded hidden dimension."""
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_shard_bounds(64, 0, 5)
+    assert e.value.name == "TP_ERR_NOT_DIVISIBLE"
+    assert "divisible" in str(e.value)
+    for p in (1, 2, 4, 8):
+        assert tp.tp_shard_bounds(64, p - 1, p) == ((p - 1) * (64 // p), 64 // p)
+    for (k, i, p) in ((64, 4, 4), (64, -1, 4), (64, 0, 0), (64, 0, 65)):
+        with pytest.raises(tp.TpError) as e:
+            tp.tp_shard_bounds(k, i, p)
+        assert e.value.name == "TP_ERR_BAD_SHARD"
+
+
+def test_workspace_bytes():
+    bf16 = torch.bfloat16
+    # many tokens: tiled path, no workspace
+    assert tp.tp_workspace_bytes(bf16, "swiglu", 4096, 8192, 28672, 8) == 0
+    assert tp.tp_workspace_bytes(torch.float32, "gelu_tanh", 4, 512, 2048, 4) == 0
+    # decode shapes split K and need partials + counters
+    for T in (1, 8, 64):
+        assert tp.tp_workspace_bytes(bf16, "swiglu", T, 8192, 28672, 8) > 0
+    # invalid arguments report 0
+    assert tp.tp_workspace_bytes(bf16, "swiglu", 8, 8192, 28672, 5) == 0
+    assert tp.tp_workspace_bytes(bf16, 9, 8, 8192, 28672, 8) == 0
+
+
+# --- fake-pointer error paths (validation happens before any launch) --------
+A = 0x10000  # 16-byte aligned, never dereferenced
+MIS = A + 2  # misaligned
+P = ctypes.c_void_p
+
+
+def col(dt=1, act=2, T=4, d=64, k=128, i=0, p=2, X=A, ldx=64, W1=A, ldw1=128, Wu=None, ldwu=0,
+        b1=None, Y=A, ldy=64, ws=None, wsb=0):
+    return tp.library().tp_col_linear(dt, act, T, d, k, i, p, P(X), ldx, P(W1), ldw1, P(Wu), ldwu,
+                                      P(b1), P(Y), ldy, P(ws), wsb, None)
+
+
+def status_name(code):
+    return tp._binding.STATUS[code]
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(k=129, ldw1=136), "TP_ERR_NOT_DIVISIBLE"),   # k % p != 0
+    (dict(i=2), "TP_ERR_BAD_SHARD"),
+    (dict(i=-1), "TP_ERR_BAD_SHARD"),
+    (dict(p=0), "TP_ERR_BAD_SHARD"),
+    (dict(p=65, k=65 * 8, ldw1=65 * 8), "TP_ERR_BAD_SHARD"),
+    (dict(T=-1), "TP_ERR_BAD_SHAPE"),
+    (dict(d=0), "TP_ERR_BAD_SHAPE"),
+    (dict(k=0), "TP_ERR_BAD_SHAPE"),
+    (dict(X=None), "TP_ERR_NULL_POINTER"),
+    (dict(W1=None), "TP_ERR_NULL_POINTER"),
+    (dict(Y=None), "TP_ERR_NULL_POINTER"),
+    (dict(X=MIS), "TP_ERR_MISALIGNED"),
+    (dict(ldx=60), "TP_ERR_BAD_SHAPE"),
+    (dict(ldx=68), "TP_ERR_MISALIGNED"),
+    (dict(d=60, ldx=64), "TP_ERR_MISALIGNED"),       # d not a multiple of 8 (bf16)
+    (dict(k=136, ldw1=136), "TP_ERR_MISALIGNED"),    # k/p = 68
+    (dict(ldy=32), "TP_ERR_BAD_SHAPE"),
+    (dict(dt=7), "TP_ERR_BAD_DTYPE"),
+    (dict(act=9), "TP_ERR_BAD_ACT"),
+    (dict(act=4), "TP_ERR_NULL_POINTER"),             # SwiGLU without Wu
+    (dict(act=4, Wu=A, ldwu=128, b1=A), "TP_ERR_BAD_ACT"),  # bias with SwiGLU
+    (dict(b1=MIS), "TP_ERR_MISALIGNED"),
+    (dict(T=1, d=8192, ldx=8192, k=28672, ldw1=28672, p=8, ldy=3584), "TP_ERR_WORKSPACE"),
+])
+def test_col_linear_rejects(kw, expect):
+    assert status_name(col(**kw)) == expect
+    assert tp.library().tp_last_error_message().decode() != ""
+
+
+@no_gpu
+def test_fp32_alignment_rule_is_four():
+    # fp32: d = 60 is allowed (multiple of 4), but a misaligned ld is not
+    assert status_name(col(dt=0, d=60, ldx=60, T=0)) == "TP_OK"
+    assert status_name(col(dt=0, ldx=66)) == "TP_ERR_MISALIGNED"
+
+
+@no_gpu
+def test_zero_tokens_launch_nothing():
+    assert status_name(col(T=0)) == "TP_OK"
+    lib = tp.library()
+    assert lib.tp_last_error_message().decode() == ""
+    st = lib.tp_row_linear(1, 0, 64, 128, 0, 2, P(A), 64, P(A), 64, P(A), 64, None, 0, None)
+    assert status_name(st) == "TP_OK"
+
+
+@no_gpu
+@pytest.mark.parametrize("args,expect", [
+    (dict(k=129), "TP_ERR_NOT_DIVISIBLE"),
+    (dict(Z=None), "TP_ERR_NULL_POINTER"),
+    (dict(ldz=60), "TP_ERR_BAD_SHAPE"),
+    (dict(ldw2=60), "TP_ERR_BAD_SHAPE"),
+    (dict(Y=MIS), "TP_ERR_MISALIGNED"),
+])
+def test_row_linear_rejects(args, expect):
+    a = dict(dt=1, T=4, d=64, k=128, i=0, p=2, Y=A, ldy=64, W2=A, ldw2=64, Z=A, ldz=64)
+    a.update(args)
+    st = tp.library().tp_row_linear(a["dt"], a["T"], a["d"], a["k"], a["i"], a["p"], P(a["Y"]),
+                                    a["ldy"], P(a["W2"]), a["ldw2"], P(a["Z"]), a["ldz"], None, 0,
+                                    None)
+    assert status_name(st) == expect
+
+
+@no_gpu
+def test_partial_sum_rejects():
+    lib = tp.library()
+    arr = (ctypes.c_void_p * 3)(A, A, None)
+    assert status_name(lib.tp_partial_sum(4, 64, 3, arr, 64, None, P(A), 64, None)) \
+        == "TP_ERR_NULL_POINTER"
+    arr = (ctypes.c_void_p * 2)(A, MIS)
+    assert status_name(lib.tp_partial_sum(4, 64, 2, arr, 64, None, P(A), 64, None)) \
+        == "TP_ERR_MISALIGNED"
+    arr = (ctypes.c_void_p * 2)(A, A)
+    assert status_name(lib.tp_partial_sum(4, 62, 2, arr, 64, None, P(A), 64, None)) \
+        == "TP_ERR_MISALIGNED"
+    assert status_name(lib.tp_partial_sum(4, 64, 0, arr, 64, None, P(A), 64, None)) \
+        == "TP_ERR_BAD_SHARD"
+    assert status_name(lib.tp_partial_sum(4, 64, 65, arr, 64, None, P(A), 64, None)) \
+        == "TP_ERR_BAD_SHARD"
+    assert status_name(lib.tp_partial_sum(0, 64, 2, arr, 64, None, P(A), 64, None)) == "TP_OK"
+
+
+@no_gpu
+def test_simulated_rejects_page_example_degree():
+    """p = 5 does not divide k = 320 ... but 320 / 5 = 64 does; the page's 64 over 5
+    is the failing case: k = 64, p = 5."""
+    lib = tp.library()
+    st = lib.tp_mlp_simulated(1, 2, 4, 64, 64, 5, P(A), 64, P(A), 64, None, 0, None, P(A), 64,
+                              None, P(A), P(A), P(A), 64, None, 0, None)
+    assert status_name(st) == "TP_ERR_NOT_DIVISIBLE"
