@@ -34,7 +34,8 @@
  *   - Alignment: every data pointer must be 16-byte aligned, and d, k/p and
  *     every leading dimension must be a multiple of 8 elements (bf16) or
  *     4 elements (fp32); otherwise TP_ERR_MISALIGNED.
- *   - T = 0 is valid and launches nothing.
+ *   - T = 0 is valid and launches nothing; the token-sized buffers (X, Y, Z,
+ *     the partials) may then be NULL.
  *   - Memory: all tensors are device memory owned by the caller.  The library
  *     allocates nothing and keeps no pointer after a call returns.  Some shapes
  *     need a caller-provided workspace (see tp_workspace_bytes).

@@ -99,9 +99,11 @@ tp_status validate_col(const ColCall &c) {
   if (c.d % elem_align(c.dt) || s % elem_align(c.dt))
     return fail(TP_ERR_MISALIGNED, "d = %lld and k/p = %lld must be multiples of %lld",
                 (long long)c.d, (long long)s, (long long)elem_align(c.dt));
-  TRY(check_ptr("X", c.X));
+  if (c.T > 0) {  // with no tokens X and Y are never touched and may be NULL
+    TRY(check_ptr("X", c.X));
+    TRY(check_ptr("Y", c.Y));
+  }
   TRY(check_ptr("W1", c.W1));
-  TRY(check_ptr("Y", c.Y));
   TRY(check_ld("ldx", c.ldx, c.d, c.dt));
   TRY(check_ld("ldw1", c.ldw1, c.k, c.dt));
   TRY(check_ld("ldy", c.ldy, s, c.dt));
@@ -131,9 +133,11 @@ tp_status validate_row(const RowCall &r) {
   if (r.d % elem_align(r.dt) || s % elem_align(r.dt))
     return fail(TP_ERR_MISALIGNED, "d = %lld and k/p = %lld must be multiples of %lld",
                 (long long)r.d, (long long)s, (long long)elem_align(r.dt));
-  TRY(check_ptr("Y", r.Y));
+  if (r.T > 0) {  // with no tokens Y and Z are never touched and may be NULL
+    TRY(check_ptr("Y", r.Y));
+    TRY(check_ptr("Z", r.Z));
+  }
   TRY(check_ptr("W2", r.W2));
-  TRY(check_ptr("Z", r.Z));
   TRY(check_ld("ldy", r.ldy, s, r.dt));
   TRY(check_ld("ldw2", r.ldw2, r.d, r.dt));
   TRY(check_ld("ldz", r.ldz, r.d, TP_F32));
@@ -317,6 +321,7 @@ tp_status tp_partial_sum(int64_t T, int64_t d, int32_t p, const float *const *pa
   if (!parts) return fail(TP_ERR_NULL_POINTER, "parts is NULL");
   TRY(check_ld("ldp", ldp, d, TP_F32));
   TRY(check_ld("ldz", ldz, d, TP_F32));
+  if (T == 0) return ok();  // nothing is read or written
   PartSumArgs a{};
   for (int q = 0; q < p; ++q) {
     char name[32];
@@ -326,7 +331,6 @@ tp_status tp_partial_sum(int64_t T, int64_t d, int32_t p, const float *const *pa
   }
   TRY(check_ptr("Z", Z));
   if (b2) TRY(check_ptr("b2", b2));
-  if (T == 0) return ok();
   a.p = p;
   a.T = T;
   a.d = d;
@@ -352,7 +356,7 @@ tp_status tp_mlp_simulated(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_
   TRY(validate_col(c));
   const RowCall r = make_row(dt, T, d, k, 0, p, Y, s, W2, ldw2, Zp, d);
   TRY(validate_row(r));
-  TRY(check_ptr("Z", Z));
+  if (T > 0) TRY(check_ptr("Z", Z));
   TRY(check_ld("ldz", ldz, d, TP_F32));
   if (b2) TRY(check_ptr("b2", b2));
   if (T == 0) return ok();

@@ -159,6 +159,11 @@ def test_zero_tokens_launch_nothing():
     assert lib.tp_last_error_message().decode() == ""
     st = lib.tp_row_linear(1, 0, 64, 128, 0, 2, P(A), 64, P(A), 64, P(A), 64, None, 0, None)
     assert status_name(st) == "TP_OK"
+    # with no tokens the token-sized buffers may be NULL (empty torch tensors are)
+    assert status_name(col(T=0, X=None, Y=None)) == "TP_OK"
+    st = lib.tp_row_linear(1, 0, 64, 128, 0, 2, None, 64, P(A), 64, None, 64, None, 0, None)
+    assert status_name(st) == "TP_OK"
+    assert status_name(col(T=0, W1=None)) == "TP_ERR_NULL_POINTER"
 
 
 @no_gpu

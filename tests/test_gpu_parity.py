@@ -186,7 +186,7 @@ def test_bad_degree_leaves_output_untouched():
     """'Tensor Parallelism Explained', section 4: a degree that does not divide the
     sharded dimension is an error; nothing is launched."""
     X, W1, _, b1, W2 = synth.small_case(8, 64, 320, 1, False, True)
-    Y = torch.full((8, 64), 7.0, dtype=torch.bfloat16, device=DEV)
+    Y = torch.full((8, 128), 7.0, dtype=torch.bfloat16, device=DEV)
     Z = torch.full((8, 64), 7.0, device=DEV)
     with pytest.raises(tp.TpError) as e:
         tp.tp_mlp_shard(dev(X), dev(W1), dev(W2), 0, 3, Y, Z, act="gelu_tanh", b1=dev(b1))
