@@ -26,6 +26,8 @@
 // reads hit distinct banks.  LDS holds two stages: the loads of k-step t+1 are
 // in flight while step t's MFMAs run; within a step the fragments of the next
 // 16-k slice are read while the current slice's MFMAs issue.
+#include <cstdlib>
+
 #include "device_common.hpp"
 #include "kernels.h"
 
@@ -33,29 +35,58 @@ namespace tpmlp {
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHREADS = 256;
-constexpr int A_BYTES = BM * BK * 2;  // 32 KiB: [256 rows][64 k]
-constexpr int B_BYTES = BK * BN * 2;  // 32 KiB: [64 k][256 cols] (or 2 x [64][128] for SwiGLU)
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int BM = 256, BN = 256, NTHREADS = 256;
 constexpr int GROUP_M = 4;            // row-tiles walked together for L2 reuse
 constexpr uint32_t OOB = 0x80000000u; // an offset past every buffer range: reads as zero
 constexpr int RSRC_WORD3 = 0x00020000;
 
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= v only.
+constexpr int wait_vm(int v) { return (v & 15) | (7 << 4) | (15 << 8) | ((v >> 4) << 14); }
+// ... and for lgkmcnt == 0 as well.
+constexpr int wait_vm_lgkm0(int v) { return (v & 15) | (7 << 4) | ((v >> 4) << 14); }
+
 // XOR masks on the 16-byte unit index of an LDS row.
-//  A rows (128 B = 8 units): fragment reads touch 8 or 16 consecutive rows at
-//  one logical unit; this mask makes them land on distinct banks.
-__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r << 2)) & 7; }
+//  A rows (2*BK bytes = BK/8 units): fragment reads touch 8 or 16 consecutive
+//  rows at one logical unit; the mask spreads them over distinct banks.
+template <int BK>
+__device__ __forceinline__ int swz_a(int r) {
+  if constexpr (BK == 64) return ((r >> 1) ^ (r << 2)) & 7;
+  else return ((r >> 1) ^ (r >> 2)) & 3;
+}
 //  B rows (512 or 256 B): a transposing read touches 4 consecutive k rows x
 //  32 or 64 bytes; rows k..k+3 get masks 0, 4, 10, 14 (distinct 64-byte
 //  segments and distinct 32-byte pairs within them).
 __device__ __forceinline__ int swz_b(int k) { return ((k & 3) << 2) ^ (k & 2); }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff,
-                                           RSRC_WORD3);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor of a raw (stride 0) buffer starting at `base` whose range
+// covers every offset below 2^31; offsets at or past OOB read as zero.
+__device__ __forceinline__ i32x4 rsrc(const void *base) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
+  r[2] = 0x7fffffff;
+  r[3] = RSRC_WORD3;
+  return r;
+}
+
+// 16 bytes per lane from buffer offset `voff` straight into LDS at
+// lds_base + 16 * lane (buffer_load_dwordx4 ... lds).  Issued as inline asm so
+// that the compiler does not add its own waits for it: every wait this kernel
+// needs on these loads (per-stage vmcnt waits before a barrier) is explicit.
+// The instruction writes no register; it reads m0 (the LDS base), which the
+// compiler loads as an input operand.
+__device__ __forceinline__ void dma16(const i32x4 &rs, const void *lds_dst, uint32_t voff) {
+  const uint32_t lds_addr =
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)lds_dst;
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rs), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
 }
 
 // Workgroup b runs on XCD b % 8.  Give every XCD a contiguous run of the tile
@@ -78,21 +109,45 @@ __device__ __forceinline__ void tile_coords(int bid, int tilesM, int tilesN, int
   tn = w / gsz;
 }
 
-template <int EPI, int ACT>
+// Barrier between the waves of the workgroup with no memory fence: the waits
+// it needs are issued explicitly before it.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int EPI, int ACT, int BK, int NST>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tiled_kernel(const GemmArgs p) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
   constexpr int NOUT = DUAL ? BN / 2 : BN;       // output columns per tile
+  constexpr int KK = BK / 16;                    // 16-k MFMA slices per step
+  constexpr int A_BYTES = BM * BK * 2;           // [256 rows][BK k]
+  constexpr int B_BYTES = BK * BN * 2;           // [BK k][256 cols] or 2 x [BK][128]
+  constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  constexpr int AUNITS = BK / 8;                 // 16-byte units per A row
+  constexpr int AROWS_PER_LOAD = 64 / AUNITS;    // A rows one wave-wide 1 KiB load fills
+  constexpr int A_LOADS = A_BYTES / 1024 / 4;    // per wave
   constexpr int BREG = DUAL ? BN / 2 : BN;       // columns per B region
   constexpr int BPITCH = BREG * 2;               // bytes per B row
   constexpr int BUNITS = BREG / 8;               // 16-byte units per B row
   constexpr int BROWS_PER_LOAD = 1024 / BPITCH;  // B rows one wave-wide load fills
-  // Two stages in two distinct arrays: the DMA into one stage and the fragment
-  // reads of the other are then provably disjoint, so the compiler does not
-  // make the reads wait for the DMA.
+  constexpr int B_LOADS = B_BYTES / 1024 / 4;    // per wave
+  constexpr int B_LOADS_PER_REGION = (B_BYTES / 1024) / (DUAL ? 2 : 1);
+  constexpr int LPS = A_LOADS + B_LOADS;         // loads per wave per stage
+  static_assert(NST >= 2 && NST <= 4, "2..4 stages");
+  static_assert(NST * STAGE_BYTES <= 160 * 1024, "LDS");
+
+  // One LDS array per stage.
   __shared__ __attribute__((aligned(1024))) char smem0[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char smem1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem2[NST > 2 ? STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char smem3[NST > 3 ? STAGE_BYTES : 16];
+  char *const stages[4] = {smem0, smem1, smem2, smem3};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int wm = wave >> 1, wn = wave & 1;
   const int tilesM = (int)((p.M + BM - 1) / BM), tilesN = (int)((p.N + NOUT - 1) / NOUT);
   int g, tm, tn;
@@ -105,58 +160,56 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tiled_kernel(const Gemm
   const bf16 *B2 = DUAL ? (const bf16 *)p.B2 + g * p.sB2 + n0 : nullptr;
 
   // ---- per-lane load offsets (bytes, relative to the k-step's base) -------
-  // A: wave w fills rows 64w .. 64w+63 with 8 loads of 8 rows; lane -> row
-  // (lane >> 3), physical unit (lane & 7), i.e. logical unit (lane&7)^swz.
-  uint32_t a_off[8];
-  int a_kof[8];
+  // A: load j of wave w fills rows (A_LOADS w + j) * AROWS_PER_LOAD + lane/AUNITS,
+  // physical unit lane % AUNITS (logical unit = physical ^ swizzle).
+  uint32_t a_off[A_LOADS];
+  int a_kof[A_LOADS];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 64 * wave + 8 * j + (lane >> 3);
-    const int lu = (lane & 7) ^ swz_a(r);
+  for (int j = 0; j < A_LOADS; ++j) {
+    const int r = (A_LOADS * wave + j) * AROWS_PER_LOAD + lane / AUNITS;
+    const int lu = (lane % AUNITS) ^ swz_a<BK>(r);
     a_kof[j] = 8 * lu;
     a_off[j] = (m0 + r < M) ? (uint32_t)((r * p.lda + 8 * lu) * 2) : OOB;
   }
-  // B: 32 wave-wide loads per step (8 per wave), each filling 1 KiB of a B
-  // region = BROWS_PER_LOAD rows; lane -> row (lane / BUNITS), unit lane % BUNITS.
-  uint32_t b_off[8];
-  int b_k[8];
-  bool b_up[8];
+  // B: load j of wave w is load gi = B_LOADS w + j of the tile, filling 1 KiB
+  // of a B region = BROWS_PER_LOAD rows; lane -> row lane / BUNITS, unit
+  // lane % BUNITS.  With SwiGLU the first half of the loads fill the gate
+  // region, the second half the up region (waves 0-1 and 2-3).
+  uint32_t b_off[B_LOADS];
+  int b_k[B_LOADS];
+  const bool b_up = DUAL && (B_LOADS * wave >= B_LOADS_PER_REGION);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int gi = 8 * wave + j;  // 0..31
-    const int region = DUAL ? gi / 16 : 0;
-    const int li = DUAL ? gi % 16 : gi;
+  for (int j = 0; j < B_LOADS; ++j) {
+    const int gi = B_LOADS * wave + j;
+    const int li = gi % B_LOADS_PER_REGION;
     const int k = li * BROWS_PER_LOAD + lane / BUNITS;
     const int lu = (lane % BUNITS) ^ swz_b(k);
     const int64_t col = 8 * lu;  // column offset from n0 within the region
-    const int64_t ld = region ? p.ldb2 : p.ldb;
+    const int64_t ld = b_up ? p.ldb2 : p.ldb;
     b_k[j] = k;
-    b_up[j] = region;
     b_off[j] = (n0 + col < N) ? (uint32_t)((k * ld + col) * 2) : OOB;
   }
 
-  auto issue_loads = [&](int kt, char *stage) {
-    const int64_t k0 = (int64_t)kt * BK;
+  // Loads of k-step kt into `stage`.  Past the last step (kt >= KT) every lane
+  // gets an out-of-range offset: the stage, which nothing reads again, is
+  // filled with zeros and no memory is touched, so the pipeline needs no branch.
+  auto issue_loads = [&](int kt, int KT, char *stage) {
+    const bool live = kt < KT;
+    const int64_t k0 = (int64_t)(live ? kt : 0) * BK;
     char *sa = stage;
     char *sb = sa + A_BYTES;
-    const __amdgpu_buffer_rsrc_t ra = rsrc(A + k0);
+    const i32x4 ra = rsrc(A + k0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t off = (k0 + a_kof[j] < K) ? a_off[j] : OOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(sa + (64 * wave + 8 * j) * 128),
-                                               16, off, 0, 0, 0);
+    for (int j = 0; j < A_LOADS; ++j) {
+      const uint32_t off = (live && k0 + a_kof[j] < K) ? a_off[j] : OOB;
+      dma16(ra, sa + (A_LOADS * wave + j) * 1024, off);
     }
-    const __amdgpu_buffer_rsrc_t rb = rsrc(B + k0 * p.ldb);
-    const __amdgpu_buffer_rsrc_t rb2 = DUAL ? rsrc(B2 + k0 * p.ldb2) : rb;
+    const i32x4 rb = rsrc(b_up ? B2 + k0 * p.ldb2 : B + k0 * p.ldb);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t off = (k0 + b_k[j] < K) ? b_off[j] : OOB;
-      const int gi = 8 * wave + j;
-      char *dst = sb + gi * 1024;  // regions are consecutive, so load gi fills bytes [gi KiB, +1 KiB)
-      if (DUAL && b_up[j])
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb2, (lds_void_t *)dst, 16, off, 0, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)dst, 16, off, 0, 0, 0);
+    for (int j = 0; j < B_LOADS; ++j) {
+      const uint32_t off = (live && k0 + b_k[j] < K) ? b_off[j] : OOB;
+      // regions are consecutive, so load gi fills bytes [gi KiB, +1 KiB)
+      dma16(rb, sb + (B_LOADS * wave + j) * 1024, off);
     }
   };
 
@@ -190,7 +243,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tiled_kernel(const Gemm
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = a_row[i], u = 2 * kk + khalf;
-      fa[buf][i] = *(const bf16x8 *)(base + r * 128 + ((u ^ swz_a(r)) << 4));
+      fa[buf][i] = *(const bf16x8 *)(base + r * (2 * BK) + ((u ^ swz_a<BK>(r)) << 4));
     }
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -226,34 +279,42 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tiled_kernel(const Gemm
   };
 
   const int KT = (int)((K + BK - 1) / BK);
-  // One k-step reading stage `cur` while stage `nxt` is filled for step kt+1
-  // (when there is one).  The MFMAs are unconditional: only loads depend on
-  // has_next, so the accumulators never flow through a branch.
-  auto step = [&](const char *cur, char *nxt, int kt, bool has_next) {
-    if (has_next) issue_loads(kt + 1, nxt);
-    load_frags(cur, 1, 1);
-    mfmas(0);
-    load_frags(cur, 2, 0);
-    mfmas(1);
-    load_frags(cur, 3, 1);
-    mfmas(0);
-    // Every wave's loads of step kt+1 have landed and every wave has read its
-    // last fragments of step kt before any wave moves on.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (has_next) load_frags(nxt, 0, 0);
-    mfmas(1);
+  // One k-step on stage s = kt % NST.  Step kt+NST-1 is loaded into the stage
+  // read by step kt-1 (free once the barrier that ended step kt-1 passed).
+  // Nothing in a step branches: the loads past the end are the zero-filling
+  // kind above, and the fragments read after the last step are never used.
+  auto step = [&](int kt, int s) {
+    issue_loads(kt + NST - 1, KT, stages[(s + NST - 1) % NST]);
+    const char *cur = stages[s];
+#pragma unroll
+    for (int kk = 1; kk < KK; ++kk) {
+      load_frags(cur, kk, kk & 1);
+      mfmas((kk - 1) & 1);
+    }
+    // This wave's loads of step kt+1 have landed (the NST-2 later steps may
+    // still be in flight) and its fragment reads of step kt are done; the
+    // barrier makes that true for every wave.
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((NST - 2) * LPS));
+    wg_barrier();
+    load_frags(stages[(s + 1) % NST], 0, 0);
+    mfmas((KK - 1) & 1);
   };
-  issue_loads(0, smem0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  load_frags(smem0, 0, 0);
+
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) issue_loads(s, KT, stages[s]);
+  __builtin_amdgcn_s_waitcnt(wait_vm((NST - 2) * LPS));
+  wg_barrier();
+  load_frags(stages[0], 0, 0);
   int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
-    step(smem0, smem1, kt, true);
-    step(smem1, smem0, kt + 1, kt + 2 < KT);
+  for (; kt + NST <= KT; kt += NST) {
+#pragma unroll
+    for (int s = 0; s < NST; ++s) step(kt + s, s);
   }
-  if (kt < KT) step(smem0, smem1, kt, false);
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (kt + s < KT) step(kt + s, s);
+  // No load may still be writing LDS when the workgroup releases it.
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
   // ---- epilogue ---------------------------------------------------------------
   // 32x32 accumulator layout: lane holds column (lane & 31) and rows
@@ -306,14 +367,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tiled_kernel(const Gemm
   }
 }
 
+// k-step size and stage count: BK = 64 with 2 stages or BK = 32 with 4
+// stages (both 128 KiB of LDS).
+int tiled_variant() {
+  static int v = [] {
+    const char *e = getenv("TPMLP_TILED_VARIANT");
+    return e ? atoi(e) : 1;
+  }();
+  return v;
+}
+
 template <int EPI, int ACT>
 hipError_t launch_t(const GemmArgs &a, hipStream_t s) {
   const int nout = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + nout - 1) / nout) * a.groups;
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_tiled_kernel<EPI, ACT>), dim3((unsigned)tiles), dim3(NTHREADS), 0,
-                     s, a);
+  switch (tiled_variant()) {
+    case 0:
+      hipLaunchKernelGGL((gemm_bf16_tiled_kernel<EPI, ACT, 64, 2>), dim3((unsigned)tiles),
+                         dim3(NTHREADS), 0, s, a);
+      break;
+    case 2:
+      hipLaunchKernelGGL((gemm_bf16_tiled_kernel<EPI, ACT, 32, 3>), dim3((unsigned)tiles),
+                         dim3(NTHREADS), 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm_bf16_tiled_kernel<EPI, ACT, 32, 4>), dim3((unsigned)tiles),
+                         dim3(NTHREADS), 0, s, a);
+      break;
+  }
   return hipGetLastError();
 }
 
