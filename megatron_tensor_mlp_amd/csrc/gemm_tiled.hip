@@ -5,27 +5,31 @@
 // the token count is large ("Transformer math: tensor parallel", sections on
 // the column- and row-parallel splits; "Tensor Parallelism Explained", 2.B).
 //
-// Tile: 256 rows x 256 accumulator columns x 64 k per step, 256 threads (four
-// wave64s as 2 x 2), each wave owning a 128 x 128 block of the tile as 4 x 4
-// v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, held in AGPRs).
-// For SwiGLU the accumulator columns are 128 gate columns and the same 128 up
-// columns; each wave takes 64 of each, so the gate and up value of an output
-// element sit in the same lane and the epilogue is local.
+// Tile: 256 rows x 256 accumulator columns per workgroup, NWAVE wave64s as
+// 2 x (NWAVE/2), each wave owning 128 rows x (512/NWAVE) columns as blocks of
+// v_mfma_f32_32x32x16_bf16 accumulators.  With 4 waves (one per SIMD) a wave
+// holds 128 x 128 (256 fp32 per lane, in AGPRs); with 8 waves (two per SIMD)
+// 128 x 64, and the SIMD switches to the other wave whenever one waits.  For
+// SwiGLU the accumulator columns are 128 gate columns and the same 128 up
+// columns, and each wave takes equal gate and up slices, so the gate and up
+// value of an output element sit in the same lane and the epilogue is local.
 //
 // Data path: both operands go from HBM to LDS by buffer loads that write LDS
 // directly (no register staging).  Lanes whose element lies outside the
 // matrix get an offset past the buffer's range, which the hardware turns into
 // zeros, so ragged tiles need no special case.
-//   A (row-major [M,K], k contiguous) is kept [row][64 k]; fragments are
+//   A (row-major [M,K], k contiguous) is kept [row][BK k]; fragments are
 //     16-byte reads of 8 consecutive k.
 //   B (row-major [K,N], n contiguous) is kept as it is in memory, [k][n]; the
 //     MFMA wants 8 consecutive k per lane, so fragments are taken with the
 //     transposing LDS read ds_read_b64_tr_b16: 16 lanes that address a 4(k) x
 //     16(n) block each receive one column as 4 consecutive k.
 // Both LDS tiles XOR-swizzle their 16-byte units by row so that the fragment
-// reads hit distinct banks.  LDS holds two stages: the loads of k-step t+1 are
-// in flight while step t's MFMAs run; within a step the fragments of the next
-// 16-k slice are read while the current slice's MFMAs issue.
+// reads hit distinct banks.  LDS holds NST stages of BK k each: the loads of
+// step t+NST-1 are in flight while step t's MFMAs run.  Within a step every
+// 16-k slice issues its MFMAs one by one, each followed by at most two memory
+// instructions (the reads of the next slice's fragments, and the loads of a
+// future step), in an order pinned with sched_barrier.
 #include <cstdlib>
 
 #include "device_common.hpp"
@@ -35,9 +39,11 @@ namespace tpmlp {
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 256, BN = 256, NTHREADS = 256;
+constexpr int BM = 256, BN = 256;
 constexpr int GROUP_M = 4;            // row-tiles walked together for L2 reuse
 constexpr uint32_t OOB = 0x80000000u; // an offset past every buffer range: reads as zero
 constexpr int RSRC_WORD3 = 0x00020000;
@@ -52,15 +58,15 @@ constexpr int wait_vm_lgkm0(int v) { return (v & 15) | (7 << 4) | ((v >> 4) << 1
 //  rows at one logical unit; the mask spreads them over distinct banks.
 template <int BK>
 __device__ __forceinline__ int swz_a(int r) {
-  if constexpr (BK == 64) return ((r >> 1) ^ (r << 2)) & 7;
-  else return ((r >> 1) ^ (r >> 2)) & 3;
+  if constexpr (BK == 64)
+    return ((r >> 1) ^ (r << 2)) & 7;
+  else
+    return ((r >> 1) ^ (r >> 2)) & 3;
 }
 //  B rows (512 or 256 B): a transposing read touches 4 consecutive k rows x
 //  32 or 64 bytes; rows k..k+3 get masks 0, 4, 10, 14 (distinct 64-byte
 //  segments and distinct 32-byte pairs within them).
 __device__ __forceinline__ int swz_b(int k) { return ((k & 3) << 2) ^ (k & 2); }
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer descriptor of a raw (stride 0) buffer starting at `base` whose range
 // covers every offset below 2^31; offsets at or past OOB read as zero.
@@ -118,26 +124,34 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int EPI, int ACT, int BK, int NST>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tiled_kernel(const GemmArgs p) {
+template <int EPI, int ACT, int BK, int NST, int NWAVE>
+__global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const GemmArgs p) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
   constexpr int NOUT = DUAL ? BN / 2 : BN;       // output columns per tile
   constexpr int KK = BK / 16;                    // 16-k MFMA slices per step
+  constexpr int WNW = NWAVE / 2;                 // waves along N
+  constexpr int WN = BN / WNW;                   // accumulator columns per wave
+  constexpr int NB = WN / 32;                    // 32-column B fragments per wave
+  constexpr int NMF = 4 * NB;                    // MFMAs per slice per wave
+  constexpr int NREAD = 4 + 2 * NB;              // LDS reads per slice per wave
   constexpr int A_BYTES = BM * BK * 2;           // [256 rows][BK k]
   constexpr int B_BYTES = BK * BN * 2;           // [BK k][256 cols] or 2 x [BK][128]
   constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   constexpr int AUNITS = BK / 8;                 // 16-byte units per A row
   constexpr int AROWS_PER_LOAD = 64 / AUNITS;    // A rows one wave-wide 1 KiB load fills
-  constexpr int A_LOADS = A_BYTES / 1024 / 4;    // per wave
+  constexpr int A_LOADS = A_BYTES / 1024 / NWAVE;  // per wave
   constexpr int BREG = DUAL ? BN / 2 : BN;       // columns per B region
   constexpr int BPITCH = BREG * 2;               // bytes per B row
   constexpr int BUNITS = BREG / 8;               // 16-byte units per B row
   constexpr int BROWS_PER_LOAD = 1024 / BPITCH;  // B rows one wave-wide load fills
-  constexpr int B_LOADS = B_BYTES / 1024 / 4;    // per wave
+  constexpr int B_LOADS = B_BYTES / 1024 / NWAVE;  // per wave
   constexpr int B_LOADS_PER_REGION = (B_BYTES / 1024) / (DUAL ? 2 : 1);
   constexpr int LPS = A_LOADS + B_LOADS;         // loads per wave per stage
+  constexpr int R0 = (NMF - NREAD) / 2;          // first slot carrying a fragment read
   static_assert(NST >= 2 && NST <= 4, "2..4 stages");
   static_assert(NST * STAGE_BYTES <= 160 * 1024, "LDS");
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && LPS <= NMF, "load split");
+  static_assert(B_LOADS_PER_REGION % B_LOADS == 0, "a wave's B loads stay in one region");
 
   // One LDS array per stage.
   __shared__ __attribute__((aligned(1024))) char smem0[STAGE_BYTES];
@@ -148,7 +162,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tiled_kernel(const Gemm
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
   const int tilesM = (int)((p.M + BM - 1) / BM), tilesN = (int)((p.N + NOUT - 1) / NOUT);
   int g, tm, tn;
   tile_coords(blockIdx.x, tilesM, tilesN, tilesM * tilesN * p.groups, g, tm, tn);
@@ -174,7 +188,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tiled_kernel(const Gemm
   // B: load j of wave w is load gi = B_LOADS w + j of the tile, filling 1 KiB
   // of a B region = BROWS_PER_LOAD rows; lane -> row lane / BUNITS, unit
   // lane % BUNITS.  With SwiGLU the first half of the loads fill the gate
-  // region, the second half the up region (waves 0-1 and 2-3).
+  // region and the second half the up region (the first and second half of
+  // the waves).
   uint32_t b_off[B_LOADS];
   int b_k[B_LOADS];
   const bool b_up = DUAL && (B_LOADS * wave >= B_LOADS_PER_REGION);
@@ -190,26 +205,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tiled_kernel(const Gemm
     b_off[j] = (n0 + col < N) ? (uint32_t)((k * ld + col) * 2) : OOB;
   }
 
-  // Loads of k-step kt into `stage`.  Past the last step (kt >= KT) every lane
-  // gets an out-of-range offset: the stage, which nothing reads again, is
-  // filled with zeros and no memory is touched, so the pipeline needs no branch.
-  auto issue_loads = [&](int kt, int KT, char *stage) {
-    const bool live = kt < KT;
-    const int64_t k0 = (int64_t)(live ? kt : 0) * BK;
-    char *sa = stage;
-    char *sb = sa + A_BYTES;
-    const i32x4 ra = rsrc(A + k0);
-#pragma unroll
-    for (int j = 0; j < A_LOADS; ++j) {
-      const uint32_t off = (live && k0 + a_kof[j] < K) ? a_off[j] : OOB;
-      dma16(ra, sa + (A_LOADS * wave + j) * 1024, off);
-    }
-    const i32x4 rb = rsrc(b_up ? B2 + k0 * p.ldb2 : B + k0 * p.ldb);
-#pragma unroll
-    for (int j = 0; j < B_LOADS; ++j) {
-      const uint32_t off = (live && k0 + b_k[j] < K) ? b_off[j] : OOB;
-      // regions are consecutive, so load gi fills bytes [gi KiB, +1 KiB)
-      dma16(rb, sb + (B_LOADS * wave + j) * 1024, off);
+  // This wave's loads of k-step dkt into `stage`, one at a time (q < LPS).
+  // Past the last step (dkt >= KT) every lane gets an out-of-range offset: the
+  // stage, which nothing reads again, is filled with zeros and no memory is
+  // touched, so the pipeline needs no branch.
+  struct LoadCtx {
+    bool live;
+    int64_t k0;
+    i32x4 ra, rb;
+  };
+  auto load_ctx = [&](int dkt, int KT) {
+    LoadCtx c;
+    c.live = dkt < KT;
+    c.k0 = (int64_t)(c.live ? dkt : 0) * BK;
+    c.ra = rsrc(A + c.k0);
+    c.rb = rsrc(b_up ? B2 + c.k0 * p.ldb2 : B + c.k0 * p.ldb);
+    return c;
+  };
+  auto issue_load = [&](const LoadCtx &c, char *stage, int q) {
+    if (q < A_LOADS) {
+      const uint32_t off = (c.live && c.k0 + a_kof[q] < K) ? a_off[q] : OOB;
+      dma16(c.ra, stage + (A_LOADS * wave + q) * 1024, off);
+    } else {
+      const int j = q - A_LOADS;
+      const uint32_t off = (c.live && c.k0 + b_k[j] < K) ? b_off[j] : OOB;
+      // regions are consecutive, so tile load gi fills bytes [gi KiB, +1 KiB)
+      dma16(c.rb, stage + A_BYTES + (B_LOADS * wave + j) * 1024, off);
     }
   };
 
@@ -222,86 +243,113 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tiled_kernel(const Gemm
   for (int i = 0; i < 4; ++i) a_row[i] = 128 * wm + 32 * i + (lane & 31);
   // B fragment f: columns cb .. cb+31 of a region; 16-lane group g = lane/16
   // reads k rows 16 kk + 8 (g/2) + 4 h + (j/4) and columns cb + 16 (g%2) + 4 (j%4).
-  int b_reg_off[4], b_col[4];
+  int b_reg_off[NB], b_col[NB];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
+  for (int f = 0; f < NB; ++f) {
     int region, cb;
     if (DUAL) {
-      region = f >> 1;
-      cb = 64 * wn + 32 * (f & 1);
+      region = f / (NB / 2);
+      cb = (WN / 2) * wn + 32 * (f % (NB / 2));
     } else {
       region = 0;
-      cb = 128 * wn + 32 * f;
+      cb = WN * wn + 32 * f;
     }
     b_reg_off[f] = A_BYTES + region * (BK * BPITCH);
     b_col[f] = cb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   }
   const int b_krow = 8 * (lane >> 5) + ((lane & 15) >> 2);
 
-  bf16x8 fa[2][4], fb[2][4];
-  auto load_frags = [&](const char *base, int kk, int buf) {
+  bf16x8 fa[2][4], fb[2][NB];
+  s16x4 fbh[2][NB][2];  // B fragments as the two transposing-read halves
+  auto load_a = [&](const char *base, int kk, int i, int buf) {
+    const int r = a_row[i], u = 2 * kk + khalf;
+    fa[buf][i] = *(const bf16x8 *)(base + r * (2 * BK) + ((u ^ swz_a<BK>(r)) << 4));
+  };
+  // Half hh (k 0-3 or 4-7 of the lane's 8) of B fragment f of slice kk.
+  auto load_bh = [&](const char *base, int kk, int f, int hh, int buf) {
+    const int k = 16 * kk + 4 * hh + b_krow;
+    const int c = b_col[f];
+    const int off = b_reg_off[f] + k * BPITCH + (((c >> 3) ^ swz_b(k)) << 4) + ((c & 4) << 1);
+    fbh[buf][f][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(base + off));
+  };
+  auto join_b = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = a_row[i], u = 2 * kk + khalf;
-      fa[buf][i] = *(const bf16x8 *)(base + r * (2 * BK) + ((u ^ swz_a<BK>(r)) << 4));
-    }
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      s16x4 h[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int k = 16 * kk + 4 * hh + b_krow;
-        const int c = b_col[f];
-        const int off = b_reg_off[f] + k * BPITCH + (((c >> 3) ^ swz_b(k)) << 4) + ((c & 4) << 1);
-        h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(base + off));
-      }
-      typedef short s16x8 __attribute__((ext_vector_type(8)));
-      const s16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+    for (int f = 0; f < NB; ++f) {
+      const s16x4 h0 = fbh[buf][f][0], h1 = fbh[buf][f][1];
+      const s16x8 v = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
       fb[buf][f] = __builtin_bit_cast(bf16x8, v);
     }
   };
+  // The NREAD LDS reads of one slice, in the order its MFMAs (i-major) consume
+  // them: B0 (both halves), A0, the other B halves, then A1, A2, A3.
+  auto load_piece = [&](const char *base, int kk, int buf, int q) {
+    if (q < 2)
+      load_bh(base, kk, 0, q, buf);
+    else if (q == 2)
+      load_a(base, kk, 0, buf);
+    else if (q < 1 + 2 * NB)
+      load_bh(base, kk, (q - 1) / 2, (q - 1) % 2, buf);
+    else
+      load_a(base, kk, q - 2 * NB, buf);
+  };
+  auto load_frags = [&](const char *base, int kk, int buf) {
+#pragma unroll
+    for (int q = 0; q < NREAD; ++q) load_piece(base, kk, buf, q);
+    join_b(buf);
+  };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < NB; ++f)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][f][v] = 0.0f;
 
-  auto mfmas = [&](int buf) {
+  // One slice of MFMAs on buffer `buf` (i-major), interleaved slot by slot
+  // with up to two memory instructions: the reads of the next slice into
+  // buffer `nbuf` and, when `dctx` is given, this wave's loads of a future
+  // k-step into `dstage` (slots 0..LPS-1).  sched_barrier(0) pins the order,
+  // so fragment reads stay a full slice ahead of their use.
+  auto slice = [&](int buf, const char *nbase, int nkk, int nbuf, const LoadCtx *dctx,
+                   char *dstage) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-        acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][f], acc[i][f], 0,
-                                                            0, 0);
+    for (int t = 0; t < NMF; ++t) {
+      const int i = t / NB, f = t % NB;
+      acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][f], acc[i][f], 0,
+                                                          0, 0);
+      if (dctx && t < LPS) issue_load(*dctx, dstage, t);
+      if (t >= R0 && t < R0 + NREAD) load_piece(nbase, nkk, nbuf, t - R0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    join_b(nbuf);
   };
 
   const int KT = (int)((K + BK - 1) / BK);
   // One k-step on stage s = kt % NST.  Step kt+NST-1 is loaded into the stage
-  // read by step kt-1 (free once the barrier that ended step kt-1 passed).
-  // Nothing in a step branches: the loads past the end are the zero-filling
-  // kind above, and the fragments read after the last step are never used.
+  // read by step kt-1 (free once the barrier that ended step kt-1 passed);
+  // past the last step those loads are the zero-filling kind and the
+  // fragments read after the last step are never used, so nothing branches.
   auto step = [&](int kt, int s) {
-    issue_loads(kt + NST - 1, KT, stages[(s + NST - 1) % NST]);
     const char *cur = stages[s];
+    const LoadCtx c = load_ctx(kt + NST - 1, KT);
 #pragma unroll
-    for (int kk = 1; kk < KK; ++kk) {
-      load_frags(cur, kk, kk & 1);
-      mfmas((kk - 1) & 1);
-    }
+    for (int kk = 1; kk < KK; ++kk)
+      slice((kk - 1) & 1, cur, kk, kk & 1, kk == 1 ? &c : nullptr, stages[(s + NST - 1) % NST]);
     // This wave's loads of step kt+1 have landed (the NST-2 later steps may
     // still be in flight) and its fragment reads of step kt are done; the
     // barrier makes that true for every wave.
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((NST - 2) * LPS));
     wg_barrier();
-    load_frags(stages[(s + 1) % NST], 0, 0);
-    mfmas((KK - 1) & 1);
+    slice((KK - 1) & 1, stages[(s + 1) % NST], 0, 0, nullptr, nullptr);
   };
 
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s) issue_loads(s, KT, stages[s]);
+  for (int s = 0; s < NST - 1; ++s) {
+    const LoadCtx c = load_ctx(s, KT);
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) issue_load(c, stages[s], q);
+  }
   __builtin_amdgcn_s_waitcnt(wait_vm((NST - 2) * LPS));
   wg_barrier();
   load_frags(stages[0], 0, 0);
@@ -323,8 +371,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tiled_kernel(const Gemm
   if constexpr (EPI == EPI_F32) {
     float *C = (float *)p.C + g * p.sC;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int64_t col = n0 + 128 * wn + 32 * f + (lane & 31);
+    for (int f = 0; f < NB; ++f) {
+      const int64_t col = n0 + WN * wn + 32 * f + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -337,23 +385,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tiled_kernel(const Gemm
   } else if constexpr (DUAL) {
     bf16 *C = (bf16 *)p.C + g * p.sC;
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int64_t col = n0 + 64 * wn + 32 * f + (lane & 31);
+    for (int f = 0; f < NB / 2; ++f) {
+      const int64_t col = n0 + (WN / 2) * wn + 32 * f + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
-          if (row < M) C[row * p.ldc + col] = to_bf16(silu(acc[i][f][v]) * acc[i][f + 2][v]);
+          if (row < M)
+            C[row * p.ldc + col] = to_bf16(silu(acc[i][f][v]) * acc[i][f + NB / 2][v]);
         }
     }
   } else {
     bf16 *C = (bf16 *)p.C + g * p.sC;
     const bf16 *bias = p.bias ? (const bf16 *)p.bias + g * p.sBias : nullptr;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int64_t col = n0 + 128 * wn + 32 * f + (lane & 31);
+    for (int f = 0; f < NB; ++f) {
+      const int64_t col = n0 + WN * wn + 32 * f + (lane & 31);
       if (col >= N) continue;
       const float bv = bias ? (float)bias[col] : 0.0f;
 #pragma unroll
@@ -367,14 +416,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_tiled_kernel(const Gemm
   }
 }
 
-// k-step size and stage count: BK = 64 with 2 stages or BK = 32 with 4
-// stages (both 128 KiB of LDS).
+// Tile-loop configuration: (BK, stages, waves).  Variant 1 is the default.
 int tiled_variant() {
   static int v = [] {
     const char *e = getenv("TPMLP_TILED_VARIANT");
     return e ? atoi(e) : 1;
   }();
   return v;
+}
+
+template <int EPI, int ACT, int BK, int NST, int NWAVE>
+void launch_cfg(const GemmArgs &a, int64_t tiles, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_bf16_tiled_kernel<EPI, ACT, BK, NST, NWAVE>), dim3((unsigned)tiles),
+                     dim3(NWAVE * 64), 0, s, a);
 }
 
 template <int EPI, int ACT>
@@ -385,16 +439,16 @@ hipError_t launch_t(const GemmArgs &a, hipStream_t s) {
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   switch (tiled_variant()) {
     case 0:
-      hipLaunchKernelGGL((gemm_bf16_tiled_kernel<EPI, ACT, 64, 2>), dim3((unsigned)tiles),
-                         dim3(NTHREADS), 0, s, a);
+      launch_cfg<EPI, ACT, 32, 4, 4>(a, tiles, s);
       break;
     case 2:
-      hipLaunchKernelGGL((gemm_bf16_tiled_kernel<EPI, ACT, 32, 3>), dim3((unsigned)tiles),
-                         dim3(NTHREADS), 0, s, a);
+      launch_cfg<EPI, ACT, 64, 2, 8>(a, tiles, s);
+      break;
+    case 3:
+      launch_cfg<EPI, ACT, 32, 3, 8>(a, tiles, s);
       break;
     default:
-      hipLaunchKernelGGL((gemm_bf16_tiled_kernel<EPI, ACT, 32, 4>), dim3((unsigned)tiles),
-                         dim3(NTHREADS), 0, s, a);
+      launch_cfg<EPI, ACT, 32, 4, 8>(a, tiles, s);
       break;
   }
   return hipGetLastError();
