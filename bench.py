@@ -5,9 +5,10 @@
 A step is one forward of one GPU's shard of the Llama-70B SwiGLU MLP at TP = 8
 (T = 4096 tokens, d = 8192, k/p = 3584): the column step (X Wg_i, X Wu_i,
 SiLU(g) * u -> bf16 Y_i) then the row step (Y_i W2_i -> fp32 partial Z_i),
-i.e. the two launches tp_mlp_shard makes, issued one by one so HIP events can
-bracket each kernel on the stream it runs on.  Inputs are seeded synthetic
-bf16 tensors already resident in HBM.
+i.e. the two launches tp_mlp_shard makes.  Inputs are seeded synthetic bf16
+tensors already resident in HBM.  The timed region is bracketed by HIP events
+on the launch stream; per-kernel durations come from HIP-graph replays (events
+only at the ends of a batch of launches).
 
 Prints ONE JSON line.  `value` is the step's algorithmic TFLOP/s (2*T*d*(k/p)
 flops per GEMM, three GEMMs).  Secondary fields report the few-token (decode)
@@ -65,34 +66,57 @@ def recorded_traffic(kernel_tag):
     return float(m.group(1))
 
 
-def time_events(torch, fn_list, steps, warmup):
-    """Run `steps` iterations of the launches in fn_list (after `warmup`), with
-    an event before and after each launch on the current stream.  Returns
-    (total seconds, per-launch mean seconds list)."""
+def time_graph(torch, fn_list, steps, warmup, per_replay=5):
+    """Capture `per_replay` rounds of the launches in fn_list into one HIP graph
+    and time `steps` replays (after `warmup`): GPU time per round, without
+    host launch gaps.  Every launch is run once eagerly first so nothing is
+    allocated during capture."""
+    for fn in fn_list:
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(per_replay):
+                for fn in fn_list:
+                    fn()
+    torch.cuda.synchronize()
+    for _ in range(max(1, warmup)):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / (steps * per_replay)
+
+
+def time_steps(torch, fn_list, steps, warmup):
+    """Wall time of `steps` rounds of the launches in fn_list (after `warmup`),
+    bracketed by a synchronisation and an event pair on the current stream."""
     for _ in range(warmup):
         for fn in fn_list:
             fn()
     torch.cuda.synchronize()
-    n = len(fn_list)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for j in range(steps):
-        evs[j][0].record()
-        for q, fn in enumerate(fn_list):
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        for fn in fn_list:
             fn()
-            evs[j][q + 1].record()
-    end.record()
+    e1.record()
     torch.cuda.synchronize()
-    total = start.elapsed_time(end) / 1e3
-    per = [sum(evs[j][q].elapsed_time(evs[j][q + 1]) for j in range(steps)) / steps / 1e3
-           for q in range(n)]
-    return total, per
+    return e0.elapsed_time(e1) / 1e3
 
 
 def headline(torch, tp, synth, steps, warmup):
+    """The timed region: `steps` shard forwards back to back.  Per-kernel
+    durations come from HIP-graph replays of each launch alone (events only at
+    the ends of a replay batch, so no event sits between two kernels)."""
     W = synth.WORKLOADS["llama70b_prefill_tp8"]
     dev = "cuda:0"
     Wg, Wu, W2 = (t.to(dev) for t in synth.llama_shard_weights(W.d, W.s))
@@ -101,7 +125,10 @@ def headline(torch, tp, synth, steps, warmup):
     Z = torch.empty(W.T, W.d, dtype=torch.float32, device=dev)
     col = lambda: tp.tp_col_linear(X, Wg, 0, 1, Y, act="swiglu", Wu=Wu)  # noqa: E731
     row = lambda: tp.tp_row_linear(Y, W2, 0, 1, Z)  # noqa: E731
-    total, (t_col, t_row) = time_events(torch, [col, row], steps, warmup)
+    total = time_steps(torch, [col, row], steps, warmup)
+    reps = max(2, steps // 4)
+    t_col = time_graph(torch, [col], reps, 1, per_replay=4)
+    t_row = time_graph(torch, [row], reps, 1, per_replay=4)
     flops_col = 2.0 * W.T * W.d * W.s * 2
     flops_row = 2.0 * W.T * W.d * W.s
     return dict(W=W, total=total, t_col=t_col, t_row=t_row, flops_col=flops_col,
@@ -109,8 +136,10 @@ def headline(torch, tp, synth, steps, warmup):
 
 
 def decode_bench(torch, tp, synth, steps, warmup, copies=3):
-    """Few-token shard; weights rotate over `copies` copies (>= 528 MB) so the
-    256 MB Infinity Cache cannot hold them."""
+    """Few-token shard (column step then row step, the launches tp_mlp_shard
+    makes); weights rotate over `copies` copies (>= 528 MB) so the 256 MB
+    Infinity Cache cannot hold them.  Timed by HIP-graph replay: a decode step
+    is ~20-50 us of GPU work, where host launch gaps would otherwise count."""
     W = synth.WORKLOADS["llama70b_decode_tp8"]
     dev = "cuda:0"
     base = [t.to(dev) for t in synth.llama_shard_weights(W.d, W.s)]
@@ -122,17 +151,16 @@ def decode_bench(torch, tp, synth, steps, warmup, copies=3):
         Y = torch.empty(T, W.s, dtype=torch.bfloat16, device=dev)
         Z = torch.empty(T, W.d, dtype=torch.float32, device=dev)
         ws = tp.workspace(tp.tp_workspace_bytes(torch.bfloat16, "swiglu", T, W.d, W.s, 1), dev)
-        fns = []
+        cols, rows = [], []
         for (Wg, Wu, W2) in sets:
-            fns.append(lambda Wg=Wg, Wu=Wu: tp.tp_col_linear(X, Wg, 0, 1, Y, act="swiglu", Wu=Wu,
-                                                              ws=ws))
-            fns.append(lambda W2=W2: tp.tp_row_linear(Y, W2, 0, 1, Z, ws=ws))
-        reps = max(1, steps)
-        total, per = time_events(torch, fns, reps, warmup)
-        step = total / (reps * copies)
+            cols.append(lambda Wg=Wg, Wu=Wu: tp.tp_col_linear(X, Wg, 0, 1, Y, act="swiglu", Wu=Wu,
+                                                               ws=ws))
+            rows.append(lambda W2=W2: tp.tp_row_linear(Y, W2, 0, 1, Z, ws=ws))
+        both = [f for pair in zip(cols, rows) for f in pair]
+        step = time_graph(torch, both, steps, warmup) / copies
+        t_col = time_graph(torch, cols, steps, warmup) / copies
+        t_row = time_graph(torch, rows, steps, warmup) / copies
         alg_bytes = wbytes + T * W.d * 2 + 2 * T * W.s * 2 + T * W.d * 4
-        t_col = sum(per[0::2]) / copies
-        t_row = sum(per[1::2]) / copies
         out[f"T{T}"] = {
             "us_per_step": round(step * 1e6, 2),
             "GBps": round(alg_bytes / step / 1e9, 1),
@@ -143,23 +171,24 @@ def decode_bench(torch, tp, synth, steps, warmup, copies=3):
         }
     out["weight_bytes"] = wbytes
     out["rotation_copies"] = copies
+    out["timing"] = "HIP graph replay"
     return out
 
 
 def partial_sum_bench(torch, tp, steps, warmup, copies=3):
-    """C5's reduction: 8 fp32 [512, 8192] partials -> Z, rotating over copies."""
+    """The simulated TP=8 block's reduction: 8 fp32 [512, 8192] partials -> Z,
+    rotating over copies; HIP-graph replay."""
     dev = "cuda:0"
     p, T, d = 8, 512, 8192
     bufs = [torch.randn(p, T, d, device=dev) for _ in range(copies)]
     Zs = [torch.empty(T, d, device=dev) for _ in range(copies)]
     fns = [lambda b=b, z=z: tp.tp_partial_sum([b[q] for q in range(p)], z) for b, z in
            zip(bufs, Zs)]
-    total, per = time_events(torch, fns, max(1, steps), warmup)
-    t = sum(per) / copies
+    t = time_graph(torch, fns, max(1, steps), warmup) / copies
     nbytes = (p + 1) * T * d * 4
     return {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
             "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4), "bytes": nbytes,
-            "rotation_copies": copies}
+            "rotation_copies": copies, "timing": "HIP graph replay"}
 
 
 def simulated_block_bench(torch, tp, synth, steps, warmup):
@@ -171,7 +200,7 @@ def simulated_block_bench(torch, tp, synth, steps, warmup):
     Zp = torch.empty(W.p, W.T, W.d, device=dev)
     Z = torch.empty(W.T, W.d, device=dev)
     fn = lambda: tp.tp_mlp_simulated(X, Wg, W2, W.p, Y, Zp, Z, act="swiglu", Wu=Wu)  # noqa: E731
-    total, (t,) = time_events(torch, [fn], max(1, steps), warmup)
+    t = time_graph(torch, [fn], max(1, steps), warmup, per_replay=2)
     flops = 2.0 * W.T * W.d * W.k * 3
     return {"us": round(t * 1e6, 1), "TFLOPs": round(flops / t / 1e12, 1),
             "frac_mfma": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
@@ -185,9 +214,10 @@ def gpt_bench(torch, tp, synth, steps, warmup):
     Z = torch.empty(W.T, W.d, device=dev)
     col = lambda: tp.tp_col_linear(X, W1, 0, 1, Y, act="gelu_tanh", b1=b1)  # noqa: E731
     row = lambda: tp.tp_row_linear(Y, W2, 0, 1, Z)  # noqa: E731
-    total, (tc, tr) = time_events(torch, [col, row], max(1, steps), warmup)
+    t = time_graph(torch, [col, row], max(1, steps), warmup)
+    tc = time_graph(torch, [col], max(1, steps), warmup)
+    tr = time_graph(torch, [row], max(1, steps), warmup)
     flops = 2.0 * W.T * W.d * W.s * 2
-    t = tc + tr
     return {"us": round(t * 1e6, 1), "TFLOPs": round(flops / t / 1e12, 1),
             "frac_mfma": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
             "col_us": round(tc * 1e6, 1), "row_us": round(tr * 1e6, 1)}
@@ -230,6 +260,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline only")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 256 MiB device copy (the reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's shard; runs on more than one GPU are not part of "
@@ -282,6 +314,11 @@ def main():
                                                           2)
         log("bench: gpt gelu shard")
         result["gpt_gelu_shard"] = gpt_bench(torch, tp, synth, max(5, args.steps // 2), 3)
+    if args.copy_calibration:
+        a = torch.empty(64 << 20, device="cuda:0")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(synth)
