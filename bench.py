@@ -36,6 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 TILED_SOURCES = ["megatron_tensor_mlp_amd/csrc/gemm_tiled.hip",
+                 "megatron_tensor_mlp_amd/csrc/lds_dma.hpp",
                  "megatron_tensor_mlp_amd/csrc/device_common.hpp",
                  "megatron_tensor_mlp_amd/csrc/kernels.h"]
 

@@ -178,10 +178,10 @@ tp_status tp_mlp_simulated(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_
 /*
  * Bytes of workspace that tp_col_linear / tp_row_linear / tp_mlp_shard /
  * tp_mlp_simulated need for these sizes (0 if none).  The workspace holds
- * split-K partial sums and arrival counters of the few-token (T <= 64) path.
- * It must be zero-filled before its first use; every call leaves its counters
- * zero again, so one zeroed buffer can be reused by any later call on the same
- * stream.  Returns 0 for invalid arguments.
+ * the split-K partial sums and arrival counters of the few-token (T <= 64)
+ * path.  It must be zero-filled before its first use; every call leaves its
+ * counters zero again, so one zeroed buffer can be reused by any later call on
+ * the same stream.  Returns 0 for invalid arguments.
  */
 size_t tp_workspace_bytes(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t p);
 

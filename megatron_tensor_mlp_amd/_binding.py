@@ -131,8 +131,8 @@ _ws_cache: dict = {}
 
 def workspace(nbytes: int, device) -> torch.Tensor | None:
     """A zero-filled device buffer of at least nbytes, cached per device.  The
-    library leaves its counters zero after every call, so the buffer can be
-    reused by later calls on the same stream."""
+    library leaves its arrival counters zero after every call, so the buffer
+    can be reused by later calls on the same stream."""
     if nbytes <= 0:
         return None
     dev = torch.device(device)

@@ -34,6 +34,7 @@
 
 #include "device_common.hpp"
 #include "kernels.h"
+#include "lds_dma.hpp"
 
 namespace tpmlp {
 namespace {
@@ -41,17 +42,9 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256;
 constexpr int GROUP_M = 4;            // row-tiles walked together for L2 reuse
-constexpr uint32_t OOB = 0x80000000u; // an offset past every buffer range: reads as zero
-constexpr int RSRC_WORD3 = 0x00020000;
-
-// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= v only.
-constexpr int wait_vm(int v) { return (v & 15) | (7 << 4) | (15 << 8) | ((v >> 4) << 14); }
-// ... and for lgkmcnt == 0 as well.
-constexpr int wait_vm_lgkm0(int v) { return (v & 15) | (7 << 4) | ((v >> 4) << 14); }
 
 // XOR masks on the 16-byte unit index of an LDS row.
 //  A rows (2*BK bytes = BK/8 units): fragment reads touch 8 or 16 consecutive
@@ -67,33 +60,6 @@ __device__ __forceinline__ int swz_a(int r) {
 //  32 or 64 bytes; rows k..k+3 get masks 0, 4, 10, 14 (distinct 64-byte
 //  segments and distinct 32-byte pairs within them).
 __device__ __forceinline__ int swz_b(int k) { return ((k & 3) << 2) ^ (k & 2); }
-
-// Buffer descriptor of a raw (stride 0) buffer starting at `base` whose range
-// covers every offset below 2^31; offsets at or past OOB read as zero.
-__device__ __forceinline__ i32x4 rsrc(const void *base) {
-  const uint64_t a = (uint64_t)base;
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
-  r[2] = 0x7fffffff;
-  r[3] = RSRC_WORD3;
-  return r;
-}
-
-// 16 bytes per lane from buffer offset `voff` straight into LDS at
-// lds_base + 16 * lane (buffer_load_dwordx4 ... lds).  Issued as inline asm so
-// that the compiler does not add its own waits for it: every wait this kernel
-// needs on these loads (per-stage vmcnt waits before a barrier) is explicit.
-// The instruction writes no register; it reads m0 (the LDS base), which the
-// compiler loads as an input operand.
-__device__ __forceinline__ void dma16(const i32x4 &rs, const void *lds_dst, uint32_t voff) {
-  const uint32_t lds_addr =
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)lds_dst;
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rs), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory");
-}
 
 // Workgroup b runs on XCD b % 8.  Give every XCD a contiguous run of the tile
 // order (a bijection for any total), then walk GROUP_M row-tiles at a time so
@@ -113,15 +79,6 @@ __device__ __forceinline__ void tile_coords(int bid, int tilesM, int tilesN, int
   const int w = u - grp * span;
   tm = first + w % gsz;
   tn = w / gsz;
-}
-
-// Barrier between the waves of the workgroup with no memory fence: the waits
-// it needs are issued explicitly before it.  The empty asm statements keep the
-// compiler from moving memory accesses across it.
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 template <int EPI, int ACT, int BK, int NST, int NWAVE>

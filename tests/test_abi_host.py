@@ -90,7 +90,7 @@ def test_workspace_bytes():
     # many tokens: tiled path, no workspace
     assert tp.tp_workspace_bytes(bf16, "swiglu", 4096, 8192, 28672, 8) == 0
     assert tp.tp_workspace_bytes(torch.float32, "gelu_tanh", 4, 512, 2048, 4) == 0
-    # decode shapes split K and need partials + counters
+    # decode shapes split K and need partial sums + arrival counters
     for T in (1, 8, 64):
         assert tp.tp_workspace_bytes(bf16, "swiglu", T, 8192, 28672, 8) > 0
     # invalid arguments report 0

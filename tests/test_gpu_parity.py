@@ -197,7 +197,8 @@ def test_bad_degree_leaves_output_untouched():
 
 def test_workspace_reuse_and_determinism():
     """One zeroed workspace serves consecutive few-token calls of different shapes
-    (the counters are left zero), and the split-K reduction is deterministic."""
+    (the arrival counters are left zero), and the split-K reduction is
+    deterministic."""
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
     outs = []
     for T, d, k, p in ((8, 1032, 4096, 2), (64, 520, 2048, 4), (8, 1032, 4096, 2)):
