@@ -136,15 +136,23 @@ def headline(torch, tp, synth, steps, warmup):
                 flops_row=flops_row, step_flops=flops_col + flops_row)
 
 
-def decode_bench(torch, tp, synth, steps, warmup, copies=3):
+def decode_bench(torch, tp, synth, steps, warmup, rotate_bytes=600 << 20):
     """Few-token shard (column step then row step, the launches tp_mlp_shard
-    makes); weights rotate over `copies` copies (>= 528 MB) so the 256 MB
-    Infinity Cache cannot hold them.  Timed by HIP-graph replay: a decode step
-    is ~20-50 us of GPU work, where host launch gaps would otherwise count."""
+    makes).  Weights rotate over enough copies that every timed sequence
+    touches more than 2x the 256 MB Infinity Cache before it comes back to a
+    copy (the step: 4 x 176 MB; the column step alone: 6 x 117 MB; the row
+    step alone: 11 x 59 MB), so they are read from HBM.  Timed by HIP-graph
+    replay: a decode step is ~20-50 us of GPU work, where host launch gaps
+    would otherwise count."""
     W = synth.WORKLOADS["llama70b_decode_tp8"]
     dev = "cuda:0"
     base = [t.to(dev) for t in synth.llama_shard_weights(W.d, W.s)]
-    sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+    col_bytes = 2 * W.d * W.s * 2
+    row_bytes = W.s * W.d * 2
+    ncol = -(-rotate_bytes // col_bytes)
+    nrow = -(-rotate_bytes // row_bytes)
+    copies = -(-rotate_bytes // (col_bytes + row_bytes))
+    sets = [base] + [[t.clone() for t in base] for _ in range(max(ncol, nrow) - 1)]
     out = {}
     wbytes = sum(t.numel() * t.element_size() for t in base)
     for T in W.Ts:
@@ -157,10 +165,10 @@ def decode_bench(torch, tp, synth, steps, warmup, copies=3):
             cols.append(lambda Wg=Wg, Wu=Wu: tp.tp_col_linear(X, Wg, 0, 1, Y, act="swiglu", Wu=Wu,
                                                                ws=ws))
             rows.append(lambda W2=W2: tp.tp_row_linear(Y, W2, 0, 1, Z, ws=ws))
-        both = [f for pair in zip(cols, rows) for f in pair]
+        both = [f for pair in zip(cols[:copies], rows[:copies]) for f in pair]
         step = time_graph(torch, both, steps, warmup) / copies
-        t_col = time_graph(torch, cols, steps, warmup) / copies
-        t_row = time_graph(torch, rows, steps, warmup) / copies
+        t_col = time_graph(torch, cols[:ncol], steps, warmup) / ncol
+        t_row = time_graph(torch, rows[:nrow], steps, warmup) / nrow
         alg_bytes = wbytes + T * W.d * 2 + 2 * T * W.s * 2 + T * W.d * 4
         out[f"T{T}"] = {
             "us_per_step": round(step * 1e6, 2),
@@ -171,7 +179,7 @@ def decode_bench(torch, tp, synth, steps, warmup, copies=3):
             "row_GBps": round((W.s * W.d * 2) / t_row / 1e9, 1),
         }
     out["weight_bytes"] = wbytes
-    out["rotation_copies"] = copies
+    out["rotation_copies"] = {"step": copies, "col": ncol, "row": nrow}
     out["timing"] = "HIP graph replay"
     return out
 

@@ -8,7 +8,9 @@
 // buffer loads that write LDS directly, a few stages deep (about 32 KiB in
 // flight per CU measured best), without holding a register; the token rows
 // (padded to 16, 32 or 64 with zeros) come along in the same stages.  Each
-// weight row is read in runs of 256 contiguous bytes.  Each of the 8 waves
+// weight row is read in runs of 256 contiguous bytes, with the nontemporal
+// hint (weights are read once per step; the token rows, read by every
+// workgroup, stay cached).  Each of the 8 waves
 // owns a 16-column block: per 32-k slice it takes its weight fragment with the
 // transposing LDS read ds_read_b64_tr_b16 (the weights stay [k][n] as stored)
 // and multiplies it with v_mfma_f32_16x16x32_bf16.  LDS rows are XOR-swizzled
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(NWAVE * 64) void gemm_bf16_decode_kernel(const Gemm
 #pragma unroll
     for (int j = 0; j < G::WL; ++j) {
       const uint32_t off = (live && k0 + w_row[j] < kend) ? w_off[j] : OOB;
-      dma16(rw, st + (G::WL * wave + j) * 1024, off);
+      dma16_nt(rw, st + (G::WL * wave + j) * 1024, off);
     }
 #pragma unroll
     for (int j = 0; j < G::XL; ++j) {

@@ -51,6 +51,16 @@ __device__ __forceinline__ void dma16(const i32x4 &rs, const void *lds_dst, uint
                : "memory");
 }
 
+// The same with the nontemporal hint, for data read exactly once (streamed
+// weights): the lines are not kept in the caches, so they do not displace data
+// that is reused.
+__device__ __forceinline__ void dma16_nt(const i32x4 &rs, const void *lds_dst, uint32_t voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds"
+               :
+               : "v"(voff), "s"(rs), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_dst)))
+               : "memory");
+}
+
 // 4 bytes per lane from buffer offset `voff` into LDS at lds_dst + 4 * lane.
 __device__ __forceinline__ void dma4(const i32x4 &rs, const void *lds_dst, uint32_t voff) {
   asm volatile("buffer_load_dword %0, %1, 0 offen lds"
