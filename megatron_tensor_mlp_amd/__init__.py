@@ -2,8 +2,9 @@
 GeLU/SwiGLU, row-parallel linear to an fp32 partial, on-device partial sum).
 
 This package is a thin ctypes binding over ``libtpmlp.so`` (declared in
-``include/tpmlp.h``): it turns torch tensors into pointers, sizes and leading
-dimensions, and the current torch stream into a ``hipStream_t``.  Every step of
+``include/tpmlp.h``, with a measurement aid in ``include/tpmlp_calib.h``): it
+turns torch tensors into pointers, sizes and leading dimensions, and the
+current torch stream into a ``hipStream_t``.  Every step of
 the computation runs in the library's HIP kernels; if the library is missing,
 every call raises.  torch is used for device memory and streams only.
 """
@@ -16,6 +17,7 @@ from ._binding import (  # noqa: F401
     library,
     library_path,
     tp_abi_version,
+    tp_calib_mfma_bf16,
     tp_col_linear,
     tp_mlp_shard,
     tp_mlp_simulated,
@@ -27,7 +29,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "ACT", "DTYPE", "TpError", "library", "library_path", "tp_abi_version", "tp_col_linear",
-    "tp_mlp_shard", "tp_mlp_simulated", "tp_partial_sum", "tp_row_linear", "tp_shard_bounds",
-    "tp_workspace_bytes", "workspace",
+    "ACT", "DTYPE", "TpError", "library", "library_path", "tp_abi_version", "tp_calib_mfma_bf16",
+    "tp_col_linear", "tp_mlp_shard", "tp_mlp_simulated", "tp_partial_sum", "tp_row_linear",
+    "tp_shard_bounds", "tp_workspace_bytes", "workspace",
 ]

@@ -66,8 +66,9 @@ def library():
     lib.tp_last_error_message.restype = ctypes.c_char_p
     lib.tp_abi_version.argtypes = []
     lib.tp_abi_version.restype = i32
+    lib.tp_calib_mfma_bf16.argtypes = [i32, i64, vp, i32, vp]
     for name in ("tp_col_linear", "tp_row_linear", "tp_mlp_shard", "tp_partial_sum",
-                 "tp_mlp_simulated", "tp_shard_bounds"):
+                 "tp_mlp_simulated", "tp_shard_bounds", "tp_calib_mfma_bf16"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -112,6 +113,15 @@ def _act(act) -> int:
 
 def tp_abi_version() -> int:
     return library().tp_abi_version()
+
+
+def tp_calib_mfma_bf16(gaussian: bool, iters: int, stats, stream=None):
+    """Enqueue the MFMA calibration kernel (include/tpmlp_calib.h): one
+    workgroup per pair of entries of `stats` (a device int64 tensor of 2*nwg)."""
+    if stats.dtype != torch.int64 or not stats.is_cuda or stats.numel() % 2:
+        raise ValueError("stats must be a device int64 tensor of even length")
+    _check(library().tp_calib_mfma_bf16(1 if gaussian else 0, iters, _ptr(stats),
+                                        stats.numel() // 2, _stream(stream)))
 
 
 def tp_shard_bounds(k: int, i: int, p: int):

@@ -8,6 +8,7 @@
 #include <string>
 
 #include "../../include/tpmlp.h"
+#include "../../include/tpmlp_calib.h"
 #include "kernels.h"
 
 using namespace tpmlp;
@@ -429,3 +430,13 @@ const char *tp_last_error_message(void) { return g_msg.c_str(); }
 int32_t tp_abi_version(void) { return TPMLP_ABI_VERSION; }
 
 }  // extern "C"
+
+extern "C" tp_status tp_calib_mfma_bf16(int32_t gaussian, int64_t iters, uint64_t *stats,
+                                        int32_t nwg, void *stream) {
+  if (nwg < 1 || iters < 1)
+    return fail(TP_ERR_BAD_SHAPE, "nwg = %d and iters = %lld must be >= 1", nwg, (long long)iters);
+  if (!stats) return fail(TP_ERR_NULL_POINTER, "stats is NULL");
+  const hipError_t e = launch_calib_mfma(gaussian ? 1 : 0, iters, stats, nwg, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}

@@ -40,6 +40,10 @@ hipError_t launch_gemm_bf16_tiled(const GemmArgs &a, hipStream_t s);
 size_t decode_workspace_bytes(const GemmArgs &a);
 hipError_t launch_gemm_bf16_decode(const GemmArgs &a, void *ws, hipStream_t s);
 
+// MFMA throughput / shader-clock calibration (measurement aid).
+hipError_t launch_calib_mfma(int gaussian, int64_t iters, uint64_t *stats, int nwg,
+                             hipStream_t s);
+
 // fp32 path (correctness-first): one output per thread, k ascending.
 hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s);
 

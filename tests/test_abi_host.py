@@ -1,5 +1,5 @@
-"""Host-side tests of the C ABI: the library loads, exports what include/tpmlp.h
-declares, does its shard bookkeeping, and rejects bad arguments before any
+"""Host-side tests of the C ABI: the library loads, exports what include/*.h
+declare, does its shard bookkeeping, and rejects bad arguments before any
 launch.  No GPU is used: the error-path cases pass fake (never dereferenced)
 pointers and are skipped whenever a GPU is visible, so no kernel can ever see
 them."""
@@ -15,22 +15,24 @@ import megatron_tensor_mlp_amd as tp
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tpmlp.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
                             reason="fake-pointer error paths run only where no GPU is visible")
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tp_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tp_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("tp_col_linear", "tp_row_linear", "tp_mlp_shard", "tp_partial_sum",
               "tp_mlp_simulated", "tp_workspace_bytes", "tp_shard_bounds", "tp_status_string",
-              "tp_last_error_message", "tp_abi_version"):
+              "tp_last_error_message", "tp_abi_version", "tp_calib_mfma_bf16"):
         assert n in names
 
 
@@ -210,3 +212,11 @@ def test_simulated_rejects_page_example_degree():
     st = lib.tp_mlp_simulated(1, 2, 4, 64, 64, 5, P(A), 64, P(A), 64, None, 0, None, P(A), 64,
                               None, P(A), P(A), P(A), 64, None, 0, None)
     assert status_name(st) == "TP_ERR_NOT_DIVISIBLE"
+
+
+@no_gpu
+def test_calibration_errors():
+    lib = tp.library()
+    assert status_name(lib.tp_calib_mfma_bf16(1, 0, P(A), 4, None)) == "TP_ERR_BAD_SHAPE"
+    assert status_name(lib.tp_calib_mfma_bf16(1, 10, P(A), 0, None)) == "TP_ERR_BAD_SHAPE"
+    assert status_name(lib.tp_calib_mfma_bf16(0, 10, None, 4, None)) == "TP_ERR_NULL_POINTER"
