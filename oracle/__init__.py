@@ -24,6 +24,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# The mutation test of the pins (tests/test_oracle_mutants.py) points this at a
+# deliberately broken build of oracle.c; nothing else sets it.
+_LIB_OVERRIDE = os.environ.get("TPMLP_ORACLE_LIB")
 
 # The oracle's own activation numbering (see oracle.c).
 ACT_NONE, ACT_RELU, ACT_GELU_TANH, ACT_GELU_ERF, ACT_SWIGLU = 0, 1, 2, 3, 4
@@ -53,8 +56,11 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build()
+            lib = ctypes.CDLL(_LIB)
         i64, i32, ci = ctypes.c_int64, ctypes.c_int32, ctypes.c_int
         vp = ctypes.c_void_p
         lib.oracle_col_shard_f64.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, vp, ci, vp]

@@ -74,6 +74,49 @@ def test_shard_bf16_small(T, d, k, p, act):
         assert_bf16_close(Z, Zr, "Z")
 
 
+# Few-token path: shapes chosen for the split-K plan's corners (k-ranges per
+# column block S, the token-block size, the k tail of a stage).
+DECODE_CASES = [
+    # (T, d, k, p, act, what)
+    (3, 264, 16384, 1, "swiglu", "column step: 256 workgroups, S = 1 (gate+up pair); row step S ~ 74"),
+    (20, 136, 32768, 1, "gelu_tanh", "column step: S = 1, no partials; row step S = 128"),
+    (40, 520, 1000, 1, "relu", "64-row stages with a k tail (520, 1000 not multiples of 64)"),
+    (16, 264, 1024, 4, "swiglu", "16 tokens: the largest single token block"),
+    (17, 264, 1024, 4, "gelu_erf", "17 tokens: two token blocks"),
+    (32, 264, 1024, 4, "swiglu", "32 tokens"),
+    (33, 264, 1024, 4, "none", "33 tokens: four token blocks"),
+]
+
+
+@pytest.mark.parametrize("T,d,k,p,act,what", DECODE_CASES)
+def test_decode_plan_corners(T, d, k, p, act, what):
+    sw = act == "swiglu"
+    X, W1, Wu, b1, W2 = synth.small_case(T, d, k, 300 + T, sw, bias=not sw)
+    for i in sorted({0, p - 1}):
+        say(f"decode case T={T} d={d} k={k} p={p} act={act} i={i}: {what}")
+        Y, Z = run_shard(X, W1, W2, i, p, act, Wu=Wu, b1=b1)
+        Yr, Zr = oracle.mlp_shard(f64(X), f64(W1), f64(W2), i, p, act, b1=f64(b1) if b1 is not None
+                                  else None, Wu=f64(Wu) if Wu is not None else None)
+        assert_bf16_close(Y, Yr, "Y")
+        assert_bf16_close(Z, Zr, "Z")
+
+
+def test_decode_counters_left_zero():
+    """The split-K arrival counters (the first bytes of the workspace) are zero
+    again after every few-token call."""
+    T, d, k = 8, 1032, 4096
+    X, W1, Wu, _, W2 = synth.small_case(T, d, k, 9, True, False)
+    need = tp.tp_workspace_bytes(torch.bfloat16, "swiglu", T, d, k, 1)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    Y = torch.empty(T, k, dtype=torch.bfloat16, device=DEV)
+    Z = torch.empty(T, d, device=DEV)
+    for _ in range(3):
+        tp.tp_mlp_shard(dev(X), dev(W1), dev(W2), 0, 1, Y, Z, act="swiglu", Wu=dev(Wu), ws=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+
+
 @pytest.mark.parametrize("T", [5, 300])
 def test_padded_leading_dimensions(T):
     """Views with leading dimensions above the row width (padding filled with NaN)."""

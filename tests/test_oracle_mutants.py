@@ -1,0 +1,78 @@
+"""The pins catch planted mistakes: each mutant below is a copy of oracle.c with
+one plausible error (a dropped term, a wrong sign, constant, index or operand
+order, a swapped gate/up, a mis-sliced bias), built with gcc; the CPU pin suite
+(tests/test_oracle_pins.py) run against it in a subprocess must fail.  All of
+this happens on the CPU; the GPU path is not involved."""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+# (name, text in oracle.c, replacement, which occurrence: 0 = first, -1 = all)
+MUTANTS = [
+    ("gelu_tanh drops the cubic term", "tanh(c * (x + 0.044715 * x * x * x))", "tanh(c * x)", 0),
+    ("gelu_tanh wrong coefficient", "0.044715 * x * x * x)))", "0.04715 * x * x * x)))", 0),
+    ("gelu_erf wrong scale", "erf(x / sqrt(2.0))", "erf(x / 2.0)", 0),
+    ("silu wrong sign", "return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));", 0),
+    ("relu leaks", "return x > 0.0 ? x : 0.0;", "return x > 0.0 ? x : 0.01 * x;", 0),
+    ("column shards in reverse order", "const int64_t s = k / p, c0 = (int64_t)i * s;",
+     "const int64_t s = k / p, c0 = (int64_t)(p - 1 - i) * s;", 0),
+    ("column bias not sliced", "const double v = b1 ? h[j] + b1[c0 + j] : h[j];",
+     "const double v = b1 ? h[j] + b1[j] : h[j];", 0),
+    ("swiglu gate and up swapped", "h[j] = act_scalar_f64(OR_ACT_SWIGLU, h[j]) * u[j];",
+     "h[j] = act_scalar_f64(OR_ACT_SWIGLU, u[j]) * h[j];", 0),
+    ("row shard reads W2 transposed",
+     "const double *w = W2 + (c0 + j) * d;\n      for (int64_t n = 0; n < d; ++n) z[n] += yv * w[n];",
+     "for (int64_t n = 0; n < d; ++n) z[n] += yv * W2[n * k + c0 + j];", 0),
+    ("partial sum drops the last shard", "for (int32_t q = 1; q < p; ++q) acc += parts[(int64_t)q * n + e];",
+     "for (int32_t q = 1; q < p - 1; ++q) acc += parts[(int64_t)q * n + e];", 0),
+    ("partial sum forgets b2", "if (b2) acc += b2[e % d];", "", 0),
+    ("unsharded MLP reads W2 transposed", "z[n] += yv * W2[j * d + n];", "z[n] += yv * W2[n * k + j];", 0),
+    ("fp32 linear reads W transposed", "h[j] += xv * W[c * k + j];", "h[j] += xv * W[j * d + c];", 0),
+    ("fp32 column shard wrong offset", "const float *w = W1 + c * k + c0;",
+     "const float *w = W1 + c * k + (c0 > 0 ? c0 - 1 : c0);", 0),
+]
+
+
+def build_mutant(text, old, new, which, out):
+    assert old in text, old
+    if which == 0:
+        text = text.replace(old, new, 1)
+    else:
+        text = text.replace(old, new)
+    src = out + ".c"
+    with open(src, "w") as f:
+        f.write(text)
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-ffp-contract=off", "-std=c11", "-D_DEFAULT_SOURCE",
+                    "-fPIC", "-shared", "-o", out, src, "-lm"], check=True)
+
+
+@pytest.mark.parametrize("name,old,new,which", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new, which):
+    text = open(SRC).read()
+    with tempfile.TemporaryDirectory() as tmp:
+        lib = os.path.join(tmp, "liboracle_mutant.so")
+        build_mutant(text, old, new, which, lib)
+        env = dict(os.environ, TPMLP_ORACLE_LIB=lib, OMP_NUM_THREADS="4")
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant '{name}' survived the pins:\n{r.stdout[-2000:]}"
+
+
+def test_unmutated_copy_passes():
+    """Control: the same procedure on an unchanged copy passes the pins."""
+    text = open(SRC).read()
+    with tempfile.TemporaryDirectory() as tmp:
+        lib = os.path.join(tmp, "liboracle_copy.so")
+        build_mutant(text, "#include <math.h>", "#include <math.h>", 0, lib)
+        env = dict(os.environ, TPMLP_ORACLE_LIB=lib, OMP_NUM_THREADS="4")
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-2000:]
