@@ -34,6 +34,10 @@
  *   - Alignment: every data pointer must be 16-byte aligned, and d, k/p and
  *     every leading dimension must be a multiple of 8 elements (bf16) or
  *     4 elements (fp32); otherwise TP_ERR_MISALIGNED.
+ *   - Range (bf16): the kernels address memory with 32-bit offsets, so every
+ *     leading dimension must be below 2^23 elements (ldx below 2^21 when
+ *     T > 64), and with T <= 64 the output width (k/p, or d) at most 8388608
+ *     columns; otherwise TP_ERR_BAD_SHAPE.
  *   - T = 0 is valid and launches nothing; the token-sized buffers (X, Y, Z,
  *     the partials) may then be NULL.
  *   - Memory: all tensors are device memory owned by the caller.  The library

@@ -35,6 +35,8 @@ tp_status ok() {
 // Few-token path threshold: at or below this many tokens the shard is a
 // weight-streaming problem (HBM-bound), above it a tiled MFMA problem.
 constexpr int64_t kDecodeMaxT = 64;
+// Column blocks of 128 the few-token path's workspace counters can track.
+constexpr int64_t kDecodeMaxCols = 65536 * 128;
 
 size_t elem_size(tp_dtype dt) { return dt == TP_BF16 ? 2 : 4; }
 int64_t elem_align(tp_dtype dt) { return dt == TP_BF16 ? 8 : 4; }
@@ -202,6 +204,21 @@ size_t gemm_ws_bytes(tp_dtype dt, const GemmArgs &a) {
   return decode_workspace_bytes(a);
 }
 
+// The bf16 kernels address memory with 32-bit buffer offsets from a tile's or
+// stage's base; shapes beyond that range are rejected here, before any launch.
+tp_status check_gemm(tp_dtype dt, const GemmArgs &a) {
+  if (dt != TP_BF16 || a.M <= 0) return TP_OK;
+  const bool fits =
+      a.M <= kDecodeMaxT ? gemm_bf16_decode_supported(a) : gemm_bf16_tiled_supported(a);
+  if (!fits)
+    return fail(TP_ERR_BAD_SHAPE,
+                "shape beyond the bf16 kernels' offset range: leading dimensions must be below "
+                "2^21 (X, more than 64 tokens) or 2^23 elements, and at most %lld output columns "
+                "with 64 or fewer tokens",
+                (long long)kDecodeMaxCols);
+  return TP_OK;
+}
+
 tp_status run_gemm(tp_dtype dt, const GemmArgs &a, void *ws, hipStream_t st) {
   hipError_t e;
   if (dt == TP_F32)
@@ -278,6 +295,7 @@ tp_status tp_col_linear(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k
   TRY(validate_col(c));
   if (T == 0) return ok();
   const GemmArgs a = col_gemm(c, 1, 0);
+  TRY(check_gemm(dt, a));
   TRY(check_ws(gemm_ws_bytes(dt, a), ws, ws_bytes));
   TRY(run_gemm(dt, a, ws, (hipStream_t)stream));
   return ok();
@@ -290,6 +308,7 @@ tp_status tp_row_linear(tp_dtype dt, int64_t T, int64_t d, int64_t k, int32_t i,
   TRY(validate_row(r));
   if (T == 0) return ok();
   const GemmArgs a = row_gemm(r, 1, 0, 0);
+  TRY(check_gemm(dt, a));
   TRY(check_ws(gemm_ws_bytes(dt, a), ws, ws_bytes));
   TRY(run_gemm(dt, a, ws, (hipStream_t)stream));
   return ok();
@@ -306,6 +325,8 @@ tp_status tp_mlp_shard(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k,
   TRY(validate_row(r));
   if (T == 0) return ok();
   const GemmArgs ac = col_gemm(c, 1, 0), ar = row_gemm(r, 1, 0, 0);
+  TRY(check_gemm(dt, ac));
+  TRY(check_gemm(dt, ar));
   TRY(check_ws(max_sz(gemm_ws_bytes(dt, ac), gemm_ws_bytes(dt, ar)), ws, ws_bytes));
   TRY(run_gemm(dt, ac, ws, (hipStream_t)stream));
   TRY(run_gemm(dt, ar, ws, (hipStream_t)stream));
@@ -362,6 +383,8 @@ tp_status tp_mlp_simulated(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_
   if (b2) TRY(check_ptr("b2", b2));
   if (T == 0) return ok();
   const GemmArgs ac = col_gemm(c, p, T * s), ar = row_gemm(r, p, T * s, T * d);
+  TRY(check_gemm(dt, ac));
+  TRY(check_gemm(dt, ar));
   TRY(check_ws(max_sz(gemm_ws_bytes(dt, ac), gemm_ws_bytes(dt, ar)), ws, ws_bytes));
   TRY(run_gemm(dt, ac, ws, (hipStream_t)stream));
   TRY(run_gemm(dt, ar, ws, (hipStream_t)stream));

@@ -49,7 +49,11 @@ constexpr int RP = RC * 2;      // bytes per weight row in LDS
 // The split aims at about one workgroup per CU of a 256-CU device.
 constexpr int TARGET_WGS = 256;
 constexpr int MIN_STAGES = 4;   // fewest k-steps a workgroup streams
-constexpr int CTR_BYTES = 256;  // counter area rounding
+// The workspace starts with a counter area of fixed size, so that calls with
+// different plans reusing one workspace never take another call's partials
+// for counters: counters of any plan lie below CTR_AREA and partials above it.
+constexpr int64_t MAX_BLOCKS = 65536;             // column blocks per call
+constexpr size_t CTR_AREA = MAX_BLOCKS * sizeof(unsigned);
 
 // Geometry of one configuration: a stage holds BK k rows of 128 columns and
 // the matching token rows.
@@ -128,12 +132,11 @@ DecodePlan make_plan(const GemmArgs &a) {
   return pl;
 }
 
-size_t ctr_bytes(int64_t nblk) { return ((size_t)nblk * 4 + CTR_BYTES - 1) / CTR_BYTES * CTR_BYTES; }
 
 size_t plan_ws_bytes(const DecodePlan &pl) {
   const int64_t parts = pl.S * pl.nmat;  // workgroups per block
   if (parts <= 1) return 0;
-  return ctr_bytes(pl.nblk) +
+  return CTR_AREA +
          (size_t)pl.nblk * parts * (NWAVE * pl.mb * 256) * sizeof(float);
 }
 
@@ -382,7 +385,7 @@ hipError_t launch_plan(const GemmArgs &a, const DecodePlan &pl, void *ws, hipStr
   float *parts = nullptr;
   if (pl.S * pl.nmat > 1) {
     ctr = (unsigned *)ws;
-    parts = (float *)((char *)ws + ctr_bytes(pl.nblk));
+    parts = (float *)((char *)ws + CTR_AREA);
   }
   hipLaunchKernelGGL((gemm_bf16_decode_kernel<EPI, ACT, MB, BK, NST>),
                      dim3((unsigned)(pl.nblk * pl.nmat * pl.S)), dim3(NWAVE * 64), 0, st, a,
@@ -431,9 +434,10 @@ size_t decode_workspace_bytes(const GemmArgs &a) { return plan_ws_bytes(make_pla
 
 bool gemm_bf16_decode_supported(const GemmArgs &a) {
   // Per-lane buffer offsets are 32-bit byte offsets from a stage's k base:
-  // 64 weight rows and 64 token rows must stay below 2^31 bytes.
+  // 64 weight rows and 64 token rows must stay below 2^31 bytes.  The column
+  // blocks of one call must fit the counter area.
   return a.M >= 1 && a.M <= 64 && a.lda < (int64_t(1) << 23) && a.ldb < (int64_t(1) << 23) &&
-         (a.epi != EPI_SWIGLU || a.ldb2 < (int64_t(1) << 23));
+         (a.epi != EPI_SWIGLU || a.ldb2 < (int64_t(1) << 23)) && (a.N + RC - 1) / RC <= MAX_BLOCKS;
 }
 
 hipError_t launch_gemm_bf16_decode(const GemmArgs &a, void *ws, hipStream_t st) {

@@ -43,7 +43,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-constexpr int BM = 256, BN = 256;
+constexpr int BN = 256;               // tile columns (SwiGLU: 128 gate + 128 up)
 constexpr int GROUP_M = 4;            // row-tiles walked together for L2 reuse
 
 // XOR masks on the 16-byte unit index of an LDS row.
@@ -81,17 +81,18 @@ __device__ __forceinline__ void tile_coords(int bid, int tilesM, int tilesN, int
   tn = w / gsz;
 }
 
-template <int EPI, int ACT, int BK, int NST, int NWAVE>
+template <int EPI, int ACT, int BK, int NST, int NWAVE, int BM>
 __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const GemmArgs p) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU);
   constexpr int NOUT = DUAL ? BN / 2 : BN;       // output columns per tile
   constexpr int KK = BK / 16;                    // 16-k MFMA slices per step
-  constexpr int WNW = NWAVE / 2;                 // waves along N
+  constexpr int WMW = BM / 128;                  // waves along M (128 rows each)
+  constexpr int WNW = NWAVE / WMW;               // waves along N
   constexpr int WN = BN / WNW;                   // accumulator columns per wave
   constexpr int NB = WN / 32;                    // 32-column B fragments per wave
   constexpr int NMF = 4 * NB;                    // MFMAs per slice per wave
   constexpr int NREAD = 4 + 2 * NB;              // LDS reads per slice per wave
-  constexpr int A_BYTES = BM * BK * 2;           // [256 rows][BK k]
+  constexpr int A_BYTES = BM * BK * 2;           // [BM rows][BK k]
   constexpr int B_BYTES = BK * BN * 2;           // [BK k][256 cols] or 2 x [BK][128]
   constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   constexpr int AUNITS = BK / 8;                 // 16-byte units per A row
@@ -106,6 +107,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
   constexpr int LPS = A_LOADS + B_LOADS;         // loads per wave per stage
   constexpr int R0 = (NMF - NREAD) / 2;          // first slot carrying a fragment read
   static_assert(NST >= 2 && NST <= 4, "2..4 stages");
+  static_assert((BM == 128 || BM == 256) && NWAVE % WMW == 0, "tile rows");
   static_assert(NST * STAGE_BYTES <= 160 * 1024, "LDS");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && LPS <= NMF, "load split");
   static_assert(B_LOADS_PER_REGION % B_LOADS == 0, "a wave's B loads stay in one region");
@@ -373,7 +375,9 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
   }
 }
 
-// Tile-loop configuration: (BK, stages, waves).  Variant 1 is the default.
+// Tile-loop configuration: (BK, stages, waves, tile rows).  Variant 1 is the
+// default (256-row tiles, or 128-row tiles for small problems); 0, 2, 3 and 4
+// force one configuration, for sweeps.
 int tiled_variant() {
   static int v = [] {
     const char *e = getenv("TPMLP_TILED_VARIANT");
@@ -382,30 +386,41 @@ int tiled_variant() {
   return v;
 }
 
-template <int EPI, int ACT, int BK, int NST, int NWAVE>
-void launch_cfg(const GemmArgs &a, int64_t tiles, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_bf16_tiled_kernel<EPI, ACT, BK, NST, NWAVE>), dim3((unsigned)tiles),
+template <int EPI, int ACT, int BK, int NST, int NWAVE, int BM>
+void launch_cfg(const GemmArgs &a, hipStream_t s) {
+  const int nout = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + nout - 1) / nout) * a.groups;
+  hipLaunchKernelGGL((gemm_bf16_tiled_kernel<EPI, ACT, BK, NST, NWAVE, BM>), dim3((unsigned)tiles),
                      dim3(NWAVE * 64), 0, s, a);
 }
+
+// Tiles of 256 rows at most fill half of a 256-CU device: switch to 128-row
+// tiles (4 waves of 128 x 64), twice as many, for problems that small.
+constexpr int64_t SMALL_TILE_MAX = 128;
 
 template <int EPI, int ACT>
 hipError_t launch_t(const GemmArgs &a, hipStream_t s) {
   const int nout = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + nout - 1) / nout) * a.groups;
+  const int64_t tiles = ((a.M + 255) / 256) * ((a.N + nout - 1) / nout) * a.groups;
   if (tiles <= 0) return hipSuccess;
-  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  switch (tiled_variant()) {
+  if (2 * tiles > 0x7fffffff) return hipErrorInvalidValue;
+  int v = tiled_variant();
+  if (v == 1 && tiles <= SMALL_TILE_MAX) v = 4;
+  switch (v) {
     case 0:
-      launch_cfg<EPI, ACT, 32, 4, 4>(a, tiles, s);
+      launch_cfg<EPI, ACT, 32, 4, 4, 256>(a, s);
       break;
     case 2:
-      launch_cfg<EPI, ACT, 64, 2, 8>(a, tiles, s);
+      launch_cfg<EPI, ACT, 64, 2, 8, 256>(a, s);
       break;
     case 3:
-      launch_cfg<EPI, ACT, 32, 3, 8>(a, tiles, s);
+      launch_cfg<EPI, ACT, 32, 3, 8, 256>(a, s);
+      break;
+    case 4:
+      launch_cfg<EPI, ACT, 32, 4, 4, 128>(a, s);
       break;
     default:
-      launch_cfg<EPI, ACT, 32, 4, 8>(a, tiles, s);
+      launch_cfg<EPI, ACT, 32, 4, 8, 256>(a, s);
       break;
   }
   return hipGetLastError();

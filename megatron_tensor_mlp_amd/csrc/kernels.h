@@ -32,12 +32,17 @@ struct GemmArgs {
   int64_t sA, sB, sB2, sBias, sC;
 };
 
-// Large-T path: MFMA tiles staged through LDS.
+// Large-T path: MFMA tiles staged through LDS.  _supported: the shape fits the
+// kernels' 32-bit buffer offsets.
+bool gemm_bf16_tiled_supported(const GemmArgs &a);
 hipError_t launch_gemm_bf16_tiled(const GemmArgs &a, hipStream_t s);
 
 // Few-token path (M <= 64): weight-streaming split-K GEMM.  `ws` must hold
 // decode_workspace_bytes(a) zero-initialised bytes (or 0 bytes if that is 0).
+// _supported: 1 <= M <= 64 and the shape fits the kernels' 32-bit buffer
+// offsets and the workspace's counter area.
 size_t decode_workspace_bytes(const GemmArgs &a);
+bool gemm_bf16_decode_supported(const GemmArgs &a);
 hipError_t launch_gemm_bf16_decode(const GemmArgs &a, void *ws, hipStream_t s);
 
 // MFMA throughput / shader-clock calibration (measurement aid).

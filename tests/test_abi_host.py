@@ -141,6 +141,8 @@ def status_name(code):
     (dict(act=4, Wu=A, ldwu=128, b1=A), "TP_ERR_BAD_ACT"),  # bias with SwiGLU
     (dict(b1=MIS), "TP_ERR_MISALIGNED"),
     (dict(T=1, d=8192, ldx=8192, k=28672, ldw1=28672, p=8, ldy=3584), "TP_ERR_WORKSPACE"),
+    (dict(T=100, ldx=1 << 21), "TP_ERR_BAD_SHAPE"),     # beyond the tiled kernels' offsets
+    (dict(T=4, ldw1=1 << 23), "TP_ERR_BAD_SHAPE"),      # beyond the few-token kernels' offsets
 ])
 def test_col_linear_rejects(kw, expect):
     assert status_name(col(**kw)) == expect

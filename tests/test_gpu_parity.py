@@ -277,6 +277,31 @@ def sampled_rows(T, n):
     return sorted(r for r in rows if 0 <= r < T)
 
 
+# Tiled path, 256-row tiles: the small cases above have few tiles and take the
+# 128-row configuration, so these shapes (more than 128 tiles of 256 rows, with
+# ragged row and column tails) cover the 256-row kernels; rows are sampled.
+TILE256_CASES = [
+    # (T, d, k, act, what)
+    (1000, 1032, 4296, "swiglu", "column step 4 x 34 tiles (ragged T and k)"),
+    (1000, 520, 8504, "gelu_erf", "column step 4 x 34 tiles with bias"),
+    (1000, 8456, 1024, "relu", "row step 4 x 34 tiles (ragged d)"),
+]
+
+
+@pytest.mark.parametrize("T,d,k,act,what", TILE256_CASES)
+def test_tiled_256_rows_ragged(T, d, k, act, what):
+    sw = act == "swiglu"
+    X, W1, Wu, b1, W2 = synth.small_case(T, d, k, 500 + d, sw, bias=not sw)
+    say(f"tiled-256 case T={T} d={d} k={k} act={act}: {what}")
+    Y, Z = run_shard(X, W1, W2, 0, 1, act, Wu=Wu, b1=b1)
+    rows = sampled_rows(T, 24)
+    Yr, Zr = oracle.mlp_shard(f64(X[rows]), f64(W1), f64(W2), 0, 1, act,
+                              b1=f64(b1) if b1 is not None else None,
+                              Wu=f64(Wu) if Wu is not None else None)
+    assert_bf16_close(Y[rows], Yr, "Y")
+    assert_bf16_close(Z[rows], Zr, "Z")
+
+
 def test_gpt_gelu_shard_full_size():
     """GPT-style GeLU shard at d = 4096, k/p = 4096 (compact shard), T = 2048."""
     W = synth.WORKLOADS["gpt_gelu_p4"]
