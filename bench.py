@@ -86,14 +86,44 @@ def time_graph(torch, fn_list, steps, warmup, per_replay=5):
     for _ in range(max(1, warmup)):
         graph.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for r in range(steps):
         graph.replay()
-    e1.record()
+        ev[r + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / 1e3 / (steps * per_replay)
+    per = [ev[r].elapsed_time(ev[r + 1]) / 1e3 / per_replay for r in range(steps)]
+    global LAST_SPREAD
+    LAST_SPREAD = spread(per)
+    return ev[0].elapsed_time(ev[steps]) / 1e3 / (steps * per_replay)
+
+
+LAST_SPREAD = None
+
+
+def spread(times):
+    """Median, p10 and p90 of per-iteration times (seconds), in microseconds."""
+    t = sorted(times)
+    q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]  # noqa: E731
+    return {"median_us": round(q(0.5) * 1e6, 2), "p10_us": round(q(0.1) * 1e6, 2),
+            "p90_us": round(q(0.9) * 1e6, 2), "iterations": len(t)}
+
+
+def time_each(torch, fn_list, n, warmup):
+    """Per-iteration times of n rounds of the launches in fn_list (after
+    `warmup`), with an event pair around every round on the current stream."""
+    for _ in range(warmup):
+        for fn in fn_list:
+            fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record()
+    for r in range(n):
+        for fn in fn_list:
+            fn()
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    return [ev[r].elapsed_time(ev[r + 1]) / 1e3 for r in range(n)]
 
 
 def time_steps(torch, fn_list, steps, warmup):
@@ -114,10 +144,27 @@ def time_steps(torch, fn_list, steps, warmup):
     return e0.elapsed_time(e1) / 1e3
 
 
+RAMP_S = 0.15
+
+
+def ramp(torch, fn_list, seconds=RAMP_S):
+    """Run rounds of fn_list for `seconds` of wall time.  After idling, the GPU
+    starts a sustained MFMA load at a low clock and needs ~50 prefill steps
+    (~35 ms) to reach its steady state (per-step time 850 -> 625 us); this
+    runs before the warm-up so that the timed steps measure that state."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            for fn in fn_list:
+                fn()
+        torch.cuda.synchronize()
+
+
 def headline(torch, tp, synth, steps, warmup):
-    """The timed region: `steps` shard forwards back to back.  Per-kernel
-    durations come from HIP-graph replays of each launch alone (events only at
-    the ends of a replay batch, so no event sits between two kernels)."""
+    """The timed region: `steps` shard forwards back to back, after the clock
+    ramp and `warmup` untimed steps.  Per-kernel durations come from HIP-graph
+    replays of each launch alone (events only at the ends of a replay batch,
+    so no event sits between two kernels)."""
     W = synth.WORKLOADS["llama70b_prefill_tp8"]
     dev = "cuda:0"
     Wg, Wu, W2 = (t.to(dev) for t in synth.llama_shard_weights(W.d, W.s))
@@ -126,13 +173,18 @@ def headline(torch, tp, synth, steps, warmup):
     Z = torch.empty(W.T, W.d, dtype=torch.float32, device=dev)
     col = lambda: tp.tp_col_linear(X, Wg, 0, 1, Y, act="swiglu", Wu=Wu)  # noqa: E731
     row = lambda: tp.tp_row_linear(Y, W2, 0, 1, Z)  # noqa: E731
+    ramp(torch, [col, row])
     total = time_steps(torch, [col, row], steps, warmup)
+    step_spread = spread(time_each(torch, [col, row], 50, 10))
     reps = max(2, steps // 4)
     t_col = time_graph(torch, [col], reps, 1, per_replay=4)
+    col_spread = LAST_SPREAD
     t_row = time_graph(torch, [row], reps, 1, per_replay=4)
+    row_spread = LAST_SPREAD
     flops_col = 2.0 * W.T * W.d * W.s * 2
     flops_row = 2.0 * W.T * W.d * W.s
-    return dict(W=W, total=total, t_col=t_col, t_row=t_row, flops_col=flops_col,
+    return dict(W=W, total=total, t_col=t_col, t_row=t_row, step_spread=step_spread,
+                col_spread=col_spread, row_spread=row_spread, flops_col=flops_col,
                 flops_row=flops_row, step_flops=flops_col + flops_row)
 
 
@@ -166,7 +218,9 @@ def decode_bench(torch, tp, synth, steps, warmup, rotate_bytes=600 << 20):
                                                                ws=ws))
             rows.append(lambda W2=W2: tp.tp_row_linear(Y, W2, 0, 1, Z, ws=ws))
         both = [f for pair in zip(cols[:copies], rows[:copies]) for f in pair]
-        step = time_graph(torch, both, steps, warmup) / copies
+        step = time_graph(torch, both, max(steps, 20), warmup) / copies
+        step_spread = {k: (round(v / copies, 2) if k.endswith("_us") else v)
+                       for k, v in LAST_SPREAD.items()}
         t_col = time_graph(torch, cols[:ncol], steps, warmup) / ncol
         t_row = time_graph(torch, rows[:nrow], steps, warmup) / nrow
         alg_bytes = wbytes + T * W.d * 2 + 2 * T * W.s * 2 + T * W.d * 4
@@ -174,6 +228,7 @@ def decode_bench(torch, tp, synth, steps, warmup, rotate_bytes=600 << 20):
             "us_per_step": round(step * 1e6, 2),
             "GBps": round(alg_bytes / step / 1e9, 1),
             "frac_hbm": round(alg_bytes / step / 1e9 / PEAK_HBM_GBS, 4),
+            "step_spread": step_spread,
             "col_us": round(t_col * 1e6, 2), "row_us": round(t_row * 1e6, 2),
             "col_GBps": round((2 * W.d * W.s * 2) / t_col / 1e9, 1),
             "row_GBps": round((W.s * W.d * 2) / t_row / 1e9, 1),
@@ -184,20 +239,22 @@ def decode_bench(torch, tp, synth, steps, warmup, rotate_bytes=600 << 20):
     return out
 
 
-def partial_sum_bench(torch, tp, steps, warmup, copies=3):
+def partial_sum_bench(torch, tp, steps, warmup, copies=4):
     """The simulated TP=8 block's reduction: 8 fp32 [512, 8192] partials -> Z,
-    rotating over copies; HIP-graph replay."""
+    rotating over `copies` sets (4 x 151 MB, more than twice the 256 MB
+    Infinity Cache); HIP-graph replay."""
     dev = "cuda:0"
     p, T, d = 8, 512, 8192
     bufs = [torch.randn(p, T, d, device=dev) for _ in range(copies)]
     Zs = [torch.empty(T, d, device=dev) for _ in range(copies)]
     fns = [lambda b=b, z=z: tp.tp_partial_sum([b[q] for q in range(p)], z) for b, z in
            zip(bufs, Zs)]
-    t = time_graph(torch, fns, max(1, steps), warmup) / copies
+    t = time_graph(torch, fns, max(20, steps), warmup) / copies
+    sp = {k: (round(v / copies, 2) if k.endswith("_us") else v) for k, v in LAST_SPREAD.items()}
     nbytes = (p + 1) * T * d * 4
     return {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
             "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4), "bytes": nbytes,
-            "rotation_copies": copies, "timing": "HIP graph replay"}
+            "spread": sp, "rotation_copies": copies, "timing": "HIP graph replay"}
 
 
 def simulated_block_bench(torch, tp, synth, steps, warmup):
@@ -209,10 +266,12 @@ def simulated_block_bench(torch, tp, synth, steps, warmup):
     Zp = torch.empty(W.p, W.T, W.d, device=dev)
     Z = torch.empty(W.T, W.d, device=dev)
     fn = lambda: tp.tp_mlp_simulated(X, Wg, W2, W.p, Y, Zp, Z, act="swiglu", Wu=Wu)  # noqa: E731
-    t = time_graph(torch, [fn], max(1, steps), warmup, per_replay=2)
+    ramp(torch, [fn])
+    t = time_graph(torch, [fn], max(10, steps), warmup, per_replay=2)
+    sp = LAST_SPREAD
     flops = 2.0 * W.T * W.d * W.k * 3
     return {"us": round(t * 1e6, 1), "TFLOPs": round(flops / t / 1e12, 1),
-            "frac_mfma": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            "frac_mfma": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4), "spread": sp}
 
 
 def gpt_bench(torch, tp, synth, steps, warmup):
@@ -223,12 +282,14 @@ def gpt_bench(torch, tp, synth, steps, warmup):
     Z = torch.empty(W.T, W.d, device=dev)
     col = lambda: tp.tp_col_linear(X, W1, 0, 1, Y, act="gelu_tanh", b1=b1)  # noqa: E731
     row = lambda: tp.tp_row_linear(Y, W2, 0, 1, Z)  # noqa: E731
-    t = time_graph(torch, [col, row], max(1, steps), warmup)
+    ramp(torch, [col, row])
+    t = time_graph(torch, [col, row], max(20, steps), warmup)
+    sp = LAST_SPREAD
     tc = time_graph(torch, [col], max(1, steps), warmup)
     tr = time_graph(torch, [row], max(1, steps), warmup)
     flops = 2.0 * W.T * W.d * W.s * 2
     return {"us": round(t * 1e6, 1), "TFLOPs": round(flops / t / 1e12, 1),
-            "frac_mfma": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "frac_mfma": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4), "spread": sp,
             "col_us": round(tc * 1e6, 1), "row_us": round(tr * 1e6, 1)}
 
 
@@ -287,8 +348,16 @@ def cpu_baseline(synth, target_s=12.0):
     oracle.mlp_shard(X[:rows], Wg, W2, 0, 1, "swiglu", Wu=Wu)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * W.d * W.s * 3
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu, "wall_s": round(dt, 2),
             "sample": f"first {rows} of {W.T} token rows of one llama70b_prefill_tp8 shard "
                       f"forward (fp64 loops), {dt:.1f} s"}
 
@@ -296,10 +365,12 @@ def cpu_baseline(synth, target_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline only")
+    ap.add_argument("--sections", default="decode,partial_sum,simulated_block,gpt,calibration",
+                    help="comma list of the secondary sections to run (without --quick)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 256 MiB device copy (the reference for HBM byte counters)")
     args = ap.parse_args()
@@ -343,17 +414,26 @@ def main():
                      "flops_per_launch": h["flops_col"]},
         "row_gemm": {"us": round(h["t_row"] * 1e6, 2),
                      "TFLOPs": round(h["flops_row"] / h["t_row"] / 1e12, 2)},
+        "timing": {"clock_ramp_s": RAMP_S,
+                   "step": dict(h["step_spread"], method="event pair around each step, eager"),
+                   "col_gemm": dict(h["col_spread"], method="HIP-graph replays of 4 launches"),
+                   "row_gemm": dict(h["row_spread"], method="HIP-graph replays of 4 launches")},
     }
-    if not args.quick:
+    sections = set() if args.quick else set(args.sections.split(","))
+    if "decode" in sections:
         log("bench: decode")
         result["decode"] = decode_bench(torch, tp, synth, max(5, args.steps // 2), 3)
+    if "partial_sum" in sections:
         log("bench: partial sum")
         result["partial_sum"] = partial_sum_bench(torch, tp, max(5, args.steps), 3)
+    if "simulated_block" in sections:
         log("bench: simulated block")
         result["simulated_block"] = simulated_block_bench(torch, tp, synth, max(3, args.steps // 4),
                                                           2)
+    if "gpt" in sections:
         log("bench: gpt gelu shard")
         result["gpt_gelu_shard"] = gpt_bench(torch, tp, synth, max(5, args.steps // 2), 3)
+    if "calibration" in sections:
         log("bench: mfma calibration")
         result["mfma_calibration"] = mfma_calibration(torch, tp)
     if args.copy_calibration:

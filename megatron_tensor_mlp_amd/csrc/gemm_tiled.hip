@@ -5,11 +5,14 @@
 // the token count is large ("Transformer math: tensor parallel", sections on
 // the column- and row-parallel splits; "Tensor Parallelism Explained", 2.B).
 //
-// Tile: 256 rows x 256 accumulator columns per workgroup, NWAVE wave64s as
-// 2 x (NWAVE/2), each wave owning 128 rows x (512/NWAVE) columns as blocks of
-// v_mfma_f32_32x32x16_bf16 accumulators.  With 4 waves (one per SIMD) a wave
-// holds 128 x 128 (256 fp32 per lane, in AGPRs); with 8 waves (two per SIMD)
-// 128 x 64, and the SIMD switches to the other wave whenever one waits.  For
+// Tile: BM (256 or 128) rows x 256 accumulator columns per workgroup, NWAVE
+// wave64s as (BM/128) x (NWAVE/(BM/128)), each wave owning 128 rows of
+// accumulator columns as blocks of v_mfma_f32_32x32x16_bf16 accumulators.
+// The default for large problems is 256 rows with 8 waves (two per SIMD), each
+// 128 x 64, so the SIMD switches to the other wave whenever one waits; 4 waves
+// of 128 x 128 (256 fp32 per lane, in AGPRs) exist for sweeps.  Problems with
+// at most 128 tiles of 256 rows (half a 256-CU device) use 128-row tiles of
+// 4 waves of 128 x 64 instead, twice as many tiles.  For
 // SwiGLU the accumulator columns are 128 gate columns and the same 128 up
 // columns, and each wave takes equal gate and up slices, so the gate and up
 // value of an output element sit in the same lane and the epilogue is local.
