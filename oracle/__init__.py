@@ -73,9 +73,10 @@ def _load():
         lib.oracle_col_shard_f32.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, vp, ci, vp]
         lib.oracle_partial_sum_f32.argtypes = [i64, i64, i32, vp, vp, vp]
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_qkv_shard_f64.argtypes = [i64, i64, i32, i32, i64, i32, i32, vp, vp, vp, vp]
         for name in ("oracle_col_shard_f64", "oracle_row_shard_f64", "oracle_partial_sum_f64",
                      "oracle_mlp_unsharded_f64", "oracle_linear_f32", "oracle_col_shard_f32",
-                     "oracle_partial_sum_f32", "oracle_num_threads"):
+                     "oracle_partial_sum_f32", "oracle_num_threads", "oracle_qkv_shard_f64"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -205,3 +206,19 @@ def partial_sum_f32(parts, b2=None):
     Z = np.empty((T, d), dtype=np.float32)
     _check(lib.oracle_partial_sum_f32(T, d, p, _p(P), _p(b2), _p(Z)), "partial_sum_f32")
     return Z
+
+
+def qkv_shard(X, Wqkv, Hq, Hkv, dh, i, p, bqkv=None):
+    """[Q_i | K_i | V_i] [T, (Hq + 2 Hkv) dh / p] in fp64: the query, key and value
+    heads of shard i of p projected from X (Wqkv is the full packed [d, (Hq + 2 Hkv) dh]
+    matrix: query heads, then key heads, then value heads)."""
+    lib = _load()
+    X, W, b = _c(X, np.float64), _c(Wqkv, np.float64), _c(bqkv, np.float64)
+    T, d = X.shape
+    ncol = (Hq + 2 * Hkv) * dh
+    if W.shape != (d, ncol) or Hq % p or Hkv % p:
+        raise ValueError("shape mismatch or head counts not divisible by p")
+    out = np.empty((T, ncol // p), dtype=np.float64)
+    _check(lib.oracle_qkv_shard_f64(T, d, Hq, Hkv, dh, i, p, _p(X), _p(W), _p(b), _p(out)),
+           "qkv_shard")
+    return out

@@ -1,5 +1,6 @@
 /*
- * CPU oracle for one tensor-parallel MLP shard.
+ * CPU oracle for one tensor-parallel MLP shard (and the attention projections
+ * of one head shard).
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain reference that the
  * GPU library is checked against.  Only the test suite, the smoke check and
@@ -29,6 +30,10 @@
  *     - The reduction adds the p partials element by element, shard 0 first,
  *       then adds the row bias once (Day 41 post, "Simulating row parallel
  *       linear").
+ *     - Attention is split the same way along its heads: the QKV projection is
+ *       a column-parallel linear whose column blocks are whole heads, and the
+ *       output projection is the row-parallel linear above over the head
+ *       columns (oracle_qkv_shard_f64 below).
  *
  * Every dot product is summed with its index ascending, in the precision of
  * the function (fp64, or fp32 for the *_f32 functions that pin the printed
@@ -313,5 +318,60 @@ int oracle_partial_sum_f32(int64_t T, int64_t d, int32_t p, const float *parts,
     if (b2) acc += b2[e % d];
     Z[e] = acc;
   }
+  return 0;
+}
+
+/* ---- attention projections ---------------------------------------------- */
+
+/*
+ * Column-parallel QKV projection of shard i of p, fp64.
+ *
+ * Multi-head attention is split across GPUs by heads: each GPU owns a
+ * disjoint, contiguous group of heads and computes the query, key and value
+ * projections of those heads alone from the replicated input X ("Transformer
+ * math: tensor parallel", section "Attention: parallel across heads";
+ * "Tensor Parallelism Explained", section 2.A; "Building GPT from Scratch,
+ * Part 9", section "Splitting the Attention Layer").  With grouped key/value
+ * heads the key and value heads are split the same way, Hkv/p per GPU
+ * ("What is Tensor Parallelism?", section "Worked example: Llama 3.1 70B on 8
+ * GPUs").  Both head counts must be divisible by p.
+ *
+ *   X    [T,d]
+ *   W    [d, (Hq + 2 Hkv) dh], the packed projection: query heads in columns
+ *        [0, Hq dh), key heads in [Hq dh, (Hq + Hkv) dh), value heads after
+ *        that; head h of a part owns the dh columns starting at h dh within it.
+ *   b    [(Hq + 2 Hkv) dh] laid out the same way, or NULL.
+ *   QKV  [T, (Hq + 2 Hkv) dh / p] receives, per token, the shard's query heads,
+ *        then its key heads, then its value heads (in that order, as the
+ *        per-GPU projection is split into q, k and v in the Part 9 module),
+ *        each head's dh columns in order.
+ */
+int oracle_qkv_shard_f64(int64_t T, int64_t d, int32_t Hq, int32_t Hkv, int64_t dh, int32_t i,
+                         int32_t p, const double *X, const double *W, const double *b,
+                         double *QKV) {
+  if (p < 1 || i < 0 || i >= p || Hq < 1 || Hkv < 1 || dh < 1) return -1;
+  if (Hq % p != 0 || Hkv % p != 0) return -1;
+  const int64_t ncol = ((int64_t)Hq + 2 * (int64_t)Hkv) * dh, nout = ncol / p;
+  /* The weight column behind each output column, listed part by part, head
+     by head. */
+  int64_t *src = (int64_t *)malloc(sizeof(int64_t) * (size_t)nout);
+  if (!src) return -1;
+  int64_t o = 0;
+  for (int part = 0; part < 3; ++part) {
+    const int64_t heads = part == 0 ? Hq : Hkv;
+    const int64_t part_start = part == 0 ? 0 : (part == 1 ? (int64_t)Hq * dh : ((int64_t)Hq + Hkv) * dh);
+    const int64_t per_gpu = heads / p;
+    for (int64_t h = (int64_t)i * per_gpu; h < ((int64_t)i + 1) * per_gpu; ++h)
+      for (int64_t j = 0; j < dh; ++j) src[o++] = part_start + h * dh + j;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t n = 0; n < nout; ++n) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < d; ++c) acc += X[t * d + c] * W[c * ncol + src[n]];
+      QKV[t * nout + n] = b ? acc + b[src[n]] : acc;
+    }
+  }
+  free(src);
   return 0;
 }

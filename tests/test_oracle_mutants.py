@@ -36,6 +36,18 @@ MUTANTS = [
     ("fp32 linear reads W transposed", "h[j] += xv * W[c * k + j];", "h[j] += xv * W[j * d + c];", 0),
     ("fp32 column shard wrong offset", "const float *w = W1 + c * k + c0;",
      "const float *w = W1 + c * k + (c0 > 0 ? c0 - 1 : c0);", 0),
+    ("qkv key and value blocks swapped",
+     "(part == 1 ? (int64_t)Hq * dh : ((int64_t)Hq + Hkv) * dh)",
+     "(part == 2 ? (int64_t)Hq * dh : ((int64_t)Hq + Hkv) * dh)", 0),
+    ("qkv heads of the mirrored shard",
+     "for (int64_t h = (int64_t)i * per_gpu; h < ((int64_t)i + 1) * per_gpu; ++h)",
+     "for (int64_t h = (int64_t)(p - 1 - i) * per_gpu; h < ((int64_t)(p - 1 - i) + 1) * per_gpu; ++h)", 0),
+    ("qkv key/value shard i starts at head i",
+     "for (int64_t h = (int64_t)i * per_gpu; h < ((int64_t)i + 1) * per_gpu; ++h)",
+     "for (int64_t h = (part == 0 ? (int64_t)i * per_gpu : i);"
+     " h < (part == 0 ? (int64_t)i * per_gpu : i) + per_gpu; ++h)", 0),
+    ("qkv bias not mapped", "QKV[t * nout + n] = b ? acc + b[src[n]] : acc;",
+     "QKV[t * nout + n] = b ? acc + b[n] : acc;", 0),
 ]
 
 

@@ -355,3 +355,157 @@ def test_partial_sum_order_fp32():
     assert oracle.partial_sum_f32(parts2)[0, 0] == np.float32(1.0)
     b2 = np.array([0.5], np.float32)
     assert oracle.partial_sum_f32(parts2, b2)[0, 0] == np.float32(1.5)
+
+
+# ---------------------------------------------------------------- P-10 -------
+# The attention projections: QKV column-parallel by heads, W_O row-parallel.
+def _int_case(T, d, ncol, seed):
+    """Small-integer inputs: every fp64 product and sum below is exact."""
+    rng = np.random.default_rng(seed)
+    X = rng.integers(-4, 5, (T, d)).astype(np.float64)
+    W = rng.integers(-4, 5, (d, ncol)).astype(np.float64)
+    b = rng.integers(-9, 10, (ncol,)).astype(np.float64)
+    return X, W, b
+
+
+@pytest.mark.parametrize("Hq,Hkv,dh,p", [(4, 4, 3, 1), (4, 4, 3, 2), (8, 2, 2, 2), (8, 4, 5, 4),
+                                         (6, 3, 1, 3)])
+def test_qkv_shards_reassemble_full_projection(Hq, Hkv, dh, p):
+    """Each GPU's Q, K and V columns are exactly its heads' columns of the full
+    projection X Wqkv + b: putting the shards' query heads side by side in shard
+    order gives the full query block, and the same for keys and values
+    ('Transformer math: tensor parallel', section "Attention: parallel across
+    heads").  Integer inputs make the comparison with numpy's matmul exact."""
+    T, d = 5, 7
+    ncol = (Hq + 2 * Hkv) * dh
+    X, W, b = _int_case(T, d, ncol, Hq * 100 + p)
+    full = X @ W + b
+    qw, kw = Hq * dh // p, Hkv * dh // p
+    shards = [oracle.qkv_shard(X, W, Hq, Hkv, dh, i, p, bqkv=b) for i in range(p)]
+    for s in shards:
+        assert s.shape == (T, qw + 2 * kw)
+    Q = np.concatenate([s[:, :qw] for s in shards], axis=1)
+    K = np.concatenate([s[:, qw:qw + kw] for s in shards], axis=1)
+    V = np.concatenate([s[:, qw + kw:] for s in shards], axis=1)
+    assert np.array_equal(Q, full[:, :Hq * dh])
+    assert np.array_equal(K, full[:, Hq * dh:(Hq + Hkv) * dh])
+    assert np.array_equal(V, full[:, (Hq + Hkv) * dh:])
+    # without a bias: the same columns of X Wqkv
+    s0 = oracle.qkv_shard(X, W, Hq, Hkv, dh, p - 1, p)
+    assert np.array_equal(s0, shards[p - 1] - np.concatenate(
+        [b[(p - 1) * qw:p * qw], b[Hq * dh + (p - 1) * kw:Hq * dh + p * kw],
+         b[(Hq + Hkv) * dh + (p - 1) * kw:(Hq + Hkv) * dh + p * kw]]))
+
+
+def _softmax_attention(Q, K, V):
+    """softmax(Q K^T / sqrt(dk)) V for one head, fp64 (scaled dot-product attention)."""
+    s = Q @ K.T / math.sqrt(Q.shape[1])
+    s = s - s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return (e / e.sum(axis=1, keepdims=True)) @ V
+
+
+def _heads_attention(Q, K, V, hq, hkv, dh):
+    """Per-head attention over [T, hq dh] queries and [T, hkv dh] keys/values;
+    query head h reads key/value head h // (hq / hkv) (grouped heads)."""
+    g = hq // hkv
+    outs = []
+    for h in range(hq):
+        c = h // g
+        outs.append(_softmax_attention(Q[:, h * dh:(h + 1) * dh], K[:, c * dh:(c + 1) * dh],
+                                       V[:, c * dh:(c + 1) * dh]))
+    return np.concatenate(outs, axis=1)
+
+
+@pytest.mark.parametrize("Hq,Hkv,dh,p", [(4, 4, 4, 2), (8, 2, 4, 2), (8, 4, 2, 4), (4, 1, 4, 1)])
+def test_head_split_attention_sums_to_full(Hq, Hkv, dh, p):
+    """Multi-head attention is the concatenation of the heads times W_O, i.e. a
+    sum over heads of head_h times W_O's rows of head h ('Building GPT from
+    Scratch, Part 9', section "Why This Works").  So per-shard attention on the
+    shard's Q_i, K_i, V_i, followed by the row-parallel W_O shard, summed over
+    shards, equals the unsharded attention block.  A head assigned to the wrong
+    shard, a key head paired with the wrong query heads, or K and V swapped
+    breaks the identity."""
+    T, d = 6, 12
+    rng = np.random.default_rng(Hq * 7 + Hkv * 3 + p)
+    ncol = (Hq + 2 * Hkv) * dh
+    X = rng.standard_normal((T, d))
+    W = rng.standard_normal((d, ncol)) / math.sqrt(d)
+    b = rng.standard_normal(ncol) * 0.1
+    WO = rng.standard_normal((Hq * dh, d)) / math.sqrt(Hq * dh)
+    full = X @ W + b
+    Qf, Kf, Vf = full[:, :Hq * dh], full[:, Hq * dh:(Hq + Hkv) * dh], full[:, (Hq + Hkv) * dh:]
+    ref = _heads_attention(Qf, Kf, Vf, Hq, Hkv, dh) @ WO
+    qw, kw = Hq * dh // p, Hkv * dh // p
+    parts = []
+    for i in range(p):
+        s = oracle.qkv_shard(X, W, Hq, Hkv, dh, i, p, bqkv=b)
+        O = _heads_attention(s[:, :qw], s[:, qw:qw + kw], s[:, qw + kw:], Hq // p, Hkv // p, dh)
+        parts.append(oracle.row_shard(O, WO, i, p))
+    assert rel_fro(oracle.partial_sum(parts), ref) < 1e-12
+
+
+def test_qkv_head_bookkeeping_one_hot(golden):
+    """'What is Tensor Parallelism?', Llama 3.1 70B at TP = 8: each GPU gets 8
+    query heads and 1 key/value head.  With X a one-hot row and weight column c
+    holding the value c, the shard's output names the weight column behind each
+    of its columns: the query columns must form whole heads, 8 of them, and the
+    key and value columns one head each; over the 8 shards every head of every
+    part appears exactly once, shard i's heads coming after shard i-1's."""
+    g = golden("attention_head_split.txt")
+    Hq, Hkv, p = int(g["llama_heads"]), int(g["llama_kv_heads"]), int(g["llama_tp"])
+    dh = int(g["llama_hidden"]) // Hq
+    ncol = (Hq + 2 * Hkv) * dh
+    d = 3
+    X = np.array([[0.0, 1.0, 0.0]])
+    W = np.zeros((d, ncol))
+    W[1, :] = np.arange(ncol, dtype=np.float64)
+    seen = {"q": [], "k": [], "v": []}
+    bounds = {"q": (0, Hq * dh), "k": (Hq * dh, (Hq + Hkv) * dh), "v": ((Hq + Hkv) * dh, ncol)}
+    for i in range(p):
+        cols = oracle.qkv_shard(X, W, Hq, Hkv, dh, i, p)[0].astype(np.int64)
+        assert cols.shape == ((int(g["llama_q_heads_per_gpu"]) + 2 * int(g["llama_kv_heads_per_gpu"]))
+                              * dh,)
+        nq = int(g["llama_q_heads_per_gpu"]) * dh
+        nk = int(g["llama_kv_heads_per_gpu"]) * dh
+        for part, seg in (("q", cols[:nq]), ("k", cols[nq:nq + nk]), ("v", cols[nq + nk:])):
+            lo, hi = bounds[part]
+            assert ((seg >= lo) & (seg < hi)).all()
+            rel = seg - lo
+            heads = rel.reshape(-1, dh)
+            # whole heads: each row of dh columns is one head's columns in order
+            assert (heads == heads[:, :1] + np.arange(dh)).all() and (heads[:, 0] % dh == 0).all()
+            seen[part].extend((heads[:, 0] // dh).tolist())
+    for part, n in (("q", Hq), ("k", Hkv), ("v", Hkv)):
+        assert seen[part] == list(range(n))
+
+
+def test_attention_split_shapes(golden):
+    """The shard shapes the pages print: Part 9's [4096, 3 x 1024] QKV shard and
+    [1024, 4096] output-projection shard at 32 heads on 4 GPUs; initnode's 16
+    heads per GPU at 64 heads and TP = 4."""
+    g = golden("attention_head_split.txt")
+    H, p, E = int(g["gpt_heads"]), int(g["gpt_tp"]), int(g["gpt_embed"])
+    dh = E // H
+    assert H // p == int(g["gpt_heads_per_gpu"])
+    d = 8  # a narrow input; the shard width does not depend on it
+    s = oracle.qkv_shard(np.ones((1, d)), np.zeros((d, 3 * E)), H, H, dh, p - 1, p)
+    assert s.shape[1] == int(g["gpt_qkv_shard_cols"])
+    # W_O is a row-parallel linear over the head columns: shard rows E / p
+    Z = oracle.row_shard(np.ones((1, E // p)), np.zeros((E, E)), p - 1, p)
+    assert (E // p, Z.shape[1]) == (int(g["gpt_out_shard_rows"]), int(g["gpt_out_shard_cols"]))
+    H4, p4 = int(g["initnode_heads"]), int(g["initnode_tp"])
+    s4 = oracle.qkv_shard(np.ones((1, d)), np.zeros((d, 3 * H4 * 2)), H4, H4, 2, 0, p4)
+    assert s4.shape[1] == 3 * int(g["initnode_heads_per_gpu"]) * 2
+
+
+def test_qkv_divisibility_errors():
+    """Head counts must be divisible by the TP degree ('Tensor Parallelism
+    Explained', section 4; Part 9's module asserts it)."""
+    X = np.zeros((1, 4))
+    with pytest.raises(ValueError):
+        oracle.qkv_shard(X, np.zeros((4, 6 * 2)), 4, 1, 2, 0, 2)   # Hkv = 1 on 2 GPUs
+    with pytest.raises(ValueError):
+        oracle.qkv_shard(X, np.zeros((4, 9 * 2)), 3, 3, 2, 0, 2)   # Hq = 3 on 2 GPUs
+    with pytest.raises(ValueError):
+        oracle.qkv_shard(X, np.zeros((4, 12 * 2)), 4, 4, 2, 2, 2)  # i outside [0, p)
