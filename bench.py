@@ -13,7 +13,8 @@ only at the ends of a batch of launches).
 Prints ONE JSON line.  `value` is the step's algorithmic TFLOP/s (2*T*d*(k/p)
 flops per GEMM, three GEMMs).  Secondary fields report the few-token (decode)
 shard in GB/s of weights streamed, the on-device partial sum in GB/s, the
-simulated TP = 8 block and the GPT-style GeLU shard.  `roofline` covers the
+simulated TP = 8 block, the GPT-style GeLU shard and the attention projections
+of one head shard (QKV and output projection).  `roofline` covers the
 dominant kernel (the SwiGLU column GEMM), `cpu_baseline` the CPU oracle timed
 on a bounded row sample of the same workload.
 """
@@ -293,6 +294,73 @@ def gpt_bench(torch, tp, synth, steps, warmup):
             "col_us": round(tc * 1e6, 1), "row_us": round(tr * 1e6, 1)}
 
 
+def attention_bench(torch, tp, synth, steps, warmup, rotate_bytes=600 << 20):
+    """Attention projections of one head shard of Llama-70B at TP = 8 (64 query
+    and 8 key/value heads of 128, d = 8192): the fused QKV projection
+    (tp_qkv_linear, shard 3 of the full packed weight) and the output
+    projection's row block (tp_row_linear on a stand-in attention output).
+    Prefill T = 4096 after the clock ramp; decode T = 1, 8, 64 with the weights
+    rotating over the 8 shards of 2 copies of the full matrices (16 x 38 MB, more
+    than twice the 256 MB Infinity Cache).  HIP-graph replay."""
+    W = synth.ATTN_WORKLOADS["llama70b_attn_prefill_tp8"]
+    dev = "cuda:0"
+    Wqkv, WO = (t.to(dev) for t in synth.attn_weights(W.d, W.Hq, W.Hkv, W.dh))
+    out = {}
+    X = synth.llama_tokens(W.T, W.d).to(dev)
+    QKV = torch.empty(W.T, W.qkv_cols, dtype=torch.bfloat16, device=dev)
+    O = synth.attn_output(W.T, W.o_rows).to(dev)
+    Z = torch.empty(W.T, W.d, device=dev)
+    qkv = lambda: tp.tp_qkv_linear(X, Wqkv, W.Hq, W.Hkv, W.dh, 3, W.p, QKV)  # noqa: E731
+    row = lambda: tp.tp_row_linear(O, WO, 3, W.p, Z)  # noqa: E731
+    ramp(torch, [qkv, row])
+    t = time_graph(torch, [qkv, row], max(10, steps), warmup)
+    sp = LAST_SPREAD
+    tq = time_graph(torch, [qkv], max(5, steps), warmup)
+    tr = time_graph(torch, [row], max(5, steps), warmup)
+    fq = 2.0 * W.T * W.d * W.qkv_cols
+    fr = 2.0 * W.T * W.o_rows * W.d
+    out["prefill"] = {
+        "workload": W.name, "T": W.T, "us": round(t * 1e6, 1),
+        "TFLOPs": round((fq + fr) / t / 1e12, 1),
+        "frac_mfma": round((fq + fr) / t / 1e12 / PEAK_BF16_TFLOPS, 4), "spread": sp,
+        "qkv_us": round(tq * 1e6, 1), "qkv_TFLOPs": round(fq / tq / 1e12, 1),
+        "o_proj_us": round(tr * 1e6, 1), "o_proj_TFLOPs": round(fr / tr / 1e12, 1)}
+    del X, QKV, O, Z
+    Wd = synth.ATTN_WORKLOADS["llama70b_attn_decode_tp8"]
+    sets = [(Wqkv, WO), (Wqkv.clone(), WO.clone())]
+    pairs = [(s, i) for s in sets for i in range(W.p)]
+    wbytes = W.weight_bytes()
+    dec = {}
+    for T in Wd.Ts:
+        X = synth.llama_tokens(T, W.d).to(dev)
+        QKV = torch.empty(T, W.qkv_cols, dtype=torch.bfloat16, device=dev)
+        O = synth.attn_output(T, W.o_rows).to(dev)
+        Z = torch.empty(T, W.d, device=dev)
+        ws = tp.workspace(max(tp.tp_qkv_workspace_bytes(torch.bfloat16, T, W.d, W.Hq, W.Hkv, W.dh,
+                                                        W.p),
+                              tp.tp_workspace_bytes(torch.bfloat16, "none", T, W.d, W.Hq * W.dh,
+                                                    W.p)), dev)
+        fns = []
+        for (wq, wo), i in pairs:
+            fns.append(lambda wq=wq, i=i: tp.tp_qkv_linear(X, wq, W.Hq, W.Hkv, W.dh, i, W.p, QKV,
+                                                            ws=ws))
+            fns.append(lambda wo=wo, i=i: tp.tp_row_linear(O, wo, i, W.p, Z, ws=ws))
+        t = time_graph(torch, fns, max(steps, 20), warmup) / len(pairs)
+        sp = {k: (round(v / len(pairs), 2) if k.endswith("_us") else v)
+              for k, v in LAST_SPREAD.items()}
+        tq = time_graph(torch, fns[0::2], max(steps, 20), warmup) / len(pairs)
+        alg = wbytes + T * W.d * 2 + T * W.qkv_cols * 2 + T * W.o_rows * 2 + T * W.d * 4
+        dec[f"T{T}"] = {"us_per_step": round(t * 1e6, 2), "GBps": round(alg / t / 1e9, 1),
+                        "frac_hbm": round(alg / t / 1e9 / PEAK_HBM_GBS, 4), "step_spread": sp,
+                        "qkv_us": round(tq * 1e6, 2),
+                        "qkv_GBps": round(2 * W.d * W.qkv_cols / tq / 1e9, 1)}
+    dec["weight_bytes"] = wbytes
+    dec["rotation"] = "8 shards x 2 copies"
+    out["decode"] = dec
+    out["timing"] = "HIP graph replay"
+    return out
+
+
 def mfma_calibration(torch, tp, iters=20000, nwg=1024):
     """Sustained dense bf16 MFMA rate and the shader clock it runs at, for zero
     operands and for operands with the workloads' value mix (A ~ N(0,1),
@@ -369,7 +437,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline only")
-    ap.add_argument("--sections", default="decode,partial_sum,simulated_block,gpt,calibration",
+    ap.add_argument("--sections",
+                    default="decode,partial_sum,simulated_block,gpt,attention,calibration",
                     help="comma list of the secondary sections to run (without --quick)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 256 MiB device copy (the reference for HBM byte counters)")
@@ -433,6 +502,10 @@ def main():
     if "gpt" in sections:
         log("bench: gpt gelu shard")
         result["gpt_gelu_shard"] = gpt_bench(torch, tp, synth, max(5, args.steps // 2), 3)
+    if "attention" in sections:
+        log("bench: attention projections")
+        result["attention_projections"] = attention_bench(torch, tp, synth,
+                                                          max(5, args.steps // 2), 3)
     if "calibration" in sections:
         log("bench: mfma calibration")
         result["mfma_calibration"] = mfma_calibration(torch, tp)

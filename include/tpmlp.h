@@ -63,14 +63,14 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 1
+#define TPMLP_ABI_VERSION 2
 #define TP_MAX_SHARDS 64
 
 typedef enum {
   TP_OK = 0,
   TP_ERR_NULL_POINTER = 1, /* a required pointer is NULL                         */
   TP_ERR_BAD_SHAPE = 2,    /* T < 0, d < 1, k < 1, or an ld below the row width  */
-  TP_ERR_NOT_DIVISIBLE = 3,/* k % p != 0                                          */
+  TP_ERR_NOT_DIVISIBLE = 3,/* k % p != 0 (head counts % p != 0 for the QKV step) */
   TP_ERR_BAD_SHARD = 4,    /* i outside [0,p), p < 1 or p > TP_MAX_SHARDS         */
   TP_ERR_MISALIGNED = 5,   /* pointer not 16-byte aligned or width/ld not a
                               multiple of 8 (bf16) / 4 (fp32) elements            */
@@ -188,6 +188,54 @@ tp_status tp_mlp_simulated(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_
  * the same stream.  Returns 0 for invalid arguments.
  */
 size_t tp_workspace_bytes(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t p);
+
+/*
+ * Attention projections of head shard i of p.
+ *
+ * Multi-head attention splits across GPUs along its heads: shard i owns query
+ * heads [i*Hq/p, (i+1)*Hq/p) and key/value heads [i*Hkv/p, (i+1)*Hkv/p), and
+ * projects the replicated input X to the queries, keys and values of those
+ * heads alone; the QKV projection is thus a column-parallel linear whose
+ * column blocks are whole heads ("Transformer math: tensor parallel", section
+ * "Attention: parallel across heads"; "Tensor Parallelism Explained", section
+ * 2.A; "Building GPT from Scratch, Part 9", section "Splitting the Attention
+ * Layer").  With grouped key/value heads (Hkv < Hq) both counts are split p
+ * ways ("What is Tensor Parallelism?", Llama 3.1 70B worked example: 64 query
+ * and 8 key/value heads give 8 and 1 per GPU at TP = 8).  Hq and Hkv must be
+ * divisible by p (TP_ERR_NOT_DIVISIBLE otherwise; "Tensor Parallelism
+ * Explained", section 4).  With qw = Hq*dh/p and kw = Hkv*dh/p:
+ *   QKV[t, j]           = sum_c X[t,c] Wqkv[c, i*qw + j]                 + b   (j < qw)
+ *   QKV[t, qw + j]      = sum_c X[t,c] Wqkv[c, Hq*dh + i*kw + j]         + b   (j < kw)
+ *   QKV[t, qw + kw + j] = sum_c X[t,c] Wqkv[c, (Hq+Hkv)*dh + i*kw + j]   + b   (j < kw)
+ * (b the same column of bqkv, or 0), in one launch.
+ *   X    [T, d], ldx              input, dtype dt (replicated on every shard)
+ *   Wqkv [d, (Hq+2*Hkv)*dh], ldw  full packed projection, dtype dt: the query
+ *                                 heads' columns, then the key heads', then the
+ *                                 value heads'; head h of a block owns its dh
+ *                                 columns starting at h*dh
+ *   bqkv [(Hq+2*Hkv)*dh] or NULL  full bias, same layout, dtype dt
+ *   QKV  [T, qw + 2*kw], ldo      output, dtype dt, overwritten: this shard's
+ *                                 query heads, then its key heads, then its value
+ *                                 heads (the q | k | v split of the per-GPU
+ *                                 projection in the Part 9 module)
+ * d and dh must be multiples of 8 (bf16) or 4 (fp32) elements.  fp32
+ * accumulation, output rounded once to dt.  A GPU that stores only its own
+ * packed [Q_i | K_i | V_i] weight passes it with Hq/p, Hkv/p, i = 0, p = 1.
+ *
+ * The output projection W_O [Hq*dh, d] is a row-parallel linear over the same
+ * head split (its row block of shard i is the rows of the shard's query heads):
+ * call tp_row_linear with k = Hq*dh on the shard's attention output
+ * [T, Hq*dh/p], and reduce the fp32 partials with tp_partial_sum.
+ */
+tp_status tp_qkv_linear(tp_dtype dt, int64_t T, int64_t d, int32_t Hq, int32_t Hkv, int64_t dh,
+                        int32_t i, int32_t p, const void *X, int64_t ldx, const void *Wqkv,
+                        int64_t ldw, const void *bqkv, void *QKV, int64_t ldo, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/* Bytes of workspace tp_qkv_linear needs for these sizes (0 if none, or for
+ * invalid arguments); the same contract as tp_workspace_bytes. */
+size_t tp_qkv_workspace_bytes(tp_dtype dt, int64_t T, int64_t d, int32_t Hq, int32_t Hkv,
+                              int64_t dh, int32_t p);
 
 /* Shard bookkeeping on the host: shard i of p of a dimension of size k owns
  * [*c0, *c0 + *s) with s = k/p and c0 = i*s (Day 41 post, "Simulating column

@@ -67,8 +67,12 @@ def library():
     lib.tp_abi_version.argtypes = []
     lib.tp_abi_version.restype = i32
     lib.tp_calib_mfma_bf16.argtypes = [i32, i64, vp, i32, vp]
+    lib.tp_qkv_linear.argtypes = [ci, i64, i64, i32, i32, i64, i32, i32, vp, i64, vp, i64, vp,
+                                  vp, i64, vp, sz, vp]
+    lib.tp_qkv_workspace_bytes.argtypes = [ci, i64, i64, i32, i32, i64, i32]
+    lib.tp_qkv_workspace_bytes.restype = sz
     for name in ("tp_col_linear", "tp_row_linear", "tp_mlp_shard", "tp_partial_sum",
-                 "tp_mlp_simulated", "tp_shard_bounds", "tp_calib_mfma_bf16"):
+                 "tp_mlp_simulated", "tp_shard_bounds", "tp_calib_mfma_bf16", "tp_qkv_linear"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -261,3 +265,27 @@ def tp_mlp_simulated(X, W1, W2, p: int, Y, Zp, Z, act="gelu_tanh", Wu=None, b1=N
                                       _ptr(Y), _ptr(Zp), _ptr(Z), ldz, wsp, wsn,
                                       _stream(stream)))
     return Z
+
+
+def tp_qkv_workspace_bytes(dtype, T: int, d: int, Hq: int, Hkv: int, dh: int, p: int) -> int:
+    dt = DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return library().tp_qkv_workspace_bytes(dt, T, d, Hq, Hkv, dh, p)
+
+
+def tp_qkv_linear(X, Wqkv, Hq: int, Hkv: int, dh: int, i: int, p: int, QKV, bqkv=None, ws=None,
+                  stream=None):
+    """QKV <- [Q_i | K_i | V_i]: the query, key and value heads of head shard i of p
+    projected from X; Wqkv is the full packed [d, (Hq + 2 Hkv) dh] weight."""
+    T, d = X.shape
+    ncol = (Hq + 2 * Hkv) * dh
+    nout = ncol // p if p > 0 else 0
+    ldx = _ld(X, T, d, "X")
+    ldw = _ld(Wqkv, d, ncol, "Wqkv")
+    ldo = _ld(QKV, T, nout, "QKV")
+    if bqkv is not None and bqkv.numel() < ncol:
+        raise ValueError("bqkv is shorter than (Hq + 2 Hkv) dh")
+    need = tp_qkv_workspace_bytes(X.dtype, T, d, Hq, Hkv, dh, p)
+    wsp, wsn = _ws_args(ws, need, X.device)
+    _check(library().tp_qkv_linear(_dt(X), T, d, Hq, Hkv, dh, i, p, _ptr(X), ldx, _ptr(Wqkv), ldw,
+                                   _ptr(bqkv), _ptr(QKV), ldo, wsp, wsn, _stream(stream)))
+    return QKV

@@ -283,6 +283,100 @@ RowCall make_row(tp_dtype dt, int64_t T, int64_t d, int64_t k, int32_t i, int32_
 
 size_t max_sz(size_t a, size_t b) { return a > b ? a : b; }
 
+struct QkvCall {
+  tp_dtype dt;
+  int64_t T, d;
+  int32_t Hq, Hkv;
+  int64_t dh;
+  int32_t i, p;
+  const void *X, *W, *b;
+  int64_t ldx, ldw, ldo;
+  void *QKV;
+};
+
+tp_status validate_qkv(const QkvCall &c) {
+  TRY(check_dtype_act(c.dt, TP_ACT_NONE));
+  if (c.T < 0) return fail(TP_ERR_BAD_SHAPE, "T = %lld < 0", (long long)c.T);
+  if (c.d < 1) return fail(TP_ERR_BAD_SHAPE, "d = %lld < 1", (long long)c.d);
+  if (c.Hq < 1 || c.Hkv < 1 || c.dh < 1)
+    return fail(TP_ERR_BAD_SHAPE, "Hq = %d, Hkv = %d and dh = %lld must be >= 1", c.Hq, c.Hkv,
+                (long long)c.dh);
+  if (c.p < 1 || c.p > TP_MAX_SHARDS)
+    return fail(TP_ERR_BAD_SHARD, "p = %d outside [1, %d]", c.p, TP_MAX_SHARDS);
+  if (c.i < 0 || c.i >= c.p)
+    return fail(TP_ERR_BAD_SHARD, "shard index i = %d outside [0, %d)", c.i, c.p);
+  if (c.Hq % c.p || c.Hkv % c.p)
+    return fail(TP_ERR_NOT_DIVISIBLE, "head counts Hq = %d and Hkv = %d must be divisible by p = %d",
+                c.Hq, c.Hkv, c.p);
+  if (c.d % elem_align(c.dt) || c.dh % elem_align(c.dt))
+    return fail(TP_ERR_MISALIGNED, "d = %lld and dh = %lld must be multiples of %lld",
+                (long long)c.d, (long long)c.dh, (long long)elem_align(c.dt));
+  const int64_t ncol = ((int64_t)c.Hq + 2 * (int64_t)c.Hkv) * c.dh;
+  if (c.T > 0) {  // with no tokens X and QKV are never touched and may be NULL
+    TRY(check_ptr("X", c.X));
+    TRY(check_ptr("QKV", c.QKV));
+  }
+  TRY(check_ptr("Wqkv", c.W));
+  if (c.b) TRY(check_ptr("bqkv", c.b));
+  TRY(check_ld("ldx", c.ldx, c.d, c.dt));
+  TRY(check_ld("ldw", c.ldw, ncol, c.dt));
+  TRY(check_ld("ldo", c.ldo, ncol / c.p, c.dt));
+  return TP_OK;
+}
+
+// The QKV projection of head shard i is a column-parallel linear whose output
+// columns come from three column blocks of the packed weight: the shard's
+// query heads, its key heads and its value heads ("Transformer math: tensor
+// parallel", section "Attention: parallel across heads").  One GEMM with a
+// three-segment column map computes all three.
+GemmArgs qkv_gemm(const QkvCall &c) {
+  const int64_t qw = (int64_t)c.Hq * c.dh / c.p, kw = (int64_t)c.Hkv * c.dh / c.p;
+  GemmArgs a{};
+  a.A = c.X;
+  a.lda = c.ldx;
+  a.B = c.W;
+  a.ldb = c.ldw;
+  a.bias = c.b;
+  a.C = c.QKV;
+  a.ldc = c.ldo;
+  a.M = c.T;
+  a.N = qw + 2 * kw;
+  a.K = c.d;
+  a.epi = EPI_ACT;
+  a.act = TP_ACT_NONE;
+  a.groups = 1;
+  a.nseg = 3;
+  a.seg_start[0] = 0;
+  a.seg_start[1] = qw;
+  a.seg_start[2] = qw + kw;
+  a.seg_src[0] = c.i * qw;
+  a.seg_src[1] = (int64_t)c.Hq * c.dh + c.i * kw;
+  a.seg_src[2] = ((int64_t)c.Hq + c.Hkv) * c.dh + c.i * kw;
+  return a;
+}
+
+QkvCall make_qkv(tp_dtype dt, int64_t T, int64_t d, int32_t Hq, int32_t Hkv, int64_t dh,
+                 int32_t i, int32_t p, const void *X, int64_t ldx, const void *W, int64_t ldw,
+                 const void *b, void *QKV, int64_t ldo) {
+  QkvCall c;
+  c.dt = dt;
+  c.T = T;
+  c.d = d;
+  c.Hq = Hq;
+  c.Hkv = Hkv;
+  c.dh = dh;
+  c.i = i;
+  c.p = p;
+  c.X = X;
+  c.W = W;
+  c.b = b;
+  c.ldx = ldx;
+  c.ldw = ldw;
+  c.ldo = ldo;
+  c.QKV = QKV;
+  return c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -412,6 +506,34 @@ size_t tp_workspace_bytes(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t
                        (void *)dummy, s);
   RowCall r = make_row(dt, T, d, k, 0, p, dummy, s, dummy, d, (float *)dummy, d);
   return max_sz(gemm_ws_bytes(dt, col_gemm(c, 1, 0)), gemm_ws_bytes(dt, row_gemm(r, 1, 0, 0)));
+}
+
+tp_status tp_qkv_linear(tp_dtype dt, int64_t T, int64_t d, int32_t Hq, int32_t Hkv, int64_t dh,
+                        int32_t i, int32_t p, const void *X, int64_t ldx, const void *Wqkv,
+                        int64_t ldw, const void *bqkv, void *QKV, int64_t ldo, void *ws,
+                        size_t ws_bytes, void *stream) {
+  const QkvCall c = make_qkv(dt, T, d, Hq, Hkv, dh, i, p, X, ldx, Wqkv, ldw, bqkv, QKV, ldo);
+  TRY(validate_qkv(c));
+  if (T == 0) return ok();
+  const GemmArgs a = qkv_gemm(c);
+  TRY(check_gemm(dt, a));
+  TRY(check_ws(gemm_ws_bytes(dt, a), ws, ws_bytes));
+  TRY(run_gemm(dt, a, ws, (hipStream_t)stream));
+  return ok();
+}
+
+size_t tp_qkv_workspace_bytes(tp_dtype dt, int64_t T, int64_t d, int32_t Hq, int32_t Hkv,
+                              int64_t dh, int32_t p) {
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  if (T < 1 || d < 1 || Hq < 1 || Hkv < 1 || dh < 1 || p < 1 || p > TP_MAX_SHARDS) return 0;
+  const int64_t ncol = ((int64_t)Hq + 2 * (int64_t)Hkv) * dh;
+  const QkvCall c = make_qkv(dt, T, d, Hq, Hkv, dh, 0, p, dummy, d, dummy, ncol, nullptr,
+                             (void *)dummy, p > 0 ? ncol / p : ncol);
+  const std::string keep = g_msg;  // a size query leaves the last error message alone
+  const tp_status st = validate_qkv(c);
+  g_msg = keep;
+  if (st != TP_OK) return 0;
+  return gemm_ws_bytes(dt, qkv_gemm(c));
 }
 
 tp_status tp_shard_bounds(int64_t k, int32_t i, int32_t p, int64_t *c0, int64_t *s) {

@@ -149,7 +149,7 @@ __device__ __forceinline__ void store_out(const GemmArgs &p, int64_t col, int la
   if (col >= p.N) return;
   float bv = 0.0f;
   if constexpr (EPI == EPI_ACT)
-    if (p.bias) bv = (float)((const bf16 *)p.bias)[col];
+    if (p.bias) bv = (float)((const bf16 *)p.bias)[src_col(p, col)];
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(NWAVE * 64) void gemm_bf16_decode_kernel(const Gemm
     const int lu = (lane % 16) ^ swz_w(r);
     const int64_t col = n0 + 8 * lu;
     w_row[j] = r;
-    w_off[j] = col < N ? (uint32_t)((r * ldw + col) * 2) : OOB;
+    w_off[j] = col < N ? (uint32_t)((r * ldw + src_col(p, col)) * 2) : OOB;
   }
   // Token rows: wave w fills bytes [XW w, XW (w+1)) of the token region, load
   // j the XLB bytes from XW w + XLB j; lane -> physical byte (XLB / 64) lane.

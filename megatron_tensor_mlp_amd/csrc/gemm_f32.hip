@@ -28,7 +28,7 @@ __global__ __launch_bounds__(TS *TS) void gemm_f32_kernel(const GemmArgs p) {
   for (int64_t k0 = 0; k0 < p.K; k0 += TS) {
     const int64_t ka = k0 + tx, kb = k0 + ty;
     As[ty][tx] = (row < p.M && ka < p.K) ? A[row * p.lda + ka] : 0.0f;
-    Bs[ty][tx] = (col < p.N && kb < p.K) ? B[kb * p.ldb + col] : 0.0f;
+    Bs[ty][tx] = (col < p.N && kb < p.K) ? B[kb * p.ldb + src_col(p, col)] : 0.0f;
     if (DUAL) B2s[ty][tx] = (col < p.N && kb < p.K) ? B2[kb * p.ldb2 + col] : 0.0f;
     __syncthreads();
     const int kn = (p.K - k0) < TS ? (int)(p.K - k0) : TS;
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(TS *TS) void gemm_f32_kernel(const GemmArgs p) {
   } else if constexpr (DUAL) {
     C[row * p.ldc + col] = silu(acc) * acc2;
   } else {
-    const float bv = p.bias ? ((const float *)p.bias + g * p.sBias)[col] : 0.0f;
+    const float bv = p.bias ? ((const float *)p.bias + g * p.sBias)[src_col(p, col)] : 0.0f;
     C[row * p.ldc + col] = activate<ACT>(acc + bv);
   }
 }

@@ -132,8 +132,10 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * NOUT;
   const bf16 *A = (const bf16 *)p.A + g * p.sA + m0 * p.lda;
-  const bf16 *B = (const bf16 *)p.B + g * p.sB + n0;
-  const bf16 *B2 = DUAL ? (const bf16 *)p.B2 + g * p.sB2 + n0 : nullptr;
+  // B offsets are taken from the matrix base: a column map may send a tile's
+  // columns to separate column blocks of B.
+  const bf16 *B = (const bf16 *)p.B + g * p.sB;
+  const bf16 *B2 = DUAL ? (const bf16 *)p.B2 + g * p.sB2 : nullptr;
 
   // ---- per-lane load offsets (bytes, relative to the k-step's base) -------
   // A: load j of wave w fills rows (A_LOADS w + j) * AROWS_PER_LOAD + lane/AUNITS,
@@ -161,10 +163,10 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
     const int li = gi % B_LOADS_PER_REGION;
     const int k = li * BROWS_PER_LOAD + lane / BUNITS;
     const int lu = (lane % BUNITS) ^ swz_b(k);
-    const int64_t col = 8 * lu;  // column offset from n0 within the region
+    const int64_t col = n0 + 8 * lu;  // output column of this 16-byte unit
     const int64_t ld = b_up ? p.ldb2 : p.ldb;
     b_k[j] = k;
-    b_off[j] = (n0 + col < N) ? (uint32_t)((k * ld + col) * 2) : OOB;
+    b_off[j] = (col < N) ? (uint32_t)((k * ld + src_col(p, col)) * 2) : OOB;
   }
 
   // This wave's loads of k-step dkt into `stage`, one at a time (q < LPS).
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
     for (int f = 0; f < NB; ++f) {
       const int64_t col = n0 + WN * wn + 32 * f + (lane & 31);
       if (col >= N) continue;
-      const float bv = bias ? (float)bias[col] : 0.0f;
+      const float bv = bias ? (float)bias[src_col(p, col)] : 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -433,7 +435,8 @@ hipError_t launch_t(const GemmArgs &a, hipStream_t s) {
 
 bool gemm_bf16_tiled_supported(const GemmArgs &a) {
   // Per-lane buffer offsets are 32-bit byte offsets from a tile's k-step base:
-  // 256 rows of A and 64 rows of B must stay below 2^31 bytes.
+  // 256 rows of A, and 64 rows of B plus a column index below ldb, must stay
+  // below 2^31 bytes.
   return a.lda < (int64_t(1) << 21) && a.ldb < (int64_t(1) << 23) &&
          (a.epi != EPI_SWIGLU || a.ldb2 < (int64_t(1) << 23));
 }

@@ -13,6 +13,12 @@ enum Epilogue : int {
   EPI_F32 = 2,          // C = acc, fp32                           (row step partial)
 };
 
+// Column map: output column c of a GEMM reads weight (and bias) column
+// c - seg_start[s] + seg_src[s], s the last segment with seg_start[s] <= c.
+// With nseg = 0 the map is the identity.  The fused QKV projection of one
+// head shard uses three segments (its query, key and value heads).
+constexpr int kMaxSegs = 3;
+
 // C[M,N] = epilogue(A[M,K] * B[K,N]) for `groups` independent problems that
 // share M, N, K and leading dimensions; problem g uses base pointers offset by
 // g * s* elements (the simulated-p grouped launch).  bf16 operands.
@@ -30,7 +36,17 @@ struct GemmArgs {
   int epi, act;
   int groups;
   int64_t sA, sB, sB2, sBias, sC;
+  int nseg;  // column map (EPI_ACT only; 0 = identity)
+  int64_t seg_start[kMaxSegs], seg_src[kMaxSegs];
 };
+
+// Weight / bias column read for output column c.
+__host__ __device__ inline int64_t src_col(const GemmArgs &p, int64_t c) {
+  int64_t base = 0;
+  for (int s = 0; s < kMaxSegs; ++s)
+    if (s < p.nseg && c >= p.seg_start[s]) base = p.seg_src[s] - p.seg_start[s];
+  return c + base;
+}
 
 // Large-T path: MFMA tiles staged through LDS.  _supported: the shape fits the
 // kernels' 32-bit buffer offsets.

@@ -16,7 +16,11 @@ Workload shapes come from the pages' worked examples:
   * Llama 3.1 70B at TP = 8: hidden 8192, feed-forward 28672, 3584 feed-forward
     columns per GPU ("What is Tensor Parallelism?", section "Worked example:
     Llama 3.1 70B on 8 GPUs"), with the gated SwiGLU feed-forward ("Tensor
-    Parallelism Explained", section 2.B).
+    Parallelism Explained", section 2.B);
+  * attention split by heads: Llama 3.1 70B's 64 query and 8 key/value heads
+    at TP = 8 (same page and section; head width 8192 / 64 = 128), and the
+    GPT-style 32 heads of width 128 over 4 GPUs ("Building GPT from Scratch,
+    Part 9", section "Splitting the Attention Layer").
 """
 from __future__ import annotations
 
@@ -67,6 +71,49 @@ WORKLOADS = {
     "llama70b_block_sim_tp8": Workload("llama70b_block_sim_tp8", 512, 8192, 28672, 8, "swiglu",
                                        "bf16", False,
                                        "all 8 shards of a TP=8 Llama-70B MLP on one GPU"),
+}
+
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    """Attention projections of one head shard: QKV [d, (Hq + 2 Hkv) dh / p] and
+    the output projection's row block [Hq dh / p, d]."""
+    name: str
+    T: int          # tokens
+    d: int          # model width
+    Hq: int         # query heads
+    Hkv: int        # key/value heads
+    dh: int         # head width
+    p: int          # tensor-parallel degree
+    note: str = ""
+    Ts: tuple = field(default_factory=tuple)  # decode: several token counts
+
+    @property
+    def qkv_cols(self) -> int:
+        return (self.Hq + 2 * self.Hkv) * self.dh // self.p
+
+    @property
+    def o_rows(self) -> int:
+        return self.Hq * self.dh // self.p
+
+    def shard_flops(self, T: int | None = None) -> float:
+        """Algorithmic flops of the shard's two projections: 2 T d (qkv_cols + o_rows)."""
+        T = self.T if T is None else T
+        return 2.0 * T * self.d * (self.qkv_cols + self.o_rows)
+
+    def weight_bytes(self) -> int:
+        """bf16 bytes of the shard's two weight blocks."""
+        return 2 * self.d * (self.qkv_cols + self.o_rows)
+
+
+ATTN_WORKLOADS = {
+    "llama70b_attn_prefill_tp8": AttnWorkload("llama70b_attn_prefill_tp8", 4096, 8192, 64, 8, 128,
+                                              8, "Llama-70B attention projections, TP=8, prefill"),
+    "llama70b_attn_decode_tp8": AttnWorkload("llama70b_attn_decode_tp8", 64, 8192, 64, 8, 128, 8,
+                                             "Llama-70B attention projections, TP=8, decode",
+                                             Ts=(1, 8, 64)),
+    "gpt_attn_p4": AttnWorkload("gpt_attn_p4", 2048, 4096, 32, 32, 128, 4,
+                                "GPT-style attention projections, 32 heads, p=4"),
 }
 
 
@@ -139,3 +186,18 @@ def small_case(T: int, d: int, k: int, seed: int, swiglu: bool, bias: bool, x_st
     b1 = gaussian_bf16((k,), seed + 3, 0.5) if bias else None
     W2 = gaussian_bf16((k, d), seed + 4, w_std)
     return X, W1, Wu, b1, W2
+
+
+def attn_weights(d: int, Hq: int, Hkv: int, dh: int, seed: int = 46):
+    """Full attention projection weights, bf16 N(0, 0.02^2): the packed QKV matrix
+    [d, (Hq + 2 Hkv) dh] (query heads, then key heads, then value heads) from seed
+    `seed`, the output projection [Hq dh, d] from seed + 1."""
+    Wqkv = gaussian_bf16((d, (Hq + 2 * Hkv) * dh), seed, WEIGHT_STD)
+    WO = gaussian_bf16((Hq * dh, d), seed + 1, WEIGHT_STD)
+    return Wqkv, WO
+
+
+def attn_output(T: int, width: int, seed: int = 48):
+    """A stand-in for one shard's attention output [T, width], bf16 N(0, 1): the
+    input of the row-parallel output projection."""
+    return gaussian_bf16((T, width), seed)

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("tp_col_linear", "tp_row_linear", "tp_mlp_shard", "tp_partial_sum",
               "tp_mlp_simulated", "tp_workspace_bytes", "tp_shard_bounds", "tp_status_string",
-              "tp_last_error_message", "tp_abi_version", "tp_calib_mfma_bf16"):
+              "tp_last_error_message", "tp_abi_version", "tp_calib_mfma_bf16", "tp_qkv_linear",
+              "tp_qkv_workspace_bytes"):
         assert n in names
 
 
@@ -222,3 +223,67 @@ def test_calibration_errors():
     assert status_name(lib.tp_calib_mfma_bf16(1, 0, P(A), 4, None)) == "TP_ERR_BAD_SHAPE"
     assert status_name(lib.tp_calib_mfma_bf16(1, 10, P(A), 0, None)) == "TP_ERR_BAD_SHAPE"
     assert status_name(lib.tp_calib_mfma_bf16(0, 10, None, 4, None)) == "TP_ERR_NULL_POINTER"
+
+
+# --- attention projections ---------------------------------------------------
+def qkv(dt=1, T=4, d=64, Hq=8, Hkv=2, dh=16, i=0, p=2, X=A, ldx=64, W=A, ldw=192, b=None, O=A,
+        ldo=96, ws=None, wsb=0):
+    return tp.library().tp_qkv_linear(dt, T, d, Hq, Hkv, dh, i, p, P(X), ldx, P(W), ldw, P(b),
+                                      P(O), ldo, P(ws), wsb, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(Hkv=1, ldw=160), "TP_ERR_NOT_DIVISIBLE"),     # 1 key/value head over 2 GPUs
+    (dict(Hq=5, ldw=144, ldo=72), "TP_ERR_NOT_DIVISIBLE"),
+    (dict(i=2), "TP_ERR_BAD_SHARD"),
+    (dict(p=0), "TP_ERR_BAD_SHARD"),
+    (dict(p=65), "TP_ERR_BAD_SHARD"),
+    (dict(T=-1), "TP_ERR_BAD_SHAPE"),
+    (dict(d=0), "TP_ERR_BAD_SHAPE"),
+    (dict(Hq=0), "TP_ERR_BAD_SHAPE"),
+    (dict(Hkv=0), "TP_ERR_BAD_SHAPE"),
+    (dict(dh=0), "TP_ERR_BAD_SHAPE"),
+    (dict(dh=12, ldw=144, ldo=72), "TP_ERR_MISALIGNED"),   # head width not a multiple of 8
+    (dict(d=60), "TP_ERR_MISALIGNED"),
+    (dict(ldw=184), "TP_ERR_BAD_SHAPE"),              # narrower than (Hq + 2 Hkv) dh
+    (dict(ldo=88), "TP_ERR_BAD_SHAPE"),               # narrower than the shard's columns
+    (dict(ldx=60), "TP_ERR_BAD_SHAPE"),
+    (dict(X=None), "TP_ERR_NULL_POINTER"),
+    (dict(W=None), "TP_ERR_NULL_POINTER"),
+    (dict(O=None), "TP_ERR_NULL_POINTER"),
+    (dict(b=MIS), "TP_ERR_MISALIGNED"),
+    (dict(dt=5), "TP_ERR_BAD_DTYPE"),
+    (dict(T=1, d=8192, ldx=8192, Hq=64, Hkv=8, dh=128, ldw=10240, p=8, ldo=1280),
+     "TP_ERR_WORKSPACE"),
+    (dict(T=4, ldw=1 << 23), "TP_ERR_BAD_SHAPE"),      # beyond the few-token kernels' offsets
+])
+def test_qkv_linear_rejects(kw, expect):
+    assert status_name(qkv(**kw)) == expect
+    assert tp.library().tp_last_error_message().decode() != ""
+
+
+@no_gpu
+def test_qkv_zero_tokens_and_fp32_alignment():
+    assert status_name(qkv(T=0, X=None, O=None)) == "TP_OK"
+    assert status_name(qkv(T=0, W=None)) == "TP_ERR_NULL_POINTER"
+    # fp32: a head width of 12 is allowed (multiple of 4)
+    assert status_name(qkv(dt=0, T=0, dh=12, ldw=144, ldo=72)) == "TP_OK"
+
+
+def test_qkv_workspace_bytes():
+    bf16 = torch.bfloat16
+    assert tp.tp_qkv_workspace_bytes(bf16, 4096, 8192, 64, 8, 128, 8) == 0
+    for T in (1, 8, 64):
+        assert tp.tp_qkv_workspace_bytes(bf16, T, 8192, 64, 8, 128, 8) > 0
+    assert tp.tp_qkv_workspace_bytes(torch.float32, 8, 8192, 64, 8, 128, 8) == 0
+    # invalid arguments report 0 and leave the last error message alone
+    lib = tp.library()
+    assert status_name(lib.tp_shard_bounds(64, 0, 5, ctypes.byref(ctypes.c_int64()),
+                                           ctypes.byref(ctypes.c_int64()))) \
+        == "TP_ERR_NOT_DIVISIBLE"
+    msg = lib.tp_last_error_message().decode()
+    assert tp.tp_qkv_workspace_bytes(bf16, 8, 8192, 64, 8, 128, 16) == 0   # 8 kv heads / 16
+    assert tp.tp_qkv_workspace_bytes(bf16, 8, 8192, 64, 8, 120, 8) > 0     # dh = 120 is aligned
+    assert tp.tp_qkv_workspace_bytes(bf16, 8, 8192, 64, 8, 100, 8) == 0    # dh = 100 misaligned
+    assert lib.tp_last_error_message().decode() == msg

@@ -1,0 +1,255 @@
+"""GPU parity of the attention projections of one head shard: the fused QKV
+projection (tp_qkv_linear, column-parallel by heads) and the output projection
+(tp_row_linear over the head rows), through the C ABI, against the CPU oracle on
+the same seeded inputs.  Small cases span several tiles with ragged tails and
+head blocks that start inside a tile; full-size workloads are checked on
+sampled token rows."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import megatron_tensor_mlp_amd as tp
+import oracle
+from megatron_tensor_mlp_amd import synth
+from tests.helpers import assert_bf16_close, assert_f32_close, f64, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def run_qkv(X, Wqkv, Hq, Hkv, dh, i, p, bqkv=None, ldpad=0):
+    T = X.shape[0]
+    n = (Hq + 2 * Hkv) * dh // p
+    buf = torch.full((T, n + ldpad), float("nan"), dtype=X.dtype, device=DEV)
+    out = buf[:, :n]
+    tp.tp_qkv_linear(dev(X), dev(Wqkv), Hq, Hkv, dh, i, p, out, bqkv=dev(bqkv))
+    torch.cuda.synchronize()
+    return out
+
+
+def small_inputs(T, d, Hq, Hkv, dh, seed, bias, dtype=torch.bfloat16):
+    ncol = (Hq + 2 * Hkv) * dh
+    X = synth.gaussian_bf16((T, d), seed)
+    W = synth.gaussian_bf16((d, ncol), seed + 1, synth.WEIGHT_STD)
+    b = synth.gaussian_bf16((ncol,), seed + 2, 0.5) if bias else None
+    if dtype == torch.float32:
+        X, W = X.float(), W.float()
+        b = b.float() if b is not None else None
+    return X, W, b
+
+
+# (T, d, Hq, Hkv, dh, p, bias, what)
+QKV_CASES = [
+    (300, 264, 8, 2, 64, 2, True, "tiled, key block starts inside a tile"),
+    (257, 520, 12, 4, 40, 4, False, "tiled, head width 40: blocks start mid 16-column group"),
+    (65, 136, 4, 4, 16, 1, True, "tiled, one shard, multi-head (Hq = Hkv)"),
+    (513, 1032, 16, 8, 24, 8, True, "tiled, 8 shards, ragged rows"),
+    (1, 264, 8, 2, 64, 2, True, "few-token, one token"),
+    (8, 520, 12, 4, 40, 4, True, "few-token, head width 40"),
+    (17, 1032, 16, 8, 32, 8, False, "few-token, 8 shards"),
+    (64, 4104, 8, 1, 128, 1, True, "few-token, 64 tokens, one key/value head"),
+]
+
+
+@pytest.mark.parametrize("T,d,Hq,Hkv,dh,p,bias,what", QKV_CASES)
+def test_qkv_bf16_small(T, d, Hq, Hkv, dh, p, bias, what):
+    X, W, b = small_inputs(T, d, Hq, Hkv, dh, 300 + T, bias)
+    for i in sorted({0, p // 2, p - 1}):
+        say(f"qkv case T={T} d={d} Hq={Hq} Hkv={Hkv} dh={dh} p={p} i={i}: {what}")
+        out = run_qkv(X, W, Hq, Hkv, dh, i, p, bqkv=b)
+        ref = oracle.qkv_shard(f64(X), f64(W), Hq, Hkv, dh, i, p,
+                               bqkv=f64(b) if b is not None else None)
+        assert_bf16_close(out, ref, f"QKV shard {i}")
+
+
+@pytest.mark.parametrize("T", [5, 64, 300])
+def test_qkv_padded_leading_dimensions(T):
+    """Output view with a leading dimension above its width (padding is NaN and
+    must stay NaN), input and weight as column views of wider buffers."""
+    Hq, Hkv, dh, p, d = 8, 4, 32, 4, 264
+    X, W, b = small_inputs(T, d, Hq, Hkv, dh, 9, True)
+    Xb = torch.zeros(T, d + 40, dtype=X.dtype, device=DEV)
+    Xb[:, :d] = dev(X)
+    Wb = torch.zeros(d, W.shape[1] + 24, dtype=W.dtype, device=DEV)
+    Wb[:, :W.shape[1]] = dev(W)
+    n = (Hq + 2 * Hkv) * dh // p
+    buf = torch.full((T, n + 16), float("nan"), dtype=X.dtype, device=DEV)
+    tp.tp_qkv_linear(Xb[:, :d], Wb[:, :W.shape[1]], Hq, Hkv, dh, 2, p, buf[:, :n], bqkv=dev(b))
+    torch.cuda.synchronize()
+    ref = oracle.qkv_shard(f64(X), f64(W), Hq, Hkv, dh, 2, p, bqkv=f64(b))
+    assert_bf16_close(buf[:, :n], ref, "QKV")
+    assert bool(torch.isnan(buf[:, n:]).all())
+
+
+def one_hot_qkv(T, d, ncol, seed):
+    """Integer inputs and one-hot +-1 weight columns (column g: row (7g + 3) mod d):
+    every output is a small integer, exact in bf16."""
+    rng = np.random.default_rng(seed)
+    X = rng.integers(-120, 121, (T, d)).astype(np.float32)
+    W = np.zeros((d, ncol), np.float32)
+    sg = rng.choice([-1.0, 1.0], ncol)
+    for g in range(ncol):
+        W[(7 * g + 3) % d, g] = sg[g]
+    b = rng.integers(-8, 9, (ncol,)).astype(np.float32)
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16)  # noqa: E731
+    return bf(X), bf(W), bf(b)
+
+
+@pytest.mark.parametrize("T", [5, 64, 300])
+def test_qkv_head_bookkeeping_exact(T):
+    """Every shard's columns come from exactly the right heads of the right block
+    (bit-exact with one-hot integer weights), on both paths."""
+    d, Hq, Hkv, dh, p = 264, 16, 4, 16, 4
+    X, W, b = one_hot_qkv(T, d, (Hq + 2 * Hkv) * dh, T)
+    for i in range(p):
+        out = run_qkv(X, W, Hq, Hkv, dh, i, p, bqkv=b)
+        ref = oracle.qkv_shard(f64(X), f64(W), Hq, Hkv, dh, i, p, bqkv=f64(b))
+        assert np.array_equal(f64(out), ref), f"shard {i}"
+
+
+def test_qkv_f32():
+    """fp32 path (head width 12, allowed in fp32), several shards, with bias."""
+    T, d, Hq, Hkv, dh, p = 37, 132, 8, 4, 12, 4
+    X, W, b = small_inputs(T, d, Hq, Hkv, dh, 77, True, dtype=torch.float32)
+    for i in range(p):
+        out = run_qkv(X, W, Hq, Hkv, dh, i, p, bqkv=b)
+        ref = oracle.qkv_shard(f64(X), f64(W), Hq, Hkv, dh, i, p, bqkv=f64(b))
+        assert_f32_close(out, ref, f"QKV shard {i}")
+
+
+def test_qkv_zero_tokens_and_bad_heads():
+    X = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    W = torch.zeros(64, 12 * 16, dtype=torch.bfloat16, device=DEV)
+    out = torch.empty(0, 96, dtype=torch.bfloat16, device=DEV)
+    tp.tp_qkv_linear(X, W, 8, 2, 16, 1, 2, out)
+    # one key/value head cannot be split two ways; the output is left untouched
+    X = torch.ones(4, 64, dtype=torch.bfloat16, device=DEV)
+    W = torch.zeros(64, 10 * 16, dtype=torch.bfloat16, device=DEV)
+    out = torch.full((4, 80), 7.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_qkv_linear(X, W, 8, 1, 16, 0, 2, out)
+    assert e.value.name == "TP_ERR_NOT_DIVISIBLE"
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+
+
+def _attention(Q, K, V, hq, hkv, dh):
+    """Test-side softmax attention per head (fp64); query head h reads key/value
+    head h // (hq / hkv)."""
+    g = hq // hkv
+    outs = []
+    for h in range(hq):
+        c = h // g
+        q, k, v = Q[:, h * dh:(h + 1) * dh], K[:, c * dh:(c + 1) * dh], V[:, c * dh:(c + 1) * dh]
+        s = q @ k.T / math.sqrt(dh)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        outs.append((e / e.sum(axis=1, keepdims=True)) @ v)
+    return np.concatenate(outs, axis=1)
+
+
+def test_head_split_attention_block():
+    """The attention sandwich on the GPU path: each shard's QKV projection, a
+    (test-side) attention over the shard's heads, the shard's row block of W_O
+    into an fp32 partial, and the on-device sum of the partials, against the
+    unsharded block computed from the oracle (full projection, attention over all
+    heads, full output projection)."""
+    T, d, Hq, Hkv, dh, p = 96, 264, 8, 4, 32, 4
+    X, W, b = small_inputs(T, d, Hq, Hkv, dh, 5, True)
+    WO = synth.gaussian_bf16((Hq * dh, d), 8, synth.WEIGHT_STD)
+    qw, kw = Hq * dh // p, Hkv * dh // p
+    parts = []
+    for i in range(p):
+        s = f64(run_qkv(X, W, Hq, Hkv, dh, i, p, bqkv=b))
+        O = _attention(s[:, :qw], s[:, qw:qw + kw], s[:, qw + kw:], Hq // p, Hkv // p, dh)
+        Ob = torch.from_numpy(O).to(torch.bfloat16).to(DEV)
+        Z = torch.empty(T, d, device=DEV)
+        tp.tp_row_linear(Ob, dev(WO), i, p, Z)
+        parts.append(Z)
+    out = torch.empty(T, d, device=DEV)
+    tp.tp_partial_sum(parts, out)
+    torch.cuda.synchronize()
+    full = oracle.qkv_shard(f64(X), f64(W), Hq, Hkv, dh, 0, 1, bqkv=f64(b))
+    Of = _attention(full[:, :Hq * dh], full[:, Hq * dh:(Hq + Hkv) * dh], full[:, (Hq + Hkv) * dh:],
+                    Hq, Hkv, dh)
+    ref = oracle.row_shard(Of, f64(WO), 0, 1)
+    assert_bf16_close(out, ref, "attention block")
+
+
+# --------------------------------------------------------------------- full-size workloads
+def sampled_rows(T, n):
+    rows = {0, 1, T - 1, T // 2}
+    for tile in (64, 128, 256):
+        rows |= {min(T - 1, tile - 1), min(T - 1, tile)}
+    rng = np.random.default_rng(T + 1)
+    rows |= set(rng.integers(0, T, max(0, n - len(rows))).tolist())
+    return sorted(r for r in rows if 0 <= r < T)
+
+
+@pytest.fixture(scope="module")
+def llama_attn():
+    W = synth.ATTN_WORKLOADS["llama70b_attn_prefill_tp8"]
+    Wqkv, WO = synth.attn_weights(W.d, W.Hq, W.Hkv, W.dh)
+    return W, Wqkv, WO, dev(Wqkv), dev(WO)
+
+
+@pytest.mark.parametrize("i", [0, 5, 7])
+def test_llama_qkv_prefill_full_size(llama_attn, i):
+    """Llama-70B attention at TP = 8 (64 query and 8 key/value heads of 128,
+    d = 8192), T = 4096 tokens, shard i of the full packed weight; the output
+    projection's row block on a stand-in attention output."""
+    W, Wqkv, WO, Wqkv_d, WO_d = llama_attn
+    X = synth.llama_tokens(W.T, W.d)
+    say(f"workload {W.name}: T={W.T} d={W.d} shard {i}")
+    Xd = dev(X)
+    out = torch.empty(W.T, W.qkv_cols, dtype=torch.bfloat16, device=DEV)
+    tp.tp_qkv_linear(Xd, Wqkv_d, W.Hq, W.Hkv, W.dh, i, W.p, out)
+    O = synth.attn_output(W.T, W.o_rows)
+    Z = torch.empty(W.T, W.d, device=DEV)
+    tp.tp_row_linear(dev(O), WO_d, i, W.p, Z)
+    torch.cuda.synchronize()
+    rows = sampled_rows(W.T, 10)
+    ref = oracle.qkv_shard(f64(X[rows]), f64(Wqkv), W.Hq, W.Hkv, W.dh, i, W.p)
+    assert_bf16_close(out[rows], ref, "QKV")
+    Zr = oracle.row_shard(f64(O[rows]), f64(WO), i, W.p)
+    assert_bf16_close(Z[rows], Zr, "Z")
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(Z).all())
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_llama_qkv_decode_full_size(llama_attn, T):
+    """Llama-70B attention projections at TP = 8, few-token decode (all rows)."""
+    W, Wqkv, WO, Wqkv_d, WO_d = llama_attn
+    i = 3
+    X = synth.llama_tokens(T, W.d)
+    say(f"workload llama70b_attn_decode_tp8: T={T} shard {i}")
+    out = torch.empty(T, W.qkv_cols, dtype=torch.bfloat16, device=DEV)
+    tp.tp_qkv_linear(dev(X), Wqkv_d, W.Hq, W.Hkv, W.dh, i, W.p, out)
+    O = synth.attn_output(T, W.o_rows)
+    Z = torch.empty(T, W.d, device=DEV)
+    tp.tp_row_linear(dev(O), WO_d, i, W.p, Z)
+    torch.cuda.synchronize()
+    ref = oracle.qkv_shard(f64(X), f64(Wqkv), W.Hq, W.Hkv, W.dh, i, W.p)
+    assert_bf16_close(out, ref, "QKV")
+    assert_bf16_close(Z, oracle.row_shard(f64(O), f64(WO), i, W.p), "Z")
+
+
+def test_gpt_qkv_full_size():
+    """GPT-style attention (32 heads of 128, d = 4096) over 4 GPUs, T = 2048."""
+    W = synth.ATTN_WORKLOADS["gpt_attn_p4"]
+    Wqkv, _ = synth.attn_weights(W.d, W.Hq, W.Hkv, W.dh, seed=50)
+    X = synth.gaussian_bf16((W.T, W.d), 42)
+    i = 2
+    say(f"workload {W.name}: T={W.T} d={W.d} shard {i}")
+    out = torch.empty(W.T, W.qkv_cols, dtype=torch.bfloat16, device=DEV)
+    tp.tp_qkv_linear(dev(X), dev(Wqkv), W.Hq, W.Hkv, W.dh, i, W.p, out)
+    torch.cuda.synchronize()
+    rows = sampled_rows(W.T, 10)
+    ref = oracle.qkv_shard(f64(X[rows]), f64(Wqkv), W.Hq, W.Hkv, W.dh, i, W.p)
+    assert_bf16_close(out[rows], ref, "QKV")
