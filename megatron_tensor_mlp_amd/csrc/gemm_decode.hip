@@ -27,9 +27,12 @@
 // only one); the workgroup that arrives last sums the partials in k-range
 // order (so the result does not depend on which one that is), applies the
 // epilogue and sets the counter back to zero.  Partials are stored and loaded
-// as agent-scope atomics, which stay coherent across the XCDs without
-// flushing or invalidating the L2 caches (a release or acquire fence at agent
-// scope would do both, at a cost of several microseconds per workgroup).
+// 16 bytes per lane with the cache policy of agent-scope atomics (sc1), which
+// stays coherent across the XCDs without flushing or invalidating the L2
+// caches (a release or acquire fence at agent scope would do both, at a cost
+// of several microseconds per workgroup); the last arriver issues all loads
+// of a batch before its first add, so the reduction costs about one memory
+// round trip.
 #include <cstdlib>
 
 #include "device_common.hpp"
@@ -42,6 +45,9 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// Cache-policy operand of the buffer builtins: sc1, the agent-coherent policy.
+constexpr int CPOL_SC1 = 16;
 
 constexpr int NWAVE = 8;
 constexpr int RC = 16 * NWAVE;  // columns per workgroup
@@ -72,7 +78,7 @@ struct Geo {
   static constexpr int XLB = XW >= 1024 ? 1024 : 256;
   static constexpr int XL = XW >= XLB ? XW / XLB : 1;
   static constexpr int LPS = WL + XL;            // loads per wave per stage
-  static constexpr int PF = NWAVE * MB * 256;    // partial floats per workgroup
+  static constexpr int PF = NWAVE * MB * 256;    // partial floats per workgroup (one slot)
   static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(WL >= 1, "loads");
   static_assert(NST >= 3 && NST * SB <= 160 * 1024, "LDS");
@@ -125,7 +131,7 @@ DecodePlan make_plan(const GemmArgs &a) {
   if (smax < 1) smax = 1;
   if (S > smax) S = smax;
   if (S < 1) S = 1;
-  if (split_override() > 0) S = split_override();
+  if (split_override() > 0) S = split_override() < 4096 ? split_override() : 4096;
   const int64_t per = (steps + S - 1) / S;
   pl.kc = per * pl.bk;
   pl.S = (a.K + pl.kc - 1) / pl.kc;
@@ -308,23 +314,28 @@ __global__ __launch_bounds__(NWAVE * 64) void gemm_bf16_decode_kernel(const Gemm
   }
 
   // ---- split-K: publish the partial; the last arriver reduces --------------------
-  // Partials are written and read as agent-scope atomics, which the hardware
-  // keeps coherent across the XCDs' L2 caches without a cache write-back or
-  // invalidate; a wave's stores have completed once vmcnt reaches zero, before
-  // the barrier that precedes the counter update.  Slots of a block: the S
-  // gate (or only) partials in k-range order, then the S up partials.  Token
-  // rows past M (padding) are neither written nor read.
-  constexpr int NV = MB * 4;  // floats per lane
-  float *base = parts + blk * nparts * G::PF + (int64_t)wave * (NV * 64) + lane;
+  // Partials are written and read with the sc1 cache policy (what agent-scope
+  // atomics use), which the hardware keeps coherent across the XCDs' L2 caches
+  // without a cache write-back or invalidate; a wave's stores have completed
+  // once vmcnt reaches zero, before the barrier that precedes the counter
+  // update.  Slots of a block: the S gate (or only) partials in k-range order,
+  // then the S up partials.  A slot holds [wave][m][lane] 16-byte groups (lane
+  // accumulator block m: rows 16 m + 4 (lane / 16) + 0..3 of column lane % 16);
+  // groups with no token row below M (padding) are neither written nor read:
+  // their lanes get an offset past the buffer range, which the hardware drops
+  // (stores) or reads as zero (loads).
+  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+      parts + blk * nparts * G::PF, 0, 0x7fffffff, RSRC_WORD3);
+  uint32_t goff[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+    goff[m] = (16 * m + 4 * (lane >> 4) < M) ? (uint32_t)(((wave * MB + m) * 64 + lane) * 16) : OOB;
   {
-    float *mine = base + ((up ? S : 0) + s) * G::PF;
+    const uint32_t mine = (uint32_t)(((up ? S : 0) + s) * (G::PF * 4));
 #pragma unroll
     for (int m = 0; m < MB; ++m)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (16 * m + 4 * (lane >> 4) + v < M)
-          __hip_atomic_store(mine + (m * 4 + v) * 64, acc[m][v], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, acc[m]), rp,
+                                             goff[m] == OOB ? OOB : goff[m] + mine, 0, CPOL_SC1);
   }
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
   __syncthreads();
@@ -336,44 +347,47 @@ __global__ __launch_bounds__(NWAVE * 64) void gemm_bf16_decode_kernel(const Gemm
   __syncthreads();
   if (!s_last) return;
 
-  // Partials are read RCH k-ranges at a time (of each matrix), all loads of a
-  // chunk issued before any is added (ranges past S read the last one again
-  // and add nothing); the gate and up sums each run in k-range order.  Which
-  // sum a slot feeds is fixed at compile time: a run-time choice would put a
-  // branch, and so a wait, between the loads.
-  constexpr int RCH = 128 / (NMAT * NV) < 2 ? 2 : (128 / (NMAT * NV) > 8 ? 8 : 128 / (NMAT * NV));
+  // The last arriver loads RCH k-ranges of each matrix at a time, every load
+  // of a batch issued before any is added (ranges past S read nothing and add
+  // nothing), and sums gate and up each in k-range order.  Which sum a slot
+  // feeds is fixed at compile time: a run-time choice would put a branch, and
+  // so a wait, between the loads.  RCH is sized so that the batch stays within
+  // 128 VGPRs; it covers every k-range of the usual plans in one batch.
+  constexpr int RCH0 = 128 / (NMAT * MB * 4);
+  constexpr int RCH = RCH0 < 2 ? 2 : (RCH0 > 32 ? 32 : RCH0);
   f32x4 sum[NMAT][MB];
 #pragma unroll
   for (int q = 0; q < NMAT; ++q)
 #pragma unroll
     for (int m = 0; m < MB; ++m) sum[q][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   for (int64_t s2 = 0; s2 < S; s2 += RCH) {
-    float val[NMAT][RCH][NV];
+    f32x4 val[NMAT][RCH][MB];
 #pragma unroll
     for (int q = 0; q < NMAT; ++q)
 #pragma unroll
       for (int c = 0; c < RCH; ++c) {
-        const int64_t sc = q * S + ((s2 + c < S) ? s2 + c : S - 1);
-        const float *ps = base + sc * G::PF;
 #pragma unroll
-        for (int e = 0; e < NV; ++e) {
-          const int m = e / 4, v = e % 4;
-          val[q][c][e] = (16 * m + 4 * (lane >> 4) + v < M)
-                             ? __hip_atomic_load(ps + e * 64, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT)
-                             : 0.0f;
+        for (int m = 0; m < MB; ++m) val[q][c][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (s2 + c < S) {  // uniform: a scalar branch, no wait
+          const uint32_t slot = (uint32_t)((q * S + s2 + c) * (G::PF * 4));
+#pragma unroll
+          for (int m = 0; m < MB; ++m)
+            val[q][c][m] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rp, goff[m] != OOB ? goff[m] + slot : OOB, 0, CPOL_SC1));
         }
       }
+    // Keep the scheduler from interleaving the adds with the loads (it would,
+    // to save registers, and each add waits for its load).
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < RCH; ++c) {
-      if (s2 + c >= S) break;
+    for (int c = 0; c < RCH; ++c)
+      if (s2 + c < S) {
 #pragma unroll
-      for (int q = 0; q < NMAT; ++q)
+        for (int q = 0; q < NMAT; ++q)
 #pragma unroll
-        for (int m = 0; m < MB; ++m)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) sum[q][m][v] += val[q][c][m * 4 + v];
-    }
+          for (int m = 0; m < MB; ++m) sum[q][m] += val[q][c][m];
+      }
   }
   if (tid == 0) __hip_atomic_store(ctr + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   store_out<EPI, ACT, MB>(p, col, lane, sum[0], sum[NMAT - 1]);
