@@ -74,9 +74,14 @@ def _load():
         lib.oracle_partial_sum_f32.argtypes = [i64, i64, i32, vp, vp, vp]
         lib.oracle_num_threads.argtypes = []
         lib.oracle_qkv_shard_f64.argtypes = [i64, i64, i32, i32, i64, i32, i32, vp, vp, vp, vp]
+        lib.oracle_dactivation_f64.argtypes = [ci, i64, vp, vp]
+        lib.oracle_dactivation_f64.restype = None
+        lib.oracle_mlp_shard_backward_f64.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, vp, ci,
+                                                      vp, vp, vp, vp, vp, vp, vp, vp]
         for name in ("oracle_col_shard_f64", "oracle_row_shard_f64", "oracle_partial_sum_f64",
                      "oracle_mlp_unsharded_f64", "oracle_linear_f32", "oracle_col_shard_f32",
-                     "oracle_partial_sum_f32", "oracle_num_threads", "oracle_qkv_shard_f64"):
+                     "oracle_partial_sum_f32", "oracle_num_threads", "oracle_qkv_shard_f64",
+                     "oracle_mlp_shard_backward_f64"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -221,4 +226,40 @@ def qkv_shard(X, Wqkv, Hq, Hkv, dh, i, p, bqkv=None):
     out = np.empty((T, ncol // p), dtype=np.float64)
     _check(lib.oracle_qkv_shard_f64(T, d, Hq, Hkv, dh, i, p, _p(X), _p(W), _p(b), _p(out)),
            "qkv_shard")
+    return out
+
+
+def dactivation(act, x):
+    """Element-wise derivative of the activation in fp64 (kind 'swiglu' / 4 means SiLU')."""
+    lib = _load()
+    x = _c(x, np.float64)
+    y = np.empty_like(x)
+    lib.oracle_dactivation_f64(_act(act), x.size, _p(x), _p(y))
+    return y
+
+
+def mlp_shard_backward(X, W1, W2, dZ, i, p, act, b1=None, Wu=None, want_db1=None):
+    """Backward pass of shard i of p in fp64, given dZ [T, d].  Returns a dict with
+    dH ([T, s]; gated: [T, 2s] = [dG | dU]), dXp [T, d] (this shard's term of dX),
+    dW1 [d, s] (gated: dWg), dWu [d, s] (gated only), db1 [s] (when b1 is given and the
+    activation is not gated, or want_db1), dW2 [s, d]."""
+    lib = _load()
+    X, W1, W2, dZ = (_c(a, np.float64) for a in (X, W1, W2, dZ))
+    Wu, b1 = _c(Wu, np.float64), _c(b1, np.float64)
+    T, d = X.shape
+    k = W1.shape[1]
+    if k % p:
+        raise ValueError("k not divisible by p")
+    s = k // p
+    gated = _act(act) == ACT_SWIGLU
+    if want_db1 is None:
+        want_db1 = b1 is not None and not gated
+    out = {"dH": np.empty((T, 2 * s if gated else s)), "dXp": np.empty((T, d)),
+           "dW1": np.empty((d, s)), "dW2": np.empty((s, d))}
+    out["dWu"] = np.empty((d, s)) if gated else None
+    out["db1"] = np.empty(s) if want_db1 else None
+    _check(lib.oracle_mlp_shard_backward_f64(
+        T, d, k, i, p, _p(X), _p(W1), _p(Wu), _p(b1), _act(act), _p(W2), _p(dZ), _p(out["dH"]),
+        _p(out["dXp"]), _p(out["dW1"]), _p(out["dWu"]), _p(out["db1"]), _p(out["dW2"])),
+        "mlp_shard_backward")
     return out

@@ -1,6 +1,6 @@
 /*
- * CPU oracle for one tensor-parallel MLP shard (and the attention projections
- * of one head shard).
+ * CPU oracle for one tensor-parallel MLP shard, forward and backward (and the
+ * attention projections of one head shard).
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain reference that the
  * GPU library is checked against.  Only the test suite, the smoke check and
@@ -34,6 +34,9 @@
  *       a column-parallel linear whose column blocks are whole heads, and the
  *       output projection is the row-parallel linear above over the head
  *       columns (oracle_qkv_shard_f64 below).
+ *     - The backward pass of a shard (oracle_mlp_shard_backward_f64 below):
+ *       the row-parallel step's input gradient is local, the column-parallel
+ *       step's is one term of a sum over the shards.
  *
  * Every dot product is summed with its index ascending, in the precision of
  * the function (fp64, or fp32 for the *_f32 functions that pin the printed
@@ -373,5 +376,155 @@ int oracle_qkv_shard_f64(int64_t T, int64_t d, int32_t Hq, int32_t Hkv, int64_t 
     }
   }
   free(src);
+  return 0;
+}
+
+/* ---- the backward pass of one MLP shard ---------------------------------- */
+
+/*
+ * Derivative of the activation at x (kind 4 is SiLU here), from the
+ * definitions above:
+ *   GeLU, tanh form: with u = sqrt(2/pi) (x + 0.044715 x^3) and t = tanh(u),
+ *                    0.5 (1 + t) + 0.5 x (1 - t^2) sqrt(2/pi) (1 + 3 * 0.044715 x^2)
+ *   GeLU, erf form:  Phi(x) + x phi(x) = 0.5 (1 + erf(x / sqrt 2)) + x exp(-x^2 / 2) / sqrt(2 pi)
+ *   SiLU:            s (1 + x (1 - s)), s = 1 / (1 + exp(-x))
+ *   ReLU:            1 for x > 0, else 0 (0 at x = 0)
+ */
+static double dact_scalar_f64(int kind, double x) {
+  switch (kind) {
+    case OR_ACT_NONE:
+      return 1.0;
+    case OR_ACT_RELU:
+      return x > 0.0 ? 1.0 : 0.0;
+    case OR_ACT_GELU_TANH: {
+      const double c = sqrt(2.0 / M_PI);
+      const double t = tanh(c * (x + 0.044715 * x * x * x));
+      return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * x * x);
+    }
+    case OR_ACT_GELU_ERF:
+      return 0.5 * (1.0 + erf(x / sqrt(2.0))) + x * exp(-0.5 * x * x) / sqrt(2.0 * M_PI);
+    case OR_ACT_SWIGLU: {
+      const double s = 1.0 / (1.0 + exp(-x));
+      return s * (1.0 + x * (1.0 - s));
+    }
+  }
+  return NAN;
+}
+
+/* y[n] = act'(x[n]) (kind 4 is SiLU'). */
+void oracle_dactivation_f64(int kind, int64_t n, const double *x, double *y) {
+  for (int64_t e = 0; e < n; ++e) y[e] = dact_scalar_f64(kind, x[e]);
+}
+
+/*
+ * Backward pass of shard i of p, fp64, given the gradient dZ [T,d] of the
+ * loss with respect to the block output Z = sum_i Z_i.
+ *
+ * The reduction after the row-parallel step passes the same dZ to every
+ * shard (its backward is the identity), and the row-parallel step's input
+ * gradient is local: dY_i = dZ B_i^T.  The activation is element-wise, so
+ * dH_i = dY_i * act'(H_i) is local too.  The column-parallel step's input
+ * gradient is one term of a sum over the shards, dX = sum_i dH_i A_i^T, which
+ * is what the all-reduce before the block adds up ("Transformer math: tensor
+ * parallel", sections "Column-parallel: split the weight by output columns",
+ * "Row-parallel: split the weight by input rows" and "The f and g conjugate
+ * operators").  The weight gradients follow from Y_i = act(X A_i + b1_i) and
+ * Z_i = Y_i B_i: dA_i = X^T dH_i, db1_i = column sums of dH_i, dB_i = Y_i^T dZ.
+ * For the gated variant Y_i = SiLU(G_i) * U_i with G_i = X Wg_i, U_i = X Wu_i:
+ * dG_i = dY_i * U_i * SiLU'(G_i), dU_i = dY_i * SiLU(G_i),
+ * dX_i = dG_i Wg_i^T + dU_i Wu_i^T, dWg_i = X^T dG_i, dWu_i = X^T dU_i.
+ *
+ * The pre-activations are computed here from X and the weights (nothing is
+ * taken from a forward run).  Inputs are the full matrices (as the forward
+ * functions take them); outputs are compact:
+ *   dH  [T,s] (gated: [T,2s], dG_i in columns [0,s), dU_i in [s,2s))
+ *   dXp [T,d]   this shard's term of dX
+ *   dW1 [d,s]   (gated: dWg_i)       dWu [d,s] (gated only, else unused)
+ *   db1 [s] or NULL (not with the gated variant)
+ *   dW2 [s,d]
+ * Every sum runs with its index ascending (dXp: over the gate columns, then
+ * over the up columns).
+ */
+int oracle_mlp_shard_backward_f64(int64_t T, int64_t d, int64_t k, int32_t i, int32_t p,
+                                  const double *X, const double *W1, const double *Wu,
+                                  const double *b1, int act, const double *W2, const double *dZ,
+                                  double *dH, double *dXp, double *dW1, double *dWu, double *db1,
+                                  double *dW2) {
+  if (!shard_ok(k, i, p)) return -1;
+  const int gated = act == OR_ACT_SWIGLU;
+  if (gated && (Wu == NULL || dWu == NULL || db1 != NULL)) return -1;
+  const int64_t s = k / p, c0 = (int64_t)i * s, hw = gated ? 2 * s : s;
+  const size_t ts = (size_t)(T > 0 ? T : 1) * (size_t)(s > 0 ? s : 1);
+  double *H = (double *)malloc(sizeof(double) * ts);  /* pre-activation (gate for SwiGLU) */
+  double *U = (double *)malloc(sizeof(double) * ts);  /* up projection (SwiGLU)           */
+  double *Y = (double *)malloc(sizeof(double) * ts);  /* activation output               */
+  if (!H || !U || !Y) {
+    free(H);
+    free(U);
+    free(Y);
+    return -1;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t j = 0; j < s; ++j) {
+      double h = 0.0, u = 0.0, dy = 0.0;
+      for (int64_t c = 0; c < d; ++c) h += X[t * d + c] * W1[c * k + c0 + j];
+      if (gated)
+        for (int64_t c = 0; c < d; ++c) u += X[t * d + c] * Wu[c * k + c0 + j];
+      else if (b1)
+        h += b1[c0 + j];
+      for (int64_t n = 0; n < d; ++n) dy += dZ[t * d + n] * W2[(c0 + j) * d + n];
+      H[t * s + j] = h;
+      U[t * s + j] = u;
+      if (gated) {
+        const double sg = act_scalar_f64(OR_ACT_SWIGLU, h);
+        Y[t * s + j] = sg * u;
+        dH[t * hw + j] = dy * u * dact_scalar_f64(OR_ACT_SWIGLU, h);
+        dH[t * hw + s + j] = dy * sg;
+      } else {
+        Y[t * s + j] = act_scalar_f64(act, h);
+        dH[t * hw + j] = dy * dact_scalar_f64(act, h);
+      }
+    }
+  }
+  /* dX_i = dH_i W1_i^T (+ dU_i Wu_i^T) */
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < s; ++j) acc += dH[t * hw + j] * W1[c * k + c0 + j];
+      if (gated)
+        for (int64_t j = 0; j < s; ++j) acc += dH[t * hw + s + j] * Wu[c * k + c0 + j];
+      dXp[t * d + c] = acc;
+    }
+  /* dW1_i = X^T dH_i, dWu_i = X^T dU_i */
+#pragma omp parallel for schedule(static)
+  for (int64_t c = 0; c < d; ++c)
+    for (int64_t j = 0; j < s; ++j) {
+      double a = 0.0, b = 0.0;
+      for (int64_t t = 0; t < T; ++t) {
+        a += X[t * d + c] * dH[t * hw + j];
+        if (gated) b += X[t * d + c] * dH[t * hw + s + j];
+      }
+      dW1[c * s + j] = a;
+      if (gated) dWu[c * s + j] = b;
+    }
+  if (db1)
+    for (int64_t j = 0; j < s; ++j) {
+      double a = 0.0;
+      for (int64_t t = 0; t < T; ++t) a += dH[t * hw + j];
+      db1[j] = a;
+    }
+  /* dW2_i = Y_i^T dZ */
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < s; ++j)
+    for (int64_t n = 0; n < d; ++n) {
+      double a = 0.0;
+      for (int64_t t = 0; t < T; ++t) a += Y[t * s + j] * dZ[t * d + n];
+      dW2[j * d + n] = a;
+    }
+  free(H);
+  free(U);
+  free(Y);
   return 0;
 }

@@ -48,6 +48,23 @@ MUTANTS = [
      " h < (part == 0 ? (int64_t)i * per_gpu : i) + per_gpu; ++h)", 0),
     ("qkv bias not mapped", "QKV[t * nout + n] = b ? acc + b[src[n]] : acc;",
      "QKV[t * nout + n] = b ? acc + b[n] : acc;", 0),
+    ("gelu_tanh derivative drops the sech^2 factor", "0.5 * x * (1.0 - t * t) * c *",
+     "0.5 * x * c *", 0),
+    ("gelu_erf derivative drops the x factor", "x * exp(-0.5 * x * x) / sqrt(2.0 * M_PI)",
+     "exp(-0.5 * x * x) / sqrt(2.0 * M_PI)", 0),
+    ("silu derivative wrong sign", "return s * (1.0 + x * (1.0 - s));", "return s * (1.0 + x * s);", 0),
+    ("swiglu up gradient uses the up value", "dH[t * hw + s + j] = dy * sg;",
+     "dH[t * hw + s + j] = dy * u;", 0),
+    ("row weight gradient from the pre-activation", "a += Y[t * s + j] * dZ[t * d + n];",
+     "a += H[t * s + j] * dZ[t * d + n];", 0),
+    ("hidden gradient reads W2 transposed", "dy += dZ[t * d + n] * W2[(c0 + j) * d + n];",
+     "dy += dZ[t * d + n] * W2[n * k + c0 + j];", 0),
+    ("input gradient drops the up term",
+     "acc += dH[t * hw + s + j] * Wu[c * k + c0 + j];", "", 0),
+    ("input gradient ignores the shard offset", "acc += dH[t * hw + j] * W1[c * k + c0 + j];",
+     "acc += dH[t * hw + j] * W1[c * k + j];", 0),
+    ("bias gradient drops the first token", "for (int64_t t = 0; t < T; ++t) a += dH[t * hw + j];",
+     "for (int64_t t = 1; t < T; ++t) a += dH[t * hw + j];", 0),
 ]
 
 

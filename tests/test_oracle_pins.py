@@ -509,3 +509,183 @@ def test_qkv_divisibility_errors():
         oracle.qkv_shard(X, np.zeros((4, 9 * 2)), 3, 3, 2, 0, 2)   # Hq = 3 on 2 GPUs
     with pytest.raises(ValueError):
         oracle.qkv_shard(X, np.zeros((4, 12 * 2)), 4, 4, 2, 2, 2)  # i outside [0, p)
+
+
+# ---------------------------------------------------------------- P-11 -------
+# The backward pass of the shard: the column-parallel step's input gradient is
+# a sum over the shards (what the all-reduce before the block adds up), the
+# row-parallel step's is local ('Transformer math: tensor parallel', sections
+# on the column- and row-parallel splits and the f and g operators).
+def _bw_case(T, d, k, seed, gated, bias):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, d))
+    W1 = rng.standard_normal((d, k)) / math.sqrt(d)
+    Wu = rng.standard_normal((d, k)) / math.sqrt(d) if gated else None
+    b1 = rng.standard_normal(k) * 0.5 if bias else None
+    W2 = rng.standard_normal((k, d)) / math.sqrt(k)
+    dZ = rng.standard_normal((T, d))
+    return X, W1, Wu, b1, W2, dZ
+
+
+def _assemble(X, W1, W2, dZ, p, act, b1=None, Wu=None):
+    """Full-matrix gradients from the p shards: dX summed, weight blocks placed."""
+    T, d = X.shape
+    k = W1.shape[1]
+    s = k // p
+    g = {"dX": np.zeros((T, d)), "dW1": np.zeros((d, k)), "dW2": np.zeros((k, d))}
+    if Wu is not None:
+        g["dWu"] = np.zeros((d, k))
+    if b1 is not None:
+        g["db1"] = np.zeros(k)
+    parts = []
+    for i in range(p):
+        o = oracle.mlp_shard_backward(X, W1, W2, dZ, i, p, act, b1=b1, Wu=Wu)
+        parts.append(o["dXp"])
+        g["dW1"][:, i * s:(i + 1) * s] = o["dW1"]
+        g["dW2"][i * s:(i + 1) * s] = o["dW2"]
+        if Wu is not None:
+            g["dWu"][:, i * s:(i + 1) * s] = o["dWu"]
+        if b1 is not None:
+            g["db1"][i * s:(i + 1) * s] = o["db1"]
+    g["dX"] = oracle.partial_sum(parts)
+    return g
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "gelu_erf", "relu", "none", "swiglu"])
+@pytest.mark.parametrize("p", [1, 2, 4])
+def test_backward_finite_differences(act, p):
+    """Central differences of L = sum(dZ * Z), Z from the forward oracle, against
+    the assembled shard gradients for every input and weight entry."""
+    gated = act == "swiglu"
+    X, W1, Wu, b1, W2, dZ = _bw_case(3, 5, 8, 17 + p, gated, not gated)
+    g = _assemble(X, W1, W2, dZ, p, act, b1=b1, Wu=Wu)
+
+    def loss(X, W1, Wu, b1, W2):
+        return float(np.sum(dZ * oracle.mlp_unsharded(X, W1, W2, act, b1=b1, Wu=Wu)))
+
+    args = {"X": X, "W1": W1, "W2": W2}
+    if gated:
+        args["Wu"] = Wu
+    else:
+        args["b1"] = b1
+    h = 1e-6
+    for name, arr in args.items():
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            kw = {key: v.copy() for key, v in args.items()}
+            kw[name][idx] += h
+            up = loss(kw["X"], kw["W1"], kw.get("Wu"), kw.get("b1"), kw["W2"])
+            kw[name][idx] -= 2 * h
+            dn = loss(kw["X"], kw["W1"], kw.get("Wu"), kw.get("b1"), kw["W2"])
+            num[idx] = (up - dn) / (2 * h)
+        ana = g["d" + name]
+        err = np.max(np.abs(num - ana)) / max(np.max(np.abs(ana)), 1e-300)
+        assert err < 1e-6, (name, err)
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "gelu_erf", "relu", "swiglu"])
+def test_backward_against_torch_autograd(act):
+    """torch's fp64 CPU autograd (its own GeLU, SiLU and ReLU) on the unsharded
+    block agrees with the assembled shard gradients."""
+    gated = act == "swiglu"
+    X, W1, Wu, b1, W2, dZ = _bw_case(6, 16, 32, 5, gated, not gated)
+    g = _assemble(X, W1, W2, dZ, 4, act, b1=b1, Wu=Wu)
+    t = {n: torch.tensor(v, dtype=torch.float64, requires_grad=True)
+         for n, v in (("X", X), ("W1", W1), ("W2", W2), ("Wu", Wu), ("b1", b1)) if v is not None}
+    F = torch.nn.functional
+    if gated:
+        Hh = F.silu(t["X"] @ t["W1"]) * (t["X"] @ t["Wu"])
+    else:
+        pre = t["X"] @ t["W1"] + t["b1"]
+        Hh = {"gelu_tanh": lambda x: F.gelu(x, approximate="tanh"), "gelu_erf": F.gelu,
+              "relu": F.relu}[act](pre)
+    Z = Hh @ t["W2"]
+    (Z * torch.tensor(dZ)).sum().backward()
+    for n, v in t.items():
+        assert rel_fro(g["d" + n], v.grad.numpy()) < 1e-12, n
+
+
+def test_backward_linear_closed_form():
+    """With no activation: dX = dZ (W1 W2)^T, dW1 = X^T dZ W2^T, dW2 = (X W1 + b1)^T dZ,
+    db1 = column sums of dZ W2^T (numpy)."""
+    X, W1, _, b1, W2, dZ = _bw_case(7, 12, 24, 9, False, True)
+    g = _assemble(X, W1, W2, dZ, 3, "none", b1=b1)
+    assert rel_fro(g["dX"], dZ @ (W1 @ W2).T) < 1e-12
+    assert rel_fro(g["dW1"], X.T @ (dZ @ W2.T)) < 1e-12
+    assert rel_fro(g["dW2"], (X @ W1 + b1).T @ dZ) < 1e-12
+    assert rel_fro(g["db1"], (dZ @ W2.T).sum(axis=0)) < 1e-12
+
+
+@pytest.mark.parametrize("T,d,k,p", [(1, 2, 2, 1), (2, 3, 4, 2), (3, 2, 6, 3)])
+def test_backward_brute_force_exact_relu(T, d, k, p):
+    """Exact rationals on small integers with ReLU (derivative 1 above 0, else 0):
+    every gradient entry is an exact integer."""
+    rng = np.random.default_rng(T * 10 + k)
+    X = rng.integers(-3, 4, (T, d))
+    W1 = rng.integers(-3, 4, (d, k))
+    b1 = rng.integers(-2, 3, (k,))
+    W2 = rng.integers(-3, 4, (k, d))
+    dZ = rng.integers(-3, 4, (T, d))
+    F = Fraction
+    H = [[sum(F(int(X[t, c])) * int(W1[c, j]) for c in range(d)) + int(b1[j]) for j in range(k)]
+         for t in range(T)]
+    Y = [[max(h, F(0)) for h in row] for row in H]
+    dY = [[sum(F(int(dZ[t, n])) * int(W2[j, n]) for n in range(d)) for j in range(k)]
+          for t in range(T)]
+    dH = [[dY[t][j] if H[t][j] > 0 else F(0) for j in range(k)] for t in range(T)]
+    dX = [[sum(dH[t][j] * int(W1[c, j]) for j in range(k)) for c in range(d)] for t in range(T)]
+    dW1 = [[sum(int(X[t, c]) * dH[t][j] for t in range(T)) for j in range(k)] for c in range(d)]
+    dW2 = [[sum(Y[t][j] * int(dZ[t, n]) for t in range(T)) for n in range(d)] for j in range(k)]
+    db1 = [sum(dH[t][j] for t in range(T)) for j in range(k)]
+    g = _assemble(X.astype(float), W1.astype(float), W2.astype(float), dZ.astype(float), p,
+                  "relu", b1=b1.astype(float))
+    assert np.array_equal(g["dX"], np.array(dX, dtype=float))
+    assert np.array_equal(g["dW1"], np.array(dW1, dtype=float))
+    assert np.array_equal(g["dW2"], np.array(dW2, dtype=float))
+    assert np.array_equal(g["db1"], np.array(db1, dtype=float))
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "swiglu"])
+def test_backward_shard_blocks_equal_unsharded(act):
+    """Each shard's weight-gradient block, and its columns of dH, are exactly the
+    corresponding block of the p = 1 result (the same sums in the same order);
+    the sum of the shards' dX terms equals the p = 1 dX up to reassociation."""
+    gated = act == "swiglu"
+    X, W1, Wu, b1, W2, dZ = _bw_case(5, 12, 32, 3, gated, not gated)
+    full = oracle.mlp_shard_backward(X, W1, W2, dZ, 0, 1, act, b1=b1, Wu=Wu)
+    p, s = 4, 8
+    parts = []
+    for i in range(p):
+        o = oracle.mlp_shard_backward(X, W1, W2, dZ, i, p, act, b1=b1, Wu=Wu)
+        cols = slice(i * s, (i + 1) * s)
+        assert np.array_equal(o["dW1"], full["dW1"][:, cols])
+        assert np.array_equal(o["dW2"], full["dW2"][cols])
+        assert np.array_equal(o["dH"][:, :s], full["dH"][:, cols])
+        if gated:
+            assert np.array_equal(o["dWu"], full["dWu"][:, cols])
+            assert np.array_equal(o["dH"][:, s:], full["dH"][:, 32 + i * s:32 + (i + 1) * s])
+        else:
+            assert np.array_equal(o["db1"], full["db1"][cols])
+        parts.append(o["dXp"])
+    assert rel_fro(oracle.partial_sum(parts), full["dXp"]) < 1e-12
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "gelu_erf", "swiglu", "relu", "none"])
+def test_activation_derivatives(act):
+    """act' against central differences of the forward activation, and against
+    torch's fp64 autograd of its own GeLU / SiLU / ReLU."""
+    x = np.concatenate([np.linspace(-10, 10, 401), [-1e-3, 1e-3, 0.5, -0.5]])
+    if act == "relu":
+        x = x[np.abs(x) > 1e-2]
+    h = 1e-6
+    num = (oracle.activation(act, x + h) - oracle.activation(act, x - h)) / (2 * h)
+    ana = oracle.dactivation(act, x)
+    assert np.max(np.abs(num - ana)) < 1e-8
+    tx = torch.tensor(x, requires_grad=True)
+    F = torch.nn.functional
+    f = {"gelu_tanh": lambda v: F.gelu(v, approximate="tanh"), "gelu_erf": F.gelu,
+         "swiglu": F.silu, "relu": F.relu, "none": lambda v: v * 1.0}[act]
+    f(tx).sum().backward()
+    assert np.max(np.abs(tx.grad.numpy() - ana)) < 1e-14
+    if act == "relu":
+        assert oracle.dactivation("relu", np.array([0.0]))[0] == 0.0
