@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 2
+#define TPMLP_ABI_VERSION 3
 #define TP_MAX_SHARDS 64
 
 typedef enum {
@@ -182,12 +182,74 @@ tp_status tp_mlp_simulated(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_
 /*
  * Bytes of workspace that tp_col_linear / tp_row_linear / tp_mlp_shard /
  * tp_mlp_simulated need for these sizes (0 if none).  The workspace holds
- * the split-K partial sums and arrival counters of the few-token (T <= 64)
- * path.  It must be zero-filled before its first use; every call leaves its
- * counters zero again, so one zeroed buffer can be reused by any later call on
- * the same stream.  Returns 0 for invalid arguments.
+ * the arrival counters (the first 256 KiB) and split-K partial sums (after
+ * them) of the few-token (T <= 64) path.  It must be zero-filled before its
+ * first use; every call leaves its counters zero again, and no entry point
+ * writes anything but zeros to the counter area, so one zeroed buffer can be
+ * reused by any later call of any entry point on the same stream.  Returns 0
+ * for invalid arguments.
  */
 size_t tp_workspace_bytes(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t p);
+
+/*
+ * Training forward of the column step: tp_col_linear, and in the same launch
+ * the pre-activation the backward pass needs,
+ *   H[t, j] = sum_c X[t,c] * W1[c, c0+j] + b1[c0+j]                  [T, s]
+ * or, for TP_ACT_SWIGLU, H = [G | U] with G = X Wg_i in columns [0, s) and
+ * U = X Wu_i in columns [s, 2s)                                      [T, 2s]
+ * rounded once to dt like Y.  Always runs the tiled (bf16) or fp32 kernels,
+ * whatever T; needs no workspace.
+ *   H [T, s] (SwiGLU [T, 2s]), ldh   output, dtype dt, overwritten
+ */
+tp_status tp_col_linear_train(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t i,
+                              int32_t p, const void *X, int64_t ldx, const void *W1, int64_t ldw1,
+                              const void *Wu, int64_t ldwu, const void *b1, void *Y, int64_t ldy,
+                              void *H, int64_t ldh, void *stream);
+
+/*
+ * Backward pass of shard i of p, given the gradient dZ of the loss with
+ * respect to the reduced output Z = sum_i Z_i.  The reduction's backward is
+ * the identity, so every shard receives the same dZ; the row-parallel step's
+ * input gradient is local; the column-parallel step's input gradient is one
+ * term of a sum over the shards, dX = sum_i dH_i W1_i^T, the all-reduce before
+ * the block ("Transformer math: tensor parallel", sections "Column-parallel:
+ * split the weight by output columns", "Row-parallel: split the weight by
+ * input rows" and "The f and g conjugate operators").  With s = k/p, c0 = i*s:
+ *   dY  = dZ W2[c0:c0+s, :]^T                        (not stored)
+ *   dH  = dY * act'(H)                               [T, s]   dtype dt
+ *         SwiGLU: [dG | dU], dG = dY * U * SiLU'(G), dU = dY * SiLU(G)   [T, 2s]
+ *   dXp = dH W1[:, c0:c0+s]^T (+ dU Wu[:, c0:c0+s]^T)    [T, d]  fp32, this
+ *         shard's term of dX (sum the p terms with tp_partial_sum)
+ *   dW1 = X^T dH (SwiGLU: X^T dG)                    [d, s]   fp32
+ *   dWu = X^T dU (SwiGLU only, else NULL)            [d, s]   fp32
+ *   db1 = sum over t of dH[t, :]                     [s]      fp32, or NULL
+ *         (must be NULL with SwiGLU; needs tp_backward_workspace_bytes)
+ *   dW2 = Y^T dZ                                     [s, d]   fp32
+ * Inputs (dtype dt): X [T,d]; the full W1, Wu [d,k] and W2 [k,d] as in the
+ * forward; H and Y as written by tp_col_linear_train; dZ [T,d].  The
+ * activation derivatives are those of the forward's definitions (ReLU'(0) =
+ * 0).  Weight-gradient outputs are compact [d, s] / [s, d] matrices,
+ * overwritten (not accumulated).  With T = 0 the weight and bias gradients
+ * are set to zero and nothing else is touched.  Always runs the tiled (bf16)
+ * or fp32 kernels; the operands W2_i^T, W1_i^T, X^T and Y^T are read in place
+ * (no transposed copies).
+ */
+tp_status tp_mlp_shard_backward(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t i,
+                                int32_t p, const void *X, int64_t ldx, const void *W1, int64_t ldw1,
+                                const void *Wu, int64_t ldwu, const void *W2, int64_t ldw2,
+                                const void *H, int64_t ldh, const void *Y, int64_t ldy,
+                                const void *dZ, int64_t lddz, void *dH, int64_t lddh, float *dXp,
+                                int64_t lddx, float *dW1, int64_t lddw1, float *dWu, int64_t lddwu,
+                                float *db1, float *dW2, int64_t lddw2, void *ws, size_t ws_bytes,
+                                void *stream);
+
+/* Bytes of workspace tp_mlp_shard_backward needs (0 if none): the bias
+ * gradient's column sums when with_db1 is non-zero.  The layout is the one
+ * tp_workspace_bytes describes (a counter area, then scratch), so one
+ * zero-filled buffer of the largest size any call needs serves every entry
+ * point on a stream.  Returns 0 for invalid arguments. */
+size_t tp_backward_workspace_bytes(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k,
+                                   int32_t p, int32_t with_db1);
 
 /*
  * Attention projections of head shard i of p.

@@ -71,8 +71,16 @@ def library():
                                   vp, i64, vp, sz, vp]
     lib.tp_qkv_workspace_bytes.argtypes = [ci, i64, i64, i32, i32, i64, i32]
     lib.tp_qkv_workspace_bytes.restype = sz
+    lib.tp_col_linear_train.argtypes = [ci, ci, i64, i64, i64, i32, i32, vp, i64, vp, i64, vp,
+                                        i64, vp, vp, i64, vp, i64, vp]
+    lib.tp_mlp_shard_backward.argtypes = [ci, ci, i64, i64, i64, i32, i32, vp, i64, vp, i64, vp,
+                                          i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp,
+                                          i64, vp, i64, vp, i64, vp, vp, i64, vp, sz, vp]
+    lib.tp_backward_workspace_bytes.argtypes = [ci, ci, i64, i64, i64, i32, i32]
+    lib.tp_backward_workspace_bytes.restype = sz
     for name in ("tp_col_linear", "tp_row_linear", "tp_mlp_shard", "tp_partial_sum",
-                 "tp_mlp_simulated", "tp_shard_bounds", "tp_calib_mfma_bf16", "tp_qkv_linear"):
+                 "tp_mlp_simulated", "tp_shard_bounds", "tp_calib_mfma_bf16", "tp_qkv_linear",
+                 "tp_col_linear_train", "tp_mlp_shard_backward"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -289,3 +297,63 @@ def tp_qkv_linear(X, Wqkv, Hq: int, Hkv: int, dh: int, i: int, p: int, QKV, bqkv
     _check(library().tp_qkv_linear(_dt(X), T, d, Hq, Hkv, dh, i, p, _ptr(X), ldx, _ptr(Wqkv), ldw,
                                    _ptr(bqkv), _ptr(QKV), ldo, wsp, wsn, _stream(stream)))
     return QKV
+
+
+def tp_col_linear_train(X, W1, i: int, p: int, Y, H, act="gelu_tanh", Wu=None, b1=None,
+                        stream=None):
+    """tp_col_linear, also writing the pre-activation H [T, k/p] (SwiGLU: [G | U], [T, 2k/p])."""
+    T, d = X.shape
+    k = W1.shape[1]
+    s = k // p if p > 0 else 0
+    a = _act(act)
+    ldx = _ld(X, T, d, "X")
+    ldw1 = _ld(W1, d, k, "W1")
+    ldwu = _ld(Wu, d, k, "Wu") if Wu is not None else 0
+    ldy = _ld(Y, T, s, "Y")
+    ldh = _ld(H, T, 2 * s if a == ACT["swiglu"] else s, "H")
+    if b1 is not None and b1.numel() < k:
+        raise ValueError("b1 is shorter than k")
+    _check(library().tp_col_linear_train(_dt(X), a, T, d, k, i, p, _ptr(X), ldx, _ptr(W1), ldw1,
+                                         _ptr(Wu), ldwu, _ptr(b1), _ptr(Y), ldy, _ptr(H), ldh,
+                                         _stream(stream)))
+    return Y, H
+
+
+def tp_backward_workspace_bytes(dtype, act, T: int, d: int, k: int, p: int, with_db1: bool) -> int:
+    dt = DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return library().tp_backward_workspace_bytes(dt, _act(act), T, d, k, p, 1 if with_db1 else 0)
+
+
+def tp_mlp_shard_backward(X, W1, W2, H, Y, dZ, i: int, p: int, dH, dXp, dW1, dW2,
+                          act="gelu_tanh", Wu=None, dWu=None, db1=None, ws=None, stream=None):
+    """Backward pass of shard i: dH (dt), dXp [T, d], dW1 [d, k/p], dWu, db1 [k/p], dW2 [k/p, d]
+    (fp32), from X, the full weights, the saved H and Y, and dZ [T, d] (dt)."""
+    T, d = X.shape
+    k = W1.shape[1]
+    s = k // p if p > 0 else 0
+    a = _act(act)
+    hw = 2 * s if a == ACT["swiglu"] else s
+    ldx = _ld(X, T, d, "X")
+    ldw1 = _ld(W1, d, k, "W1")
+    ldwu = _ld(Wu, d, k, "Wu") if Wu is not None else 0
+    ldw2 = _ld(W2, k, d, "W2")
+    ldh = _ld(H, T, hw, "H")
+    ldy = _ld(Y, T, s, "Y")
+    lddz = _ld(dZ, T, d, "dZ")
+    lddh = _ld(dH, T, hw, "dH")
+    lddx = _ld(dXp, T, d, "dXp")
+    lddw1 = _ld(dW1, d, s, "dW1")
+    lddwu = _ld(dWu, d, s, "dWu") if dWu is not None else 0
+    lddw2 = _ld(dW2, s, d, "dW2")
+    for name, t in (("dXp", dXp), ("dW1", dW1), ("dW2", dW2), ("dWu", dWu), ("db1", db1)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    if db1 is not None and db1.numel() < s:
+        raise ValueError("db1 is shorter than k/p")
+    need = tp_backward_workspace_bytes(X.dtype, a, T, d, k, p, db1 is not None)
+    wsp, wsn = _ws_args(ws, need, X.device)
+    _check(library().tp_mlp_shard_backward(
+        _dt(X), a, T, d, k, i, p, _ptr(X), ldx, _ptr(W1), ldw1, _ptr(Wu), ldwu, _ptr(W2), ldw2,
+        _ptr(H), ldh, _ptr(Y), ldy, _ptr(dZ), lddz, _ptr(dH), lddh, _ptr(dXp), lddx, _ptr(dW1),
+        lddw1, _ptr(dWu), lddwu, _ptr(db1), _ptr(dW2), lddw2, wsp, wsn, _stream(stream)))
+    return dH, dXp, dW1, dW2

@@ -355,6 +355,172 @@ GemmArgs qkv_gemm(const QkvCall &c) {
   return a;
 }
 
+// The backward pass and the forward that keeps what it needs always run the
+// tiled kernels (bf16) or the fp32 kernels, whatever T: they need the
+// transposed-operand layouts and epilogues only those have.
+tp_status check_tiled(tp_dtype dt, const GemmArgs &a) {
+  if (dt != TP_BF16) return TP_OK;
+  if (!gemm_bf16_tiled_supported(a))
+    return fail(TP_ERR_BAD_SHAPE,
+                "shape beyond the bf16 kernels' offset range: leading dimensions must be below "
+                "2^21 elements (2^23 for weights), and a transposed weight block below 2^30");
+  return TP_OK;
+}
+
+tp_status run_tiled(tp_dtype dt, const GemmArgs &a, hipStream_t st) {
+  const hipError_t e = dt == TP_F32 ? launch_gemm_f32(a, st) : launch_gemm_bf16_tiled(a, st);
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return TP_OK;
+}
+
+struct BwdCall {
+  tp_dtype dt;
+  int act;
+  int64_t T, d, k;
+  int32_t i, p;
+  const void *X, *W1, *Wu, *W2, *H, *Y, *dZ;
+  int64_t ldx, ldw1, ldwu, ldw2, ldh, ldy, lddz;
+  void *dH;
+  int64_t lddh;
+  float *dXp, *dW1, *dWu, *db1, *dW2;
+  int64_t lddx, lddw1, lddwu, lddw2;
+};
+
+tp_status validate_bwd(const BwdCall &c) {
+  TRY(check_dtype_act(c.dt, c.act));
+  TRY(check_shard(c.T, c.d, c.k, c.i, c.p));
+  const int64_t s = c.k / c.p;
+  const bool gated = c.act == TP_ACT_SWIGLU;
+  const int64_t hw = gated ? 2 * s : s;
+  if (c.d % elem_align(c.dt) || s % elem_align(c.dt))
+    return fail(TP_ERR_MISALIGNED, "d = %lld and k/p = %lld must be multiples of %lld",
+                (long long)c.d, (long long)s, (long long)elem_align(c.dt));
+  if (c.T > 0) {  // token-sized buffers are never touched with no tokens
+    TRY(check_ptr("X", c.X));
+    TRY(check_ptr("H", c.H));
+    TRY(check_ptr("Y", c.Y));
+    TRY(check_ptr("dZ", c.dZ));
+    TRY(check_ptr("dH", c.dH));
+    TRY(check_ptr("dXp", c.dXp));
+  }
+  TRY(check_ptr("W1", c.W1));
+  TRY(check_ptr("W2", c.W2));
+  TRY(check_ptr("dW1", c.dW1));
+  TRY(check_ptr("dW2", c.dW2));
+  TRY(check_ld("ldx", c.ldx, c.d, c.dt));
+  TRY(check_ld("ldw1", c.ldw1, c.k, c.dt));
+  TRY(check_ld("ldw2", c.ldw2, c.d, c.dt));
+  TRY(check_ld("ldh", c.ldh, hw, c.dt));
+  TRY(check_ld("ldy", c.ldy, s, c.dt));
+  TRY(check_ld("lddz", c.lddz, c.d, c.dt));
+  TRY(check_ld("lddh", c.lddh, hw, c.dt));
+  TRY(check_ld("lddx", c.lddx, c.d, TP_F32));
+  TRY(check_ld("lddw1", c.lddw1, s, TP_F32));
+  TRY(check_ld("lddw2", c.lddw2, c.d, TP_F32));
+  if (gated) {
+    TRY(check_ptr("Wu", c.Wu));
+    TRY(check_ptr("dWu", c.dWu));
+    TRY(check_ld("ldwu", c.ldwu, c.k, c.dt));
+    TRY(check_ld("lddwu", c.lddwu, s, TP_F32));
+    if (c.db1) return fail(TP_ERR_BAD_ACT, "a column bias gradient is not defined with SWIGLU");
+  } else if (c.db1) {
+    TRY(check_ptr("db1", c.db1));
+  }
+  return TP_OK;
+}
+
+// The GEMMs of the backward pass of shard i ("Transformer math: tensor
+// parallel", sections "Column-parallel: split the weight by output columns",
+// "Row-parallel: split the weight by input rows" and "The f and g conjugate
+// operators": the row step's input gradient is local, dY_i = dZ W2_i^T; the
+// column step's is the shard's term of dX = sum_i dH_i W1_i^T).
+struct BwdGemms {
+  GemmArgs dh;        // dH = act'(H) * (dZ W2_i^T)            [T, s] (gated: [T, 2s])
+  GemmArgs dw2;       // dW2_i = Y_i^T dZ                      [s, d]
+  GemmArgs dx[2];     // dXp = dH W1_i^T (+ dU Wu_i^T)         [T, d]
+  GemmArgs dw1[2];    // dW1_i = X^T dH (dWu_i = X^T dU)       [d, s]
+  int n;              // 1, or 2 with SwiGLU
+};
+
+BwdGemms bwd_gemms(const BwdCall &c) {
+  const int64_t s = c.k / c.p, c0 = (int64_t)c.i * s;
+  const size_t es = elem_size(c.dt);
+  const bool gated = c.act == TP_ACT_SWIGLU;
+  BwdGemms b{};
+  b.n = gated ? 2 : 1;
+  GemmArgs &h = b.dh;
+  h.A = c.dZ;
+  h.lda = c.lddz;
+  h.B = (const char *)c.W2 + c0 * c.ldw2 * es;  // rows c0.. of W2 are the columns of W2_i^T
+  h.ldb = c.ldw2;
+  h.lay = LAY_NT;
+  h.C = c.dH;
+  h.ldc = c.lddh;
+  h.aux = c.H;
+  h.ldaux = c.ldh;
+  h.M = c.T;
+  h.N = s;
+  h.K = c.d;
+  h.epi = gated ? EPI_DSWIGLU : EPI_DACT;
+  h.act = gated ? TP_ACT_SWIGLU : c.act;
+  h.groups = 1;
+  GemmArgs &w2 = b.dw2;
+  w2.A = c.Y;  // held as Y_i [T, s] = (Y_i^T)^T
+  w2.lda = c.ldy;
+  w2.lay = LAY_TN;
+  w2.B = c.dZ;
+  w2.ldb = c.lddz;
+  w2.C = c.dW2;
+  w2.ldc = c.lddw2;
+  w2.M = s;
+  w2.N = c.d;
+  w2.K = c.T;
+  w2.epi = EPI_F32;
+  w2.act = TP_ACT_NONE;
+  w2.groups = 1;
+  for (int q = 0; q < b.n; ++q) {
+    const void *Wq = q == 0 ? c.W1 : c.Wu;
+    const int64_t ldwq = q == 0 ? c.ldw1 : c.ldwu;
+    const void *dHq = (const char *)c.dH + q * s * es;
+    GemmArgs &x = b.dx[q];
+    x.A = dHq;
+    x.lda = c.lddh;
+    x.B = (const char *)Wq + c0 * es;  // W_i^T: row n of W, columns c0..
+    x.ldb = ldwq;
+    x.lay = LAY_NT;
+    x.C = c.dXp;
+    x.ldc = c.lddx;
+    x.M = c.T;
+    x.N = c.d;
+    x.K = s;
+    x.epi = q == 0 ? EPI_F32 : EPI_F32_ACC;
+    x.act = TP_ACT_NONE;
+    x.groups = 1;
+    GemmArgs &w = b.dw1[q];
+    w.A = c.X;  // held as X [T, d] = (X^T)^T
+    w.lda = c.ldx;
+    w.lay = LAY_TN;
+    w.B = dHq;
+    w.ldb = c.lddh;
+    w.C = q == 0 ? c.dW1 : c.dWu;
+    w.ldc = q == 0 ? c.lddw1 : c.lddwu;
+    w.M = c.d;
+    w.N = s;
+    w.K = c.T;
+    w.epi = EPI_F32;
+    w.act = TP_ACT_NONE;
+    w.groups = 1;
+  }
+  return b;
+}
+
+// The bias gradient's column sums use the scratch part of the shared
+// workspace layout (after the counter area), so one workspace buffer can
+// serve the forward and backward entry points alike.
+size_t bwd_ws_bytes(const BwdCall &c) {
+  return c.db1 ? kWsCounterBytes + colsum_workspace_bytes(c.T, c.k / c.p) : 0;
+}
+
 QkvCall make_qkv(tp_dtype dt, int64_t T, int64_t d, int32_t Hq, int32_t Hkv, int64_t dh,
                  int32_t i, int32_t p, const void *X, int64_t ldx, const void *W, int64_t ldw,
                  const void *b, void *QKV, int64_t ldo) {
@@ -506,6 +672,99 @@ size_t tp_workspace_bytes(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t
                        (void *)dummy, s);
   RowCall r = make_row(dt, T, d, k, 0, p, dummy, s, dummy, d, (float *)dummy, d);
   return max_sz(gemm_ws_bytes(dt, col_gemm(c, 1, 0)), gemm_ws_bytes(dt, row_gemm(r, 1, 0, 0)));
+}
+
+tp_status tp_col_linear_train(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t i,
+                              int32_t p, const void *X, int64_t ldx, const void *W1, int64_t ldw1,
+                              const void *Wu, int64_t ldwu, const void *b1, void *Y, int64_t ldy,
+                              void *H, int64_t ldh, void *stream) {
+  const ColCall c = make_col(dt, act, T, d, k, i, p, X, ldx, W1, ldw1, Wu, ldwu, b1, Y, ldy);
+  TRY(validate_col(c));
+  const int64_t s = (k / p) * (act == TP_ACT_SWIGLU ? 2 : 1);
+  if (T > 0) TRY(check_ptr("H", H));
+  TRY(check_ld("ldh", ldh, s, dt));
+  if (T == 0) return ok();
+  GemmArgs a = col_gemm(c, 1, 0);
+  a.epi = act == TP_ACT_SWIGLU ? EPI_SWIGLU_SAVE : EPI_ACT_SAVE;
+  a.C2 = H;
+  a.ldc2 = ldh;
+  TRY(check_tiled(dt, a));
+  TRY(run_tiled(dt, a, (hipStream_t)stream));
+  return ok();
+}
+
+tp_status tp_mlp_shard_backward(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t i,
+                                int32_t p, const void *X, int64_t ldx, const void *W1, int64_t ldw1,
+                                const void *Wu, int64_t ldwu, const void *W2, int64_t ldw2,
+                                const void *H, int64_t ldh, const void *Y, int64_t ldy,
+                                const void *dZ, int64_t lddz, void *dH, int64_t lddh, float *dXp,
+                                int64_t lddx, float *dW1, int64_t lddw1, float *dWu, int64_t lddwu,
+                                float *db1, float *dW2, int64_t lddw2, void *ws, size_t ws_bytes,
+                                void *stream) {
+  BwdCall c;
+  c.dt = dt;
+  c.act = (int)act;
+  c.T = T;
+  c.d = d;
+  c.k = k;
+  c.i = i;
+  c.p = p;
+  c.X = X;
+  c.W1 = W1;
+  c.Wu = act == TP_ACT_SWIGLU ? Wu : nullptr;
+  c.W2 = W2;
+  c.H = H;
+  c.Y = Y;
+  c.dZ = dZ;
+  c.ldx = ldx;
+  c.ldw1 = ldw1;
+  c.ldwu = ldwu;
+  c.ldw2 = ldw2;
+  c.ldh = ldh;
+  c.ldy = ldy;
+  c.lddz = lddz;
+  c.dH = dH;
+  c.lddh = lddh;
+  c.dXp = dXp;
+  c.dW1 = dW1;
+  c.dWu = act == TP_ACT_SWIGLU ? dWu : nullptr;
+  c.db1 = db1;
+  c.dW2 = dW2;
+  c.lddx = lddx;
+  c.lddw1 = lddw1;
+  c.lddwu = lddwu;
+  c.lddw2 = lddw2;
+  TRY(validate_bwd(c));
+  const BwdGemms b = bwd_gemms(c);
+  TRY(check_tiled(dt, b.dh));
+  TRY(check_tiled(dt, b.dw2));
+  for (int q = 0; q < b.n; ++q) {
+    TRY(check_tiled(dt, b.dx[q]));
+    TRY(check_tiled(dt, b.dw1[q]));
+  }
+  TRY(check_ws(bwd_ws_bytes(c), ws, ws_bytes));
+  const hipStream_t st = (hipStream_t)stream;
+  // With no tokens the weight and bias gradients are zero: the weight-gradient
+  // GEMMs (K = T = 0) and the column sum write zeros; the others launch nothing.
+  TRY(run_tiled(dt, b.dh, st));
+  TRY(run_tiled(dt, b.dw2, st));
+  for (int q = 0; q < b.n; ++q) TRY(run_tiled(dt, b.dx[q], st));
+  for (int q = 0; q < b.n; ++q) TRY(run_tiled(dt, b.dw1[q], st));
+  if (db1) {
+    const hipError_t e = launch_colsum(dt == TP_BF16, dH, lddh, T, k / p,
+                                       (float *)((char *)ws + kWsCounterBytes), db1, st);
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+size_t tp_backward_workspace_bytes(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k,
+                                   int32_t p, int32_t with_db1) {
+  if (dt != TP_F32 && dt != TP_BF16) return 0;
+  if ((int)act < TP_ACT_NONE || (int)act > TP_ACT_SWIGLU) return 0;
+  if (T < 0 || d < 1 || k < 1 || p < 1 || p > TP_MAX_SHARDS || k % p) return 0;
+  if (!with_db1 || act == TP_ACT_SWIGLU) return 0;
+  return kWsCounterBytes + colsum_workspace_bytes(T, k / p);
 }
 
 tp_status tp_qkv_linear(tp_dtype dt, int64_t T, int64_t d, int32_t Hq, int32_t Hkv, int64_t dh,

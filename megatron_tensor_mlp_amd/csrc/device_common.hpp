@@ -37,6 +37,32 @@ __device__ __forceinline__ float activate(float x) {
 
 __device__ __forceinline__ float silu(float x) { return activate<ACT_SWIGLU>(x); }
 
+// Derivatives of the activations (for the backward pass), from the
+// definitions above by the chain rule:
+//   GeLU tanh form: with t = tanh(sqrt(2/pi) (x + 0.044715 x^3)),
+//                   0.5 (1 + t) + 0.5 x (1 - t^2) sqrt(2/pi) (1 + 3 * 0.044715 x^2)
+//   GeLU erf form:  0.5 (1 + erf(x / sqrt 2)) + x exp(-x^2 / 2) / sqrt(2 pi)
+//   SiLU:           s (1 + x (1 - s)), s = 1 / (1 + exp(-x))
+//   ReLU:           1 for x > 0, else 0
+template <int ACT>
+__device__ __forceinline__ float dactivate(float x) {
+  if constexpr (ACT == ACT_RELU) {
+    return x > 0.0f ? 1.0f : 0.0f;
+  } else if constexpr (ACT == ACT_GELU_TANH) {
+    const float c = 0.7978845608028654f;  // sqrt(2/pi)
+    const float t = tanhf(c * (x + 0.044715f * x * x * x));
+    return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * c * (1.0f + 0.134145f * x * x);
+  } else if constexpr (ACT == ACT_GELU_ERF) {
+    return 0.5f * (1.0f + erff(x * 0.7071067811865476f)) +
+           x * expf(-0.5f * x * x) * 0.3989422804014327f;  // 1/sqrt(2 pi)
+  } else if constexpr (ACT == ACT_SWIGLU) {  // SiLU'
+    const float s = 1.0f / (1.0f + expf(-x));
+    return s * (1.0f + x * (1.0f - s));
+  } else {
+    return 1.0f;
+  }
+}
+
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
 

@@ -56,10 +56,11 @@ constexpr int RP = RC * 2;      // bytes per weight row in LDS
 constexpr int TARGET_WGS = 256;
 constexpr int MIN_STAGES = 4;   // fewest k-steps a workgroup streams
 // The workspace starts with a counter area of fixed size, so that calls with
-// different plans reusing one workspace never take another call's partials
-// for counters: counters of any plan lie below CTR_AREA and partials above it.
-constexpr int64_t MAX_BLOCKS = 65536;             // column blocks per call
-constexpr size_t CTR_AREA = MAX_BLOCKS * sizeof(unsigned);
+// different plans (or other entry points) reusing one workspace never take
+// partials for counters: counters of any plan lie below CTR_AREA and partials
+// above it.
+constexpr int64_t MAX_BLOCKS = kWsMaxBlocks;  // column blocks per call
+constexpr size_t CTR_AREA = kWsCounterBytes;
 
 // Geometry of one configuration: a stage holds BK k rows of 128 columns and
 // the matching token rows.
@@ -450,7 +451,8 @@ bool gemm_bf16_decode_supported(const GemmArgs &a) {
   // Per-lane buffer offsets are 32-bit byte offsets from a stage's k base:
   // 64 weight rows and 64 token rows must stay below 2^31 bytes.  The column
   // blocks of one call must fit the counter area.
-  return a.M >= 1 && a.M <= 64 && a.lda < (int64_t(1) << 23) && a.ldb < (int64_t(1) << 23) &&
+  return a.lay == LAY_NN && (a.epi == EPI_ACT || a.epi == EPI_SWIGLU || a.epi == EPI_F32) &&
+         a.M >= 1 && a.M <= 64 && a.lda < (int64_t(1) << 23) && a.ldb < (int64_t(1) << 23) &&
          (a.epi != EPI_SWIGLU || a.ldb2 < (int64_t(1) << 23)) && (a.N + RC - 1) / RC <= MAX_BLOCKS;
 }
 

@@ -8,9 +8,24 @@ namespace tpmlp {
 
 // What a GEMM does with its fp32 accumulator tile.
 enum Epilogue : int {
-  EPI_ACT = 0,     // C = act(acc + bias) in the element type  (column step, GeLU/ReLU/none)
-  EPI_SWIGLU = 1,  // C = SiLU(acc_gate) * acc_up              (column step, SwiGLU)
+  EPI_ACT = 0,          // C = act(acc + bias) in the element type  (column step, GeLU/ReLU/none)
+  EPI_SWIGLU = 1,       // C = SiLU(acc_gate) * acc_up              (column step, SwiGLU)
   EPI_F32 = 2,          // C = acc, fp32                           (row step partial)
+  EPI_F32_ACC = 3,      // C = C + acc, fp32                       (second term of a gradient)
+  EPI_ACT_SAVE = 4,     // EPI_ACT, and C2 = acc + bias            (pre-activation kept for
+                        //                                          the backward pass)
+  EPI_SWIGLU_SAVE = 5,  // EPI_SWIGLU, and C2 = [gate | up]        (columns [0,N) and [N,2N))
+  EPI_DACT = 6,         // C = acc * act'(aux)                     (hidden gradient)
+  EPI_DSWIGLU = 7,      // C = [acc * up * SiLU'(gate) | acc * SiLU(gate)], aux = [gate | up]
+};
+
+// Operand layouts.  A GEMM multiplies A [M,K] by B [K,N]; either operand may
+// be stored as its transpose (the backward pass multiplies by transposed
+// weights and activations without copying them).
+enum Layout : int {
+  LAY_NN = 0,  // A row-major [M,K] (k contiguous), B row-major [K,N] (n contiguous)
+  LAY_NT = 1,  // B stored as B^T [N,K] (k contiguous; ldb between its rows)
+  LAY_TN = 2,  // A stored as A^T [K,M] (m contiguous; lda between its rows)
 };
 
 // Column map: output column c of a GEMM reads weight (and bias) column
@@ -38,6 +53,11 @@ struct GemmArgs {
   int64_t sA, sB, sB2, sBias, sC;
   int nseg;  // column map (EPI_ACT only; 0 = identity)
   int64_t seg_start[kMaxSegs], seg_src[kMaxSegs];
+  int lay;          // Layout (LAY_NN unless set)
+  void *C2;         // second output (EPI_ACT_SAVE, EPI_SWIGLU_SAVE), element type
+  int64_t ldc2;
+  const void *aux;  // saved pre-activation (EPI_DACT, EPI_DSWIGLU), element type
+  int64_t ldaux;
 };
 
 // Weight / bias column read for output column c.
@@ -48,12 +68,20 @@ __host__ __device__ inline int64_t src_col(const GemmArgs &p, int64_t c) {
   return c + base;
 }
 
-// Large-T path: MFMA tiles staged through LDS.  _supported: the shape fits the
-// kernels' 32-bit buffer offsets.
+// Large-T path: MFMA tiles staged through LDS (every epilogue and layout).
+// _supported: the shape fits the kernels' 32-bit buffer offsets.
 bool gemm_bf16_tiled_supported(const GemmArgs &a);
 hipError_t launch_gemm_bf16_tiled(const GemmArgs &a, hipStream_t s);
 
-// Few-token path (M <= 64): weight-streaming split-K GEMM.  `ws` must hold
+// Every entry point that takes a workspace lays it out the same way, so that
+// one buffer can serve them all: a counter area of kWsCounterBytes (arrival
+// counters of the few-token path, zero between calls) and scratch after it
+// (overwritten before it is read, never assumed zero).
+constexpr int64_t kWsMaxBlocks = 65536;  // few-token column blocks per call
+constexpr size_t kWsCounterBytes = kWsMaxBlocks * sizeof(unsigned);
+
+// Few-token path (M <= 64): weight-streaming split-K GEMM (LAY_NN; EPI_ACT,
+// EPI_SWIGLU and EPI_F32).  `ws` must hold
 // decode_workspace_bytes(a) zero-initialised bytes (or 0 bytes if that is 0).
 // _supported: 1 <= M <= 64 and the shape fits the kernels' 32-bit buffer
 // offsets and the workspace's counter area.
@@ -67,6 +95,12 @@ hipError_t launch_calib_mfma(int gaussian, int64_t iters, uint64_t *stats, int n
 
 // fp32 path (correctness-first): one output per thread, k ascending.
 hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s);
+
+// out[j] = sum over rows t of H[t, j] (fp32), rows ascending within chunks of
+// 64, chunks ascending; ws holds colsum_workspace_bytes(T, n) bytes of scratch.
+size_t colsum_workspace_bytes(int64_t T, int64_t n);
+hipError_t launch_colsum(bool bf16_in, const void *H, int64_t ldh, int64_t T, int64_t n, float *ws,
+                         float *out, hipStream_t s);
 
 // Z = ((P0 + P1) + ...) + P_{p-1} (+ b2), fp32.
 constexpr int kMaxParts = 64;

@@ -287,3 +287,64 @@ def test_qkv_workspace_bytes():
     assert tp.tp_qkv_workspace_bytes(bf16, 8, 8192, 64, 8, 120, 8) > 0     # dh = 120 is aligned
     assert tp.tp_qkv_workspace_bytes(bf16, 8, 8192, 64, 8, 100, 8) == 0    # dh = 100 misaligned
     assert lib.tp_last_error_message().decode() == msg
+
+
+# --- training forward and backward --------------------------------------------
+def train(dt=1, act=2, T=4, d=64, k=128, i=0, p=2, X=A, ldx=64, W1=A, ldw1=128, Wu=None, ldwu=0,
+          b1=None, Y=A, ldy=64, H=A, ldh=64):
+    return tp.library().tp_col_linear_train(dt, act, T, d, k, i, p, P(X), ldx, P(W1), ldw1, P(Wu),
+                                            ldwu, P(b1), P(Y), ldy, P(H), ldh, None)
+
+
+def bwd(dt=1, act=2, T=4, d=64, k=128, i=0, p=2, X=A, ldx=64, W1=A, ldw1=128, Wu=None, ldwu=0,
+        W2=A, ldw2=64, H=A, ldh=64, Y=A, ldy=64, dZ=A, lddz=64, dH=A, lddh=64, dXp=A, lddx=64,
+        dW1=A, lddw1=64, dWu=None, lddwu=0, db1=None, dW2=A, lddw2=64, ws=None, wsb=0):
+    return tp.library().tp_mlp_shard_backward(
+        dt, act, T, d, k, i, p, P(X), ldx, P(W1), ldw1, P(Wu), ldwu, P(W2), ldw2, P(H), ldh, P(Y),
+        ldy, P(dZ), lddz, P(dH), lddh, P(dXp), lddx, P(dW1), lddw1, P(dWu), lddwu, P(db1), P(dW2),
+        lddw2, P(ws), wsb, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(H=None), "TP_ERR_NULL_POINTER"),
+    (dict(ldh=60), "TP_ERR_BAD_SHAPE"),
+    (dict(act=4, Wu=A, ldwu=128), "TP_ERR_BAD_SHAPE"),     # SwiGLU keeps [G | U]: ldh >= 2 k/p
+    (dict(k=129, ldw1=136), "TP_ERR_NOT_DIVISIBLE"),
+    (dict(H=MIS), "TP_ERR_MISALIGNED"),
+])
+def test_col_linear_train_rejects(kw, expect):
+    assert status_name(train(**kw)) == expect
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(k=129, ldw1=136), "TP_ERR_NOT_DIVISIBLE"),
+    (dict(i=2), "TP_ERR_BAD_SHARD"),
+    (dict(dZ=None), "TP_ERR_NULL_POINTER"),
+    (dict(dW1=None), "TP_ERR_NULL_POINTER"),
+    (dict(dW2=None), "TP_ERR_NULL_POINTER"),
+    (dict(act=4, Wu=A, ldwu=128, ldh=128, lddh=128), "TP_ERR_NULL_POINTER"),   # no dWu
+    (dict(act=4, Wu=A, ldwu=128, dWu=A, lddwu=64), "TP_ERR_BAD_SHAPE"),        # dH narrower than 2s
+    (dict(act=4, Wu=A, ldwu=128, dWu=A, lddwu=64, ldh=128, lddh=128, db1=A),
+     "TP_ERR_BAD_ACT"),                                                         # no db1 with SwiGLU
+    (dict(lddw2=60), "TP_ERR_BAD_SHAPE"),
+    (dict(lddw1=60), "TP_ERR_BAD_SHAPE"),
+    (dict(lddx=60), "TP_ERR_BAD_SHAPE"),
+    (dict(ldw2=60), "TP_ERR_BAD_SHAPE"),
+    (dict(dXp=MIS), "TP_ERR_MISALIGNED"),
+    (dict(db1=A), "TP_ERR_WORKSPACE"),                     # the bias gradient needs a workspace
+    (dict(dt=3), "TP_ERR_BAD_DTYPE"),
+])
+def test_backward_rejects(kw, expect):
+    assert status_name(bwd(**kw)) == expect
+    assert tp.library().tp_last_error_message().decode() != ""
+
+
+def test_backward_workspace_bytes():
+    bf16 = torch.bfloat16
+    assert tp.tp_backward_workspace_bytes(bf16, "gelu_tanh", 4096, 8192, 28672, 8, True) \
+        == (256 << 10) + 64 * 3584 * 4
+    assert tp.tp_backward_workspace_bytes(bf16, "gelu_tanh", 4096, 8192, 28672, 8, False) == 0
+    assert tp.tp_backward_workspace_bytes(bf16, "swiglu", 4096, 8192, 28672, 8, True) == 0
+    assert tp.tp_backward_workspace_bytes(bf16, "gelu_tanh", 4096, 8192, 28672, 5, True) == 0
