@@ -13,8 +13,9 @@ only at the ends of a batch of launches).
 Prints ONE JSON line.  `value` is the step's algorithmic TFLOP/s (2*T*d*(k/p)
 flops per GEMM, three GEMMs).  Secondary fields report the few-token (decode)
 shard in GB/s of weights streamed, the on-device partial sum in GB/s, the
-simulated TP = 8 block, the GPT-style GeLU shard and the attention projections
-of one head shard (QKV and output projection).  `roofline` covers the
+simulated TP = 8 block, the GPT-style GeLU shard, the attention projections
+of one head shard (QKV and output projection) and the shard's training step
+(forward that keeps the pre-activation, and the backward pass).  `roofline` covers the
 dominant kernel (the SwiGLU column GEMM), `cpu_baseline` the CPU oracle timed
 on a bounded row sample of the same workload.
 """
@@ -361,6 +362,47 @@ def attention_bench(torch, tp, synth, steps, warmup, rotate_bytes=600 << 20):
     return out
 
 
+def backward_bench(torch, tp, synth, steps, warmup):
+    """Training step of the Llama-70B SwiGLU shard at TP = 8, T = 4096: the
+    training forward of the column step (Y and the kept [G | U]), the row step,
+    and the shard backward (dH = dY * SwiGLU', the dX term, dWg, dWu, dW2) from
+    a seeded dZ.  Algorithmic flops: 3 GEMMs forward, 6 backward, 2 T d (k/p)
+    each.  HIP-graph replay after the clock ramp."""
+    W = synth.WORKLOADS["llama70b_prefill_tp8"]
+    dev = "cuda:0"
+    T, d, s = W.T, W.d, W.s
+    Wg, Wu, W2 = (t.to(dev) for t in synth.llama_shard_weights(d, s))
+    X = synth.llama_tokens(T, d).to(dev)
+    dZ = synth.gaussian_bf16((T, d), 46).to(dev)
+    Y = torch.empty(T, s, dtype=torch.bfloat16, device=dev)
+    H = torch.empty(T, 2 * s, dtype=torch.bfloat16, device=dev)
+    Z = torch.empty(T, d, device=dev)
+    dH = torch.empty(T, 2 * s, dtype=torch.bfloat16, device=dev)
+    dXp = torch.empty(T, d, device=dev)
+    dWg = torch.empty(d, s, device=dev)
+    dWu = torch.empty(d, s, device=dev)
+    dW2 = torch.empty(s, d, device=dev)
+    fwd = [lambda: tp.tp_col_linear_train(X, Wg, 0, 1, Y, H, act="swiglu", Wu=Wu),
+           lambda: tp.tp_row_linear(Y, W2, 0, 1, Z)]
+    bwd = lambda: tp.tp_mlp_shard_backward(X, Wg, W2, H, Y, dZ, 0, 1, dH, dXp, dWg, dW2,  # noqa
+                                           act="swiglu", Wu=Wu, dWu=dWu)
+    ramp(torch, fwd + [bwd])
+    tb = time_graph(torch, [bwd], max(5, steps), warmup, per_replay=2)
+    sb = LAST_SPREAD
+    tf = time_graph(torch, fwd, max(5, steps), warmup, per_replay=2)
+    tt = time_graph(torch, fwd + [bwd], max(5, steps), warmup, per_replay=2)
+    st = LAST_SPREAD
+    unit = 2.0 * T * d * s
+    return {"workload": W.name, "T": T,
+            "backward_us": round(tb * 1e6, 1), "backward_TFLOPs": round(6 * unit / tb / 1e12, 1),
+            "backward_frac_mfma": round(6 * unit / tb / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "backward_spread": sb,
+            "train_forward_us": round(tf * 1e6, 1),
+            "train_forward_TFLOPs": round(3 * unit / tf / 1e12, 1),
+            "train_step_us": round(tt * 1e6, 1), "train_step_TFLOPs": round(9 * unit / tt / 1e12, 1),
+            "train_step_spread": st, "flops_backward": 6 * unit, "timing": "HIP graph replay"}
+
+
 def mfma_calibration(torch, tp, iters=20000, nwg=1024):
     """Sustained dense bf16 MFMA rate and the shader clock it runs at, for zero
     operands and for operands with the workloads' value mix (A ~ N(0,1),
@@ -438,7 +480,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline only")
     ap.add_argument("--sections",
-                    default="decode,partial_sum,simulated_block,gpt,attention,calibration",
+                    default="decode,partial_sum,simulated_block,gpt,attention,backward,calibration",
                     help="comma list of the secondary sections to run (without --quick)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 256 MiB device copy (the reference for HBM byte counters)")
@@ -506,6 +548,9 @@ def main():
         log("bench: attention projections")
         result["attention_projections"] = attention_bench(torch, tp, synth,
                                                           max(5, args.steps // 2), 3)
+    if "backward" in sections:
+        log("bench: training step (backward)")
+        result["training_step"] = backward_bench(torch, tp, synth, max(5, args.steps // 4), 2)
     if "calibration" in sections:
         log("bench: mfma calibration")
         result["mfma_calibration"] = mfma_calibration(torch, tp)

@@ -439,7 +439,9 @@ struct BwdGemms {
   GemmArgs dw2;       // dW2_i = Y_i^T dZ                      [s, d]
   GemmArgs dx[2];     // dXp = dH W1_i^T (+ dU Wu_i^T)         [T, d]
   GemmArgs dw1[2];    // dW1_i = X^T dH (dWu_i = X^T dU)       [d, s]
-  int n;              // 1, or 2 with SwiGLU
+  int n;              // weight-gradient GEMMs: 1, or 2 with SwiGLU
+  int ndx;            // dX GEMMs: 1, or 2 with SwiGLU when the two terms cannot
+                      // share one GEMM
 };
 
 BwdGemms bwd_gemms(const BwdCall &c) {
@@ -478,24 +480,37 @@ BwdGemms bwd_gemms(const BwdCall &c) {
   w2.epi = EPI_F32;
   w2.act = TP_ACT_NONE;
   w2.groups = 1;
+  // With SwiGLU, dXp = dG Wg_i^T + dU Wu_i^T is one GEMM over K = 2s when the
+  // two weights share a leading dimension and s is a whole number of k-steps:
+  // dH = [dG | dU] is then A, and B^T's rows run through Wg_i then Wu_i.
+  const bool fuse = gated && s % 32 == 0 && c.ldw1 == c.ldwu;
+  b.ndx = gated && !fuse ? 2 : 1;
   for (int q = 0; q < b.n; ++q) {
     const void *Wq = q == 0 ? c.W1 : c.Wu;
     const int64_t ldwq = q == 0 ? c.ldw1 : c.ldwu;
     const void *dHq = (const char *)c.dH + q * s * es;
-    GemmArgs &x = b.dx[q];
-    x.A = dHq;
-    x.lda = c.lddh;
-    x.B = (const char *)Wq + c0 * es;  // W_i^T: row n of W, columns c0..
-    x.ldb = ldwq;
-    x.lay = LAY_NT;
-    x.C = c.dXp;
-    x.ldc = c.lddx;
-    x.M = c.T;
-    x.N = c.d;
-    x.K = s;
-    x.epi = q == 0 ? EPI_F32 : EPI_F32_ACC;
-    x.act = TP_ACT_NONE;
-    x.groups = 1;
+    if (q < b.ndx) {
+      GemmArgs &x = b.dx[q];
+      x.A = dHq;
+      x.lda = c.lddh;
+      x.B = (const char *)Wq + c0 * es;  // W_i^T: row n of W, columns c0..
+      x.ldb = ldwq;
+      x.lay = LAY_NT;
+      x.C = c.dXp;
+      x.ldc = c.lddx;
+      x.M = c.T;
+      x.N = c.d;
+      x.K = s;
+      x.epi = q == 0 ? EPI_F32 : EPI_F32_ACC;
+      x.act = TP_ACT_NONE;
+      x.groups = 1;
+      if (fuse) {
+        x.B2 = (const char *)c.Wu + c0 * es;
+        x.ldb2 = c.ldwu;
+        x.K = 2 * s;
+        x.ksplit = s;
+      }
+    }
     GemmArgs &w = b.dw1[q];
     w.A = c.X;  // held as X [T, d] = (X^T)^T
     w.lda = c.ldx;
@@ -738,17 +753,15 @@ tp_status tp_mlp_shard_backward(tp_dtype dt, tp_act act, int64_t T, int64_t d, i
   const BwdGemms b = bwd_gemms(c);
   TRY(check_tiled(dt, b.dh));
   TRY(check_tiled(dt, b.dw2));
-  for (int q = 0; q < b.n; ++q) {
-    TRY(check_tiled(dt, b.dx[q]));
-    TRY(check_tiled(dt, b.dw1[q]));
-  }
+  for (int q = 0; q < b.ndx; ++q) TRY(check_tiled(dt, b.dx[q]));
+  for (int q = 0; q < b.n; ++q) TRY(check_tiled(dt, b.dw1[q]));
   TRY(check_ws(bwd_ws_bytes(c), ws, ws_bytes));
   const hipStream_t st = (hipStream_t)stream;
   // With no tokens the weight and bias gradients are zero: the weight-gradient
   // GEMMs (K = T = 0) and the column sum write zeros; the others launch nothing.
   TRY(run_tiled(dt, b.dh, st));
   TRY(run_tiled(dt, b.dw2, st));
-  for (int q = 0; q < b.n; ++q) TRY(run_tiled(dt, b.dx[q], st));
+  for (int q = 0; q < b.ndx; ++q) TRY(run_tiled(dt, b.dx[q], st));
   for (int q = 0; q < b.n; ++q) TRY(run_tiled(dt, b.dw1[q], st));
   if (db1) {
     const hipError_t e = launch_colsum(dt == TP_BF16, dH, lddh, T, k / p,

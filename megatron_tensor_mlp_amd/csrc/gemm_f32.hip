@@ -37,7 +37,11 @@ __global__ __launch_bounds__(TS *TS) void gemm_f32_kernel(const GemmArgs p) {
     }
     if constexpr (LAY == LAY_NT) {
       const int64_t bc = (int64_t)blockIdx.x * TS + ty, bk = k0 + tx;  // coalesced along k
-      Bs[tx][ty] = (bc < p.N && bk < p.K) ? B[src_col(p, bc) * p.ldb + bk] : 0.0f;
+      // k past ksplit comes from the second matrix (same leading dimension)
+      const bool second = p.ksplit > 0 && bk >= p.ksplit;
+      const float *Bk = second ? (const float *)p.B2 : B;
+      const int64_t kq = second ? bk - p.ksplit : bk;
+      Bs[tx][ty] = (bc < p.N && bk < p.K) ? Bk[src_col(p, bc) * p.ldb + kq] : 0.0f;
     } else {
       Bs[ty][tx] = (col < p.N && kb < p.K) ? B[kb * p.ldb + src_col(p, col)] : 0.0f;
     }

@@ -215,8 +215,9 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
     c.live = dkt < KT;
     c.k0 = (int64_t)(c.live ? dkt : 0) * BK;
     c.ra = rsrc(TA ? A + c.k0 * p.lda : A + c.k0);
-    if constexpr (TB)
-      c.rb = rsrc((b_up ? B2 : B) + c.k0);
+    if constexpr (TB)  // k past ksplit comes from the second matrix (same ld)
+      c.rb = rsrc(p.ksplit > 0 && c.k0 >= p.ksplit ? (const bf16 *)p.B2 + (c.k0 - p.ksplit)
+                                                    : (b_up ? B2 : B) + c.k0);
     else
       c.rb = rsrc(b_up ? B2 + c.k0 * p.ldb2 : B + c.k0 * p.ldb);
     return c;
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
   // 32x32 accumulator layout: lane holds column (lane & 31) and rows
   // 8 (v / 4) + 4 (lane / 32) + (v % 4), v = 0..15.
   const int64_t rbase = m0 + 128 * wm + 4 * (lane >> 5);
-  if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ACC) {
+  if constexpr (EPI == EPI_F32) {
     float *C = (float *)p.C + g * p.sC;
 #pragma unroll
     for (int f = 0; f < NB; ++f) {
@@ -415,13 +416,33 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
-          if (row < M) {
-            if constexpr (EPI == EPI_F32_ACC)
-              C[row * p.ldc + col] += acc[i][f][v];
-            else
-              C[row * p.ldc + col] = acc[i][f][v];
-          }
+          if (row < M) C[row * p.ldc + col] = acc[i][f][v];
         }
+    }
+  } else if constexpr (EPI == EPI_F32_ACC) {
+    // All 16 loads of a 32-row block are issued before the first add (rows
+    // past M load row M-1 and store nothing), so the block costs one memory
+    // round trip instead of sixteen.
+    float *C = (float *)p.C + g * p.sC;
+#pragma unroll
+    for (int f = 0; f < NB; ++f) {
+      const int64_t col = n0 + WN * wn + 32 * f + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float old[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+          old[v] = C[(row < M ? row : M - 1) * p.ldc + col];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+          if (row < M) C[row * p.ldc + col] = old[v] + acc[i][f][v];
+        }
+      }
     }
   } else if constexpr (DUAL) {
     bf16 *C = (bf16 *)p.C + g * p.sC;
@@ -455,22 +476,33 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
       const int64_t col = n0 + WN * wn + 32 * f + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        // The kept values of a 32-row block are all loaded before the first
+        // use (rows past M load row M-1 and store nothing).
+        constexpr int NH = EPI == EPI_DSWIGLU ? 2 : 1;
+        float hv[NH][16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+          const int64_t r = row < M ? row : M - 1;
+#pragma unroll
+          for (int q = 0; q < NH; ++q) hv[q][v] = (float)H[r * p.ldaux + q * N + col];
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
           if (row >= M) continue;
           const float dy = acc[i][f][v];
           if constexpr (EPI == EPI_DACT) {
-            const float h = (float)H[row * p.ldaux + col];
-            C[row * p.ldc + col] = to_bf16(dy * dactivate<ACT>(h));
+            C[row * p.ldc + col] = to_bf16(dy * dactivate<ACT>(hv[0][v]));
           } else {
-            const float gv = (float)H[row * p.ldaux + col];
-            const float uv = (float)H[row * p.ldaux + N + col];
+            const float gv = hv[0][v], uv = hv[NH - 1][v];
             C[row * p.ldc + col] = to_bf16(dy * uv * dactivate<ACT_SWIGLU>(gv));
             C[row * p.ldc + N + col] = to_bf16(dy * silu(gv));
           }
         }
+      }
     }
   } else {
     bf16 *C = (bf16 *)p.C + g * p.sC;
@@ -573,6 +605,8 @@ bool gemm_bf16_tiled_supported(const GemmArgs &a) {
   // below 2^31 bytes; with B^T, every row of B^T the tile can reach (N of
   // them, no column map); with A^T, 64 k rows of it.
   const int64_t one = 1;
+  if (a.ksplit != 0 && (a.lay != LAY_NT || a.ksplit % 32 != 0 || a.ksplit < 0 || a.ksplit >= a.K))
+    return false;
   switch (a.lay) {
     case LAY_NN:
       return a.lda < (one << 21) && a.ldb < (one << 23) &&

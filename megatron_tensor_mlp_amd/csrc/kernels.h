@@ -58,6 +58,11 @@ struct GemmArgs {
   int64_t ldc2;
   const void *aux;  // saved pre-activation (EPI_DACT, EPI_DSWIGLU), element type
   int64_t ldaux;
+  // LAY_NT only: B^T rows are the concatenation along k of B^T [N, ksplit]
+  // and B2^T [N, K - ksplit] (both with leading dimension ldb), so that
+  // A [M, K] times them sums two products in one GEMM; 0 = off.  ksplit is a
+  // multiple of 32 (a k-step never straddles the two).
+  int64_t ksplit;
 };
 
 // Weight / bias column read for output column c.

@@ -73,6 +73,7 @@ CASES = [
     (65, 1032, 2048, 8, "swiglu", False),
     (17, 264, 1024, 4, "gelu_tanh", True),
     (1, 264, 512, 2, "swiglu", False),
+    (300, 264, 1056, 4, "swiglu", False),   # k/p = 264: the two dX terms run as two GEMMs
 ]
 
 
