@@ -74,6 +74,7 @@ def _load():
         lib.oracle_partial_sum_f32.argtypes = [i64, i64, i32, vp, vp, vp]
         lib.oracle_num_threads.argtypes = []
         lib.oracle_qkv_shard_f64.argtypes = [i64, i64, i32, i32, i64, i32, i32, vp, vp, vp, vp]
+        lib.oracle_attention_f64.argtypes = [i64, i64, i32, i32, i64, ci, vp, vp, vp, vp]
         lib.oracle_dactivation_f64.argtypes = [ci, i64, vp, vp]
         lib.oracle_dactivation_f64.restype = None
         lib.oracle_mlp_shard_backward_f64.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, vp, ci,
@@ -81,7 +82,7 @@ def _load():
         for name in ("oracle_col_shard_f64", "oracle_row_shard_f64", "oracle_partial_sum_f64",
                      "oracle_mlp_unsharded_f64", "oracle_linear_f32", "oracle_col_shard_f32",
                      "oracle_partial_sum_f32", "oracle_num_threads", "oracle_qkv_shard_f64",
-                     "oracle_mlp_shard_backward_f64"):
+                     "oracle_mlp_shard_backward_f64", "oracle_attention_f64"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -263,3 +264,21 @@ def mlp_shard_backward(X, W1, W2, dZ, i, p, act, b1=None, Wu=None, want_db1=None
         _p(out["dXp"]), _p(out["dW1"]), _p(out["dWu"]), _p(out["db1"]), _p(out["dW2"])),
         "mlp_shard_backward")
     return out
+
+
+def attention(Q, K, V, Hq, Hkv, dh, causal=True, S=None):
+    """Scaled dot-product attention per head in fp64: Q [T, Hq dh], K and V [T, Hkv dh]
+    (query head h reads key/value head h // (Hq / Hkv)); the T tokens are sequences of S
+    (default: one sequence of T).  Returns O [T, Hq dh]."""
+    lib = _load()
+    Q, K, V = _c(Q, np.float64), _c(K, np.float64), _c(V, np.float64)
+    T = Q.shape[0]
+    S = T if S is None else S
+    if Q.shape != (T, Hq * dh) or K.shape != (T, Hkv * dh) or V.shape != (T, Hkv * dh):
+        raise ValueError("shape mismatch")
+    if S <= 0 and T > 0 or (S > 0 and T % S):
+        raise ValueError("T must be a whole number of sequences")
+    O = np.empty((T, Hq * dh), dtype=np.float64)
+    _check(lib.oracle_attention_f64(T // S if S else 0, S, Hq, Hkv, dh, 1 if causal else 0,
+                                    _p(Q), _p(K), _p(V), _p(O)), "attention")
+    return O

@@ -34,6 +34,8 @@
  *       a column-parallel linear whose column blocks are whole heads, and the
  *       output projection is the row-parallel linear above over the head
  *       columns (oracle_qkv_shard_f64 below).
+ *     - The attention core between the projections, per head with grouped
+ *       key/value heads, causal or not (oracle_attention_f64 below).
  *     - The backward pass of a shard (oracle_mlp_shard_backward_f64 below):
  *       the row-parallel step's input gradient is local, the column-parallel
  *       step's is one term of a sum over the shards.
@@ -526,5 +528,64 @@ int oracle_mlp_shard_backward_f64(int64_t T, int64_t d, int64_t k, int32_t i, in
   free(H);
   free(U);
   free(Y);
+  return 0;
+}
+
+/* ---- the attention core between the projections -------------------------- */
+
+/*
+ * Scaled dot-product attention of one head shard, fp64: for every sequence,
+ * query head h and query token t,
+ *   s_j  = (Q[t, h] . K[j, c]) / sqrt(dh)     for the keys j the query sees
+ *   O[t, h] = sum_j softmax(s)_j V[j, c]
+ * with c = h / (Hq / Hkv) the key/value head that query head h reads
+ * (grouped heads; c = h when Hq = Hkv).  Heads never mix, so a GPU that owns
+ * a group of heads computes their attention alone ("Transformer math: tensor
+ * parallel", section "Attention: parallel across heads", which writes the
+ * per-head softmax(Q K^T / sqrt(d_k)) V).  With causal != 0 token t of a
+ * sequence sees the keys 0..t of that sequence (the causal self-attention of
+ * "Building GPT from Scratch, Part 9"); otherwise every key of its sequence.
+ * The T = nseq * S tokens form nseq sequences of S consecutive tokens.
+ *   Q [T, Hq dh] (head h in columns [h dh, (h+1) dh)), K and V [T, Hkv dh],
+ *   O [T, Hq dh], all dense.
+ * The softmax subtracts the largest score before exponentiating.
+ */
+int oracle_attention_f64(int64_t nseq, int64_t S, int32_t Hq, int32_t Hkv, int64_t dh, int causal,
+                         const double *Q, const double *K, const double *V, double *O) {
+  if (nseq < 0 || S < 0 || Hq < 1 || Hkv < 1 || dh < 1 || Hq % Hkv != 0) return -1;
+  const int64_t group = Hq / Hkv, qw = (int64_t)Hq * dh, kw = (int64_t)Hkv * dh;
+  const double scale = 1.0 / sqrt((double)dh);
+#pragma omp parallel
+  {
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+#pragma omp for collapse(2) schedule(static)
+    for (int64_t b = 0; b < nseq; ++b)
+      for (int64_t h = 0; h < Hq; ++h) {
+        const int64_t c = h / group;
+        for (int64_t t = 0; t < S; ++t) {
+          const int64_t tq = b * S + t;
+          const int64_t nk = causal ? t + 1 : S;
+          double mx = -INFINITY;
+          for (int64_t j = 0; j < nk; ++j) {
+            const int64_t tk = b * S + j;
+            double dot = 0.0;
+            for (int64_t e = 0; e < dh; ++e) dot += Q[tq * qw + h * dh + e] * K[tk * kw + c * dh + e];
+            sc[j] = dot * scale;
+            if (sc[j] > mx) mx = sc[j];
+          }
+          double den = 0.0;
+          for (int64_t j = 0; j < nk; ++j) {
+            sc[j] = exp(sc[j] - mx);
+            den += sc[j];
+          }
+          for (int64_t e = 0; e < dh; ++e) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < nk; ++j) acc += sc[j] * V[(b * S + j) * kw + c * dh + e];
+            O[tq * qw + h * dh + e] = acc / den;
+          }
+        }
+      }
+    free(sc);
+  }
   return 0;
 }

@@ -65,6 +65,12 @@ MUTANTS = [
      "acc += dH[t * hw + j] * W1[c * k + j];", 0),
     ("bias gradient drops the first token", "for (int64_t t = 0; t < T; ++t) a += dH[t * hw + j];",
      "for (int64_t t = 1; t < T; ++t) a += dH[t * hw + j];", 0),
+    ("attention without the 1/sqrt(dh) scale", "const double scale = 1.0 / sqrt((double)dh);",
+     "const double scale = 1.0;", 0),
+    ("attention mask hides the diagonal", "const int64_t nk = causal ? t + 1 : S;",
+     "const int64_t nk = causal ? (t > 0 ? t : 1) : S;", 0),
+    ("grouped heads interleaved", "const int64_t c = h / group;", "const int64_t c = h % Hkv;", 0),
+    ("attention ignores the sequence start", "const int64_t tk = b * S + j;", "const int64_t tk = j;", 0),
 ]
 
 

@@ -689,3 +689,79 @@ def test_activation_derivatives(act):
     assert np.max(np.abs(tx.grad.numpy() - ana)) < 1e-14
     if act == "relu":
         assert oracle.dactivation("relu", np.array([0.0]))[0] == 0.0
+
+
+# ---------------------------------------------------------------- P-12 -------
+# The attention core between the projections: per-head softmax(Q K^T / sqrt(dk)) V
+# ('Transformer math: tensor parallel', section "Attention: parallel across heads"),
+# causal in the GPT module of 'Building GPT from Scratch, Part 9'.
+def _qkv(T, Hq, Hkv, dh, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((T, Hq * dh)) * scale, rng.standard_normal((T, Hkv * dh)) * scale,
+            rng.standard_normal((T, Hkv * dh)))
+
+
+@pytest.mark.parametrize("Hq,Hkv,causal,S", [(4, 4, True, 12), (8, 2, True, 6), (6, 3, False, 4),
+                                             (4, 1, False, 12)])
+def test_attention_against_torch_sdpa(Hq, Hkv, causal, S):
+    """torch's fp64 scaled_dot_product_attention (key/value heads repeated for the
+    grouped case), per sequence."""
+    T, dh = 12, 8
+    Q, K, V = _qkv(T, Hq, Hkv, dh, Hq * 10 + Hkv)
+    O = oracle.attention(Q, K, V, Hq, Hkv, dh, causal=causal, S=S)
+    g = Hq // Hkv
+    for b in range(T // S):
+        rows = slice(b * S, (b + 1) * S)
+        q = torch.tensor(Q[rows]).reshape(S, Hq, dh).transpose(0, 1)
+        k = torch.tensor(K[rows]).reshape(S, Hkv, dh).transpose(0, 1).repeat_interleave(g, dim=0)
+        v = torch.tensor(V[rows]).reshape(S, Hkv, dh).transpose(0, 1).repeat_interleave(g, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)
+        ref = ref.transpose(0, 1).reshape(S, Hq * dh).numpy()
+        assert rel_fro(O[rows], ref) < 1e-12
+
+
+def test_attention_special_cases():
+    """The first token of a causal sequence sees only itself (output = its value
+    row); equal keys give the plain mean of the visible values; one key far above
+    the others takes all the weight."""
+    T, H, dh = 6, 2, 4
+    Q, K, V = _qkv(T, H, H, dh, 3)
+    O = oracle.attention(Q, K, V, H, H, dh, causal=True)
+    assert np.array_equal(O[0], V[0])
+    Ke = np.tile(K[:1], (T, 1))
+    Oe = oracle.attention(Q, Ke, V, H, H, dh, causal=True)
+    for t in range(T):
+        assert np.allclose(Oe[t], V[:t + 1].mean(axis=0), rtol=0, atol=1e-12)
+    Qs = np.ones((T, H * dh))
+    Ks = np.zeros((T, H * dh))
+    Ks[2] = 100.0
+    Os = oracle.attention(Qs, Ks, V, H, H, dh, causal=False)
+    assert np.allclose(Os, np.tile(V[2], (T, 1)), rtol=0, atol=1e-12)
+
+
+def test_attention_scale_and_key_order():
+    """Scores are scaled by 1/sqrt(dh) (doubling Q and K is the same as quartering
+    the temperature); without the causal mask the order of the keys does not
+    matter."""
+    T, H, dh = 7, 3, 16
+    Q, K, V = _qkv(T, H, H, dh, 11)
+    O = oracle.attention(Q, K, V, H, H, dh, causal=False)
+    perm = np.random.default_rng(1).permutation(T)
+    assert rel_fro(oracle.attention(Q, K[perm], V[perm], H, H, dh, causal=False), O) < 1e-13
+    # plain definition at dh = 16 for one row of one head (numpy), via the scale
+    s = Q[3, :dh] @ K[:, :dh].T / 4.0
+    w = np.exp(s - s.max())
+    assert np.allclose(O[3, :dh], (w / w.sum()) @ V[:, :dh], rtol=0, atol=1e-13)
+
+
+def test_attention_heads_split_across_shards():
+    """Head shards: the attention of shard i's heads (its query and key/value
+    column blocks) is exactly shard i's block of the unsharded attention."""
+    T, Hq, Hkv, dh, p = 9, 8, 4, 4, 4
+    Q, K, V = _qkv(T, Hq, Hkv, dh, 21)
+    O = oracle.attention(Q, K, V, Hq, Hkv, dh)
+    qw, kw = Hq * dh // p, Hkv * dh // p
+    for i in range(p):
+        Oi = oracle.attention(Q[:, i * qw:(i + 1) * qw], K[:, i * kw:(i + 1) * kw],
+                              V[:, i * kw:(i + 1) * kw], Hq // p, Hkv // p, dh)
+        assert np.array_equal(Oi, O[:, i * qw:(i + 1) * qw])
