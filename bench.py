@@ -296,10 +296,11 @@ def gpt_bench(torch, tp, synth, steps, warmup):
 
 
 def attention_bench(torch, tp, synth, steps, warmup, rotate_bytes=600 << 20):
-    """Attention projections of one head shard of Llama-70B at TP = 8 (64 query
-    and 8 key/value heads of 128, d = 8192): the fused QKV projection
-    (tp_qkv_linear, shard 3 of the full packed weight) and the output
-    projection's row block (tp_row_linear on a stand-in attention output).
+    """Attention block of one head shard of Llama-70B at TP = 8 (64 query and 8
+    key/value heads of 128, d = 8192): the fused QKV projection (tp_qkv_linear,
+    shard 3 of the full packed weight), the causal attention core (tp_attention,
+    8 query heads on 1 key/value head) and the output projection's row block
+    (tp_row_linear; timed alone on a stand-in attention output).
     Prefill T = 4096 after the clock ramp; decode T = 1, 8, 64 with the weights
     rotating over the 8 shards of 2 copies of the full matrices (16 x 38 MB, more
     than twice the 256 MB Infinity Cache).  HIP-graph replay."""
@@ -313,20 +314,32 @@ def attention_bench(torch, tp, synth, steps, warmup, rotate_bytes=600 << 20):
     Z = torch.empty(W.T, W.d, device=dev)
     qkv = lambda: tp.tp_qkv_linear(X, Wqkv, W.Hq, W.Hkv, W.dh, 3, W.p, QKV)  # noqa: E731
     row = lambda: tp.tp_row_linear(O, WO, 3, W.p, Z)  # noqa: E731
+    hq, hkv = W.Hq // W.p, W.Hkv // W.p
+    qw, kw = hq * W.dh, hkv * W.dh
+    Oc = torch.empty(W.T, W.o_rows, dtype=torch.bfloat16, device=dev)
+    core = lambda: tp.tp_attention(QKV[:, :qw], QKV[:, qw:qw + kw], QKV[:, qw + kw:], Oc,  # noqa
+                                   hq, hkv, W.dh)
+    blockf = lambda: tp.tp_row_linear(Oc, WO, 3, W.p, Z)  # noqa: E731
     ramp(torch, [qkv, row])
     t = time_graph(torch, [qkv, row], max(10, steps), warmup)
     sp = LAST_SPREAD
     tq = time_graph(torch, [qkv], max(5, steps), warmup)
     tr = time_graph(torch, [row], max(5, steps), warmup)
+    tc = time_graph(torch, [core], max(5, steps), warmup)
+    tb = time_graph(torch, [qkv, core, blockf], max(5, steps), warmup)
     fq = 2.0 * W.T * W.d * W.qkv_cols
     fr = 2.0 * W.T * W.o_rows * W.d
+    fc = 4.0 * W.dh * hq * (W.T * (W.T + 1) / 2)  # causal: query t sees t + 1 keys
     out["prefill"] = {
         "workload": W.name, "T": W.T, "us": round(t * 1e6, 1),
         "TFLOPs": round((fq + fr) / t / 1e12, 1),
         "frac_mfma": round((fq + fr) / t / 1e12 / PEAK_BF16_TFLOPS, 4), "spread": sp,
         "qkv_us": round(tq * 1e6, 1), "qkv_TFLOPs": round(fq / tq / 1e12, 1),
-        "o_proj_us": round(tr * 1e6, 1), "o_proj_TFLOPs": round(fr / tr / 1e12, 1)}
-    del X, QKV, O, Z
+        "o_proj_us": round(tr * 1e6, 1), "o_proj_TFLOPs": round(fr / tr / 1e12, 1),
+        "core_us": round(tc * 1e6, 1), "core_TFLOPs": round(fc / tc / 1e12, 1),
+        "core_flops": fc, "block_us": round(tb * 1e6, 1),
+        "block_TFLOPs": round((fq + fr + fc) / tb / 1e12, 1)}
+    del X, QKV, O, Z, Oc
     Wd = synth.ATTN_WORKLOADS["llama70b_attn_decode_tp8"]
     sets = [(Wqkv, WO), (Wqkv.clone(), WO.clone())]
     pairs = [(s, i) for s in sets for i in range(W.p)]

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 3
+#define TPMLP_ABI_VERSION 4
 #define TP_MAX_SHARDS 64
 
 typedef enum {
@@ -293,6 +293,29 @@ tp_status tp_qkv_linear(tp_dtype dt, int64_t T, int64_t d, int32_t Hq, int32_t H
                         int32_t i, int32_t p, const void *X, int64_t ldx, const void *Wqkv,
                         int64_t ldw, const void *bqkv, void *QKV, int64_t ldo, void *ws,
                         size_t ws_bytes, void *stream);
+
+/*
+ * Attention core of head shard i, between the QKV projection and W_O (bf16
+ * only): for every sequence, query head h and query token t,
+ *   O[t, h] = sum_j softmax_j( Q[t, h] . K[j, c] / sqrt(dh) ) V[j, c]
+ * over the keys j of t's sequence (j <= t when causal != 0), with
+ * c = h / (Hq / Hkv) the key/value head query head h reads.  Heads never mix,
+ * so a GPU computes the attention of its own heads with no communication
+ * ("Transformer math: tensor parallel", section "Attention: parallel across
+ * heads"; the causal form is the GPT module's of "Building GPT from Scratch,
+ * Part 9").  Here Hq and Hkv are the shard's own head counts.
+ *   T = nseq * S tokens: nseq sequences of S consecutive tokens
+ *   Q [T, Hq dh], ldq; K and V [T, Hkv dh], ldk, ldv   (head h in columns
+ *     [h dh, (h+1) dh)); the output of tp_qkv_linear is Q = QKV, K = QKV + qw,
+ *     V = QKV + qw + kw with ldq = ldk = ldv = its ldo
+ *   O [T, Hq dh], ldo   output, overwritten; the input of the W_O row block
+ * dh must be 64 or 128 (TP_ERR_BAD_SHAPE otherwise), Hq a multiple of Hkv
+ * (TP_ERR_NOT_DIVISIBLE).  fp32 softmax and accumulation; the probabilities
+ * enter the second product rounded to bf16.  No workspace.
+ */
+tp_status tp_attention(tp_dtype dt, int64_t nseq, int64_t S, int32_t Hq, int32_t Hkv, int64_t dh,
+                       int32_t causal, const void *Q, int64_t ldq, const void *K, int64_t ldk,
+                       const void *V, int64_t ldv, void *O, int64_t ldo, void *stream);
 
 /* Bytes of workspace tp_qkv_linear needs for these sizes (0 if none, or for
  * invalid arguments); the same contract as tp_workspace_bytes. */

@@ -20,8 +20,9 @@ from ._binding import (  # noqa: F401
     library,
     library_path,
     tp_abi_version,
-    tp_calib_mfma_bf16,
+    tp_attention,
     tp_backward_workspace_bytes,
+    tp_calib_mfma_bf16,
     tp_col_linear,
     tp_col_linear_train,
     tp_mlp_shard,
@@ -37,8 +38,9 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "ACT", "DTYPE", "TpError", "library", "library_path", "tp_abi_version", "tp_calib_mfma_bf16",
-    "tp_backward_workspace_bytes", "tp_col_linear", "tp_col_linear_train", "tp_mlp_shard_backward", "tp_mlp_shard", "tp_mlp_simulated", "tp_partial_sum", "tp_qkv_linear",
-    "tp_qkv_workspace_bytes", "tp_row_linear",
-    "tp_shard_bounds", "tp_workspace_bytes", "workspace",
+    "ACT", "DTYPE", "TpError", "library", "library_path", "tp_abi_version", "tp_attention",
+    "tp_backward_workspace_bytes", "tp_calib_mfma_bf16", "tp_col_linear", "tp_col_linear_train",
+    "tp_mlp_shard", "tp_mlp_shard_backward", "tp_mlp_simulated", "tp_partial_sum", "tp_qkv_linear",
+    "tp_qkv_workspace_bytes", "tp_row_linear", "tp_shard_bounds", "tp_workspace_bytes",
+    "workspace",
 ]

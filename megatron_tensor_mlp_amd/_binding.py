@@ -76,11 +76,13 @@ def library():
     lib.tp_mlp_shard_backward.argtypes = [ci, ci, i64, i64, i64, i32, i32, vp, i64, vp, i64, vp,
                                           i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp,
                                           i64, vp, i64, vp, i64, vp, vp, i64, vp, sz, vp]
+    lib.tp_attention.argtypes = [ci, i64, i64, i32, i32, i64, i32, vp, i64, vp, i64, vp, i64,
+                                 vp, i64, vp]
     lib.tp_backward_workspace_bytes.argtypes = [ci, ci, i64, i64, i64, i32, i32]
     lib.tp_backward_workspace_bytes.restype = sz
     for name in ("tp_col_linear", "tp_row_linear", "tp_mlp_shard", "tp_partial_sum",
                  "tp_mlp_simulated", "tp_shard_bounds", "tp_calib_mfma_bf16", "tp_qkv_linear",
-                 "tp_col_linear_train", "tp_mlp_shard_backward"):
+                 "tp_col_linear_train", "tp_mlp_shard_backward", "tp_attention"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -357,3 +359,22 @@ def tp_mlp_shard_backward(X, W1, W2, H, Y, dZ, i: int, p: int, dH, dXp, dW1, dW2
         _ptr(H), ldh, _ptr(Y), ldy, _ptr(dZ), lddz, _ptr(dH), lddh, _ptr(dXp), lddx, _ptr(dW1),
         lddw1, _ptr(dWu), lddwu, _ptr(db1), _ptr(dW2), lddw2, wsp, wsn, _stream(stream)))
     return dH, dXp, dW1, dW2
+
+
+def tp_attention(Q, K, V, O, Hq: int, Hkv: int, dh: int, S: int | None = None, causal=True,
+                 stream=None):
+    """O <- per-head softmax(Q K^T / sqrt(dh)) V (bf16) over sequences of S tokens (default:
+    one sequence of T).  Q, O: [T, Hq dh] views, K, V: [T, Hkv dh] views (e.g. the column
+    blocks of tp_qkv_linear's output)."""
+    T = Q.shape[0]
+    S = T if S is None else S
+    if S < 0 or (S > 0 and T % S) or (S == 0 and T > 0):
+        raise ValueError("T must be a whole number of sequences of S tokens")
+    nseq = T // S if S > 0 else 0
+    ldq = _ld(Q, T, Hq * dh, "Q")
+    ldk = _ld(K, T, Hkv * dh, "K")
+    ldv = _ld(V, T, Hkv * dh, "V")
+    ldo = _ld(O, T, Hq * dh, "O")
+    _check(library().tp_attention(_dt(Q), nseq, S, Hq, Hkv, dh, 1 if causal else 0, _ptr(Q), ldq,
+                                  _ptr(K), ldk, _ptr(V), ldv, _ptr(O), ldo, _stream(stream)))
+    return O

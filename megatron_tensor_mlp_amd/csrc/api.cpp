@@ -794,6 +794,52 @@ tp_status tp_qkv_linear(tp_dtype dt, int64_t T, int64_t d, int32_t Hq, int32_t H
   return ok();
 }
 
+tp_status tp_attention(tp_dtype dt, int64_t nseq, int64_t S, int32_t Hq, int32_t Hkv, int64_t dh,
+                       int32_t causal, const void *Q, int64_t ldq, const void *K, int64_t ldk,
+                       const void *V, int64_t ldv, void *O, int64_t ldo, void *stream) {
+  if (dt != TP_BF16)
+    return fail(TP_ERR_BAD_DTYPE, "the attention core runs in bf16 only (dtype %d)", (int)dt);
+  if (nseq < 0 || S < 0)
+    return fail(TP_ERR_BAD_SHAPE, "nseq = %lld and S = %lld must be >= 0", (long long)nseq,
+                (long long)S);
+  if (Hq < 1 || Hkv < 1)
+    return fail(TP_ERR_BAD_SHAPE, "Hq = %d and Hkv = %d must be >= 1", Hq, Hkv);
+  if (Hq % Hkv)
+    return fail(TP_ERR_NOT_DIVISIBLE, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
+  if (dh != 64 && dh != 128)
+    return fail(TP_ERR_BAD_SHAPE, "head width dh = %lld: 64 and 128 are supported", (long long)dh);
+  TRY(check_ld("ldq", ldq, (int64_t)Hq * dh, dt));
+  TRY(check_ld("ldk", ldk, (int64_t)Hkv * dh, dt));
+  TRY(check_ld("ldv", ldv, (int64_t)Hkv * dh, dt));
+  TRY(check_ld("ldo", ldo, (int64_t)Hq * dh, dt));
+  if (nseq == 0 || S == 0) return ok();
+  TRY(check_ptr("Q", Q));
+  TRY(check_ptr("K", K));
+  TRY(check_ptr("V", V));
+  TRY(check_ptr("O", O));
+  AttnArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.ldq = ldq;
+  a.ldk = ldk;
+  a.ldv = ldv;
+  a.ldo = ldo;
+  a.nseq = nseq;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.dh = (int)dh;
+  a.causal = causal ? 1 : 0;
+  a.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)dh));
+  if (!attention_supported(a))
+    return fail(TP_ERR_BAD_SHAPE, "leading dimensions must be below 2^23 elements");
+  const hipError_t e = launch_attention(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t tp_qkv_workspace_bytes(tp_dtype dt, int64_t T, int64_t d, int32_t Hq, int32_t Hkv,
                               int64_t dh, int32_t p) {
   static const char dummy[16] __attribute__((aligned(16))) = {0};

@@ -98,6 +98,19 @@ hipError_t launch_gemm_bf16_decode(const GemmArgs &a, void *ws, hipStream_t s);
 hipError_t launch_calib_mfma(int gaussian, int64_t iters, uint64_t *stats, int nwg,
                              hipStream_t s);
 
+// Attention core of one head shard (bf16): O = softmax(Q K^T / sqrt(dh)) V per
+// query head h, key/value head h / (Hq / Hkv); nseq sequences of S tokens.
+struct AttnArgs {
+  const void *Q, *K, *V;  // [T, Hq dh], [T, Hkv dh], [T, Hkv dh] (head-major columns)
+  void *O;                // [T, Hq dh]
+  int64_t ldq, ldk, ldv, ldo;
+  int64_t nseq, S;
+  int Hq, Hkv, dh, causal;
+  float scale_log2;       // log2(e) / sqrt(dh)
+};
+bool attention_supported(const AttnArgs &a);
+hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
+
 // fp32 path (correctness-first): one output per thread, k ascending.
 hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s);
 

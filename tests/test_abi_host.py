@@ -348,3 +348,32 @@ def test_backward_workspace_bytes():
     assert tp.tp_backward_workspace_bytes(bf16, "gelu_tanh", 4096, 8192, 28672, 8, False) == 0
     assert tp.tp_backward_workspace_bytes(bf16, "swiglu", 4096, 8192, 28672, 8, True) == 0
     assert tp.tp_backward_workspace_bytes(bf16, "gelu_tanh", 4096, 8192, 28672, 5, True) == 0
+
+
+def attn(dt=1, nseq=1, S=64, Hq=4, Hkv=2, dh=128, causal=1, Q=A, ldq=1024, K=A, ldk=1024, V=A,
+         ldv=1024, O=A, ldo=512):
+    return tp.library().tp_attention(dt, nseq, S, Hq, Hkv, dh, causal, P(Q), ldq, P(K), ldk, P(V),
+                                     ldv, P(O), ldo, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dt=0), "TP_ERR_BAD_DTYPE"),          # bf16 only
+    (dict(Hkv=3), "TP_ERR_NOT_DIVISIBLE"),
+    (dict(dh=96, ldq=384, ldo=384), "TP_ERR_BAD_SHAPE"),
+    (dict(Hq=0), "TP_ERR_BAD_SHAPE"),
+    (dict(S=-1), "TP_ERR_BAD_SHAPE"),
+    (dict(ldo=500), "TP_ERR_BAD_SHAPE"),
+    (dict(ldk=200), "TP_ERR_BAD_SHAPE"),
+    (dict(ldq=1028), "TP_ERR_MISALIGNED"),
+    (dict(Q=None), "TP_ERR_NULL_POINTER"),
+    (dict(V=MIS), "TP_ERR_MISALIGNED"),
+])
+def test_attention_rejects(kw, expect):
+    assert status_name(attn(**kw)) == expect
+
+
+@no_gpu
+def test_attention_empty_is_ok():
+    assert status_name(attn(nseq=0, Q=None, K=None, V=None, O=None)) == "TP_OK"
+    assert status_name(attn(S=0, Q=None, K=None, V=None, O=None)) == "TP_OK"

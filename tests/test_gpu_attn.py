@@ -1,11 +1,9 @@
-"""GPU parity of the attention projections of one head shard: the fused QKV
-projection (tp_qkv_linear, column-parallel by heads) and the output projection
-(tp_row_linear over the head rows), through the C ABI, against the CPU oracle on
-the same seeded inputs.  Small cases span several tiles with ragged tails and
-head blocks that start inside a tile; full-size workloads are checked on
-sampled token rows."""
-import math
-
+"""GPU parity of the attention block of one head shard: the fused QKV
+projection (tp_qkv_linear, column-parallel by heads), the attention core
+(tp_attention) and the output projection (tp_row_linear over the head rows),
+through the C ABI, against the CPU oracle on the same seeded inputs.  Small
+cases span several tiles with ragged tails and head blocks that start inside a
+tile; full-size workloads are checked on sampled token rows (or heads)."""
 import numpy as np
 import pytest
 import torch
@@ -140,48 +138,6 @@ def test_qkv_zero_tokens_and_bad_heads():
     assert bool((out == 7.0).all())
 
 
-def _attention(Q, K, V, hq, hkv, dh):
-    """Test-side softmax attention per head (fp64); query head h reads key/value
-    head h // (hq / hkv)."""
-    g = hq // hkv
-    outs = []
-    for h in range(hq):
-        c = h // g
-        q, k, v = Q[:, h * dh:(h + 1) * dh], K[:, c * dh:(c + 1) * dh], V[:, c * dh:(c + 1) * dh]
-        s = q @ k.T / math.sqrt(dh)
-        e = np.exp(s - s.max(axis=1, keepdims=True))
-        outs.append((e / e.sum(axis=1, keepdims=True)) @ v)
-    return np.concatenate(outs, axis=1)
-
-
-def test_head_split_attention_block():
-    """The attention sandwich on the GPU path: each shard's QKV projection, a
-    (test-side) attention over the shard's heads, the shard's row block of W_O
-    into an fp32 partial, and the on-device sum of the partials, against the
-    unsharded block computed from the oracle (full projection, attention over all
-    heads, full output projection)."""
-    T, d, Hq, Hkv, dh, p = 96, 264, 8, 4, 32, 4
-    X, W, b = small_inputs(T, d, Hq, Hkv, dh, 5, True)
-    WO = synth.gaussian_bf16((Hq * dh, d), 8, synth.WEIGHT_STD)
-    qw, kw = Hq * dh // p, Hkv * dh // p
-    parts = []
-    for i in range(p):
-        s = f64(run_qkv(X, W, Hq, Hkv, dh, i, p, bqkv=b))
-        O = _attention(s[:, :qw], s[:, qw:qw + kw], s[:, qw + kw:], Hq // p, Hkv // p, dh)
-        Ob = torch.from_numpy(O).to(torch.bfloat16).to(DEV)
-        Z = torch.empty(T, d, device=DEV)
-        tp.tp_row_linear(Ob, dev(WO), i, p, Z)
-        parts.append(Z)
-    out = torch.empty(T, d, device=DEV)
-    tp.tp_partial_sum(parts, out)
-    torch.cuda.synchronize()
-    full = oracle.qkv_shard(f64(X), f64(W), Hq, Hkv, dh, 0, 1, bqkv=f64(b))
-    Of = _attention(full[:, :Hq * dh], full[:, Hq * dh:(Hq + Hkv) * dh], full[:, (Hq + Hkv) * dh:],
-                    Hq, Hkv, dh)
-    ref = oracle.row_shard(Of, f64(WO), 0, 1)
-    assert_bf16_close(out, ref, "attention block")
-
-
 # --------------------------------------------------------------------- full-size workloads
 def sampled_rows(T, n):
     rows = {0, 1, T - 1, T // 2}
@@ -253,3 +209,93 @@ def test_gpt_qkv_full_size():
     rows = sampled_rows(W.T, 10)
     ref = oracle.qkv_shard(f64(X[rows]), f64(Wqkv), W.Hq, W.Hkv, W.dh, i, W.p)
     assert_bf16_close(out[rows], ref, "QKV")
+
+
+
+# --------------------------------------------------------------------- attention core
+def attn_inputs(T, Hq, Hkv, dh, seed):
+    return (synth.gaussian_bf16((T, Hq * dh), seed), synth.gaussian_bf16((T, Hkv * dh), seed + 1),
+            synth.gaussian_bf16((T, Hkv * dh), seed + 2))
+
+
+# (nseq, S, Hq, Hkv, dh, causal, what)
+ATTN_CASES = [
+    (1, 200, 4, 2, 128, True, "causal, ragged last key tile and query block"),
+    (2, 65, 2, 2, 64, False, "two sequences, dh 64, one key past a tile"),
+    (1, 256, 8, 1, 128, True, "8 query heads on one key/value head"),
+    (3, 1, 2, 1, 64, True, "one-token sequences"),
+    (1, 300, 4, 4, 128, False, "no mask, odd block count"),
+    (2, 128, 6, 3, 64, True, "two sequences, groups of 2"),
+]
+
+
+@pytest.mark.parametrize("nseq,S,Hq,Hkv,dh,causal,what", ATTN_CASES)
+def test_attention_core(nseq, S, Hq, Hkv, dh, causal, what):
+    T = nseq * S
+    Q, K, V = attn_inputs(T, Hq, Hkv, dh, 70 + S)
+    say(f"attention case nseq={nseq} S={S} Hq={Hq} Hkv={Hkv} dh={dh} causal={causal}: {what}")
+    O = torch.full((T, Hq * dh + 8), float("nan"), dtype=torch.bfloat16, device=DEV)
+    tp.tp_attention(dev(Q), dev(K), dev(V), O[:, :Hq * dh], Hq, Hkv, dh, S=S, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.attention(f64(Q), f64(K), f64(V), Hq, Hkv, dh, causal=causal, S=S)
+    assert_bf16_close(O[:, :Hq * dh], ref, "O")
+    assert bool(torch.isnan(O[:, Hq * dh:]).all())
+
+
+def test_attention_on_qkv_views():
+    """The core reads Q, K and V as column blocks of tp_qkv_linear's output (one
+    leading dimension for all three) and writes the input of the W_O row block."""
+    T, d, Hq, Hkv, dh, p = 192, 264, 8, 2, 64, 2
+    X, W, b = small_inputs(T, d, Hq, Hkv, dh, 31, True)
+    qw, kw = Hq * dh // p, Hkv * dh // p
+    QKV = run_qkv(X, W, Hq, Hkv, dh, 1, p, bqkv=b)
+    O = torch.empty(T, qw, dtype=torch.bfloat16, device=DEV)
+    tp.tp_attention(QKV[:, :qw], QKV[:, qw:qw + kw], QKV[:, qw + kw:], O, Hq // p, Hkv // p, dh)
+    torch.cuda.synchronize()
+    ref = oracle.attention(f64(QKV[:, :qw]), f64(QKV[:, qw:qw + kw]), f64(QKV[:, qw + kw:]),
+                           Hq // p, Hkv // p, dh)
+    assert_bf16_close(O, ref, "O")
+
+
+def test_attention_block_through_gpu_path():
+    """The whole attention sandwich on the GPU path: each shard's QKV projection,
+    attention core and W_O row block, then the on-device sum of the partials,
+    against the oracle's unsharded chain (full projection, attention over all
+    heads, full output projection)."""
+    T, d, Hq, Hkv, dh, p = 160, 264, 8, 4, 64, 4
+    X, W, b = small_inputs(T, d, Hq, Hkv, dh, 12, True)
+    WO = synth.gaussian_bf16((Hq * dh, d), 13, synth.WEIGHT_STD)
+    qw, kw = Hq * dh // p, Hkv * dh // p
+    parts = []
+    for i in range(p):
+        QKV = run_qkv(X, W, Hq, Hkv, dh, i, p, bqkv=b)
+        O = torch.empty(T, qw, dtype=torch.bfloat16, device=DEV)
+        tp.tp_attention(QKV[:, :qw], QKV[:, qw:qw + kw], QKV[:, qw + kw:], O, Hq // p, Hkv // p, dh)
+        Z = torch.empty(T, d, device=DEV)
+        tp.tp_row_linear(O, dev(WO), i, p, Z)
+        parts.append(Z)
+    out = torch.empty(T, d, device=DEV)
+    tp.tp_partial_sum(parts, out)
+    torch.cuda.synchronize()
+    full = oracle.qkv_shard(f64(X), f64(W), Hq, Hkv, dh, 0, 1, bqkv=f64(b))
+    Of = oracle.attention(full[:, :Hq * dh], full[:, Hq * dh:(Hq + Hkv) * dh],
+                          full[:, (Hq + Hkv) * dh:], Hq, Hkv, dh)
+    assert_bf16_close(out, oracle.row_shard(Of, f64(WO), 0, 1), "attention block")
+
+
+def test_llama_attention_core_full_size():
+    """Llama-70B head shard at TP = 8 (8 query heads, 1 key/value head of 128), one
+    causal sequence of 4096 tokens; checked on two of the eight heads (the oracle
+    on the full sequence)."""
+    W = synth.ATTN_WORKLOADS["llama70b_attn_prefill_tp8"]
+    hq, hkv, dh, T = W.Hq // W.p, W.Hkv // W.p, W.dh, W.T
+    Q, K, V = attn_inputs(T, hq, hkv, dh, 80)
+    say(f"workload {W.name} attention core: T={T} heads {hq}/{hkv}")
+    O = torch.empty(T, hq * dh, dtype=torch.bfloat16, device=DEV)
+    tp.tp_attention(dev(Q), dev(K), dev(V), O, hq, hkv, dh)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(O).all())
+    heads = [0, hq - 1]
+    cols = np.concatenate([np.arange(h * dh, (h + 1) * dh) for h in heads])
+    ref = oracle.attention(f64(Q)[:, cols], f64(K), f64(V), len(heads), hkv, dh)
+    assert_bf16_close(f64(O)[:, cols], ref, "O")
