@@ -1,6 +1,15 @@
 // Direct HBM -> LDS loads and the explicit waits and barriers that go with
 // them (gfx950).
 //
+// Hazard: on this GPU family a vector memory instruction that reads an SGPR
+// written by a VALU instruction (the descriptor bases below come from
+// v_readfirstlane) needs 5 wait states in between, and an LDS DMA that reads
+// M0 right after an SALU write of M0 needs 1.  The compiler inserts those
+// wait states for the memory instructions it emits, but it cannot see into
+// the asm statements below, and it may schedule the descriptor's
+// v_readfirstlane one or two instructions before them; so every load here
+// begins with s_nop 4 (5 wait states) of its own.
+//
 // A buffer load with the `lds` modifier writes the data of lane i straight to
 // LDS at m0 + size * i, without passing through registers.  The loads are
 // issued as inline asm so that the compiler adds no waits of its own for them:
@@ -45,7 +54,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 
 // 16 bytes per lane from buffer offset `voff` into LDS at lds_dst + 16 * lane.
 __device__ __forceinline__ void dma16(const i32x4 &rs, const void *lds_dst, uint32_t voff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(rs), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_dst)))
                : "memory");
@@ -55,7 +64,7 @@ __device__ __forceinline__ void dma16(const i32x4 &rs, const void *lds_dst, uint
 // weights): the lines are not kept in the caches, so they do not displace data
 // that is reused.
 __device__ __forceinline__ void dma16_nt(const i32x4 &rs, const void *lds_dst, uint32_t voff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
                :
                : "v"(voff), "s"(rs), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_dst)))
                : "memory");
@@ -63,7 +72,7 @@ __device__ __forceinline__ void dma16_nt(const i32x4 &rs, const void *lds_dst, u
 
 // 4 bytes per lane from buffer offset `voff` into LDS at lds_dst + 4 * lane.
 __device__ __forceinline__ void dma4(const i32x4 &rs, const void *lds_dst, uint32_t voff) {
-  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(rs), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_dst)))
                : "memory");
