@@ -226,6 +226,13 @@ ATTN_CASES = [
     (3, 1, 2, 1, 64, True, "one-token sequences"),
     (1, 300, 4, 4, 128, False, "no mask, odd block count"),
     (2, 128, 6, 3, 64, True, "two sequences, groups of 2"),
+    (2, 129, 2, 1, 128, True, "odd block count: the middle block's tiles split between the groups"),
+    (1, 64, 2, 2, 128, True, "one full tile"),
+    (1, 576, 2, 1, 128, True, "9 blocks, 45 tiles: every pair splits a block"),
+    (2, 333, 3, 1, 64, False, "no mask, 6 blocks per sequence, ragged end"),
+    (1, 300, 4, 1, 128, True, "4 heads per workgroup (16-query blocks), ragged end"),
+    (2, 200, 8, 2, 64, True, "4 heads per workgroup, two key/value heads, dh 64"),
+    (1, 250, 8, 4, 128, False, "2 heads per workgroup, no mask"),
 ]
 
 
