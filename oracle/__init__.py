@@ -79,10 +79,15 @@ def _load():
         lib.oracle_dactivation_f64.restype = None
         lib.oracle_mlp_shard_backward_f64.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, vp, ci,
                                                       vp, vp, vp, vp, vp, vp, vp, vp]
+        cd = ctypes.c_double
+        lib.oracle_layernorm_f64.argtypes = [i64, i64, vp, vp, vp, cd, vp]
+        lib.oracle_block_f64.argtypes = [i64, i64, i64, i32, i32, i64, i64, ci, ci, cd, vp, vp, vp,
+                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp]
         for name in ("oracle_col_shard_f64", "oracle_row_shard_f64", "oracle_partial_sum_f64",
                      "oracle_mlp_unsharded_f64", "oracle_linear_f32", "oracle_col_shard_f32",
                      "oracle_partial_sum_f32", "oracle_num_threads", "oracle_qkv_shard_f64",
-                     "oracle_mlp_shard_backward_f64", "oracle_attention_f64"):
+                     "oracle_mlp_shard_backward_f64", "oracle_attention_f64",
+                     "oracle_layernorm_f64", "oracle_block_f64"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -282,3 +287,42 @@ def attention(Q, K, V, Hq, Hkv, dh, causal=True, S=None):
     _check(lib.oracle_attention_f64(T // S if S else 0, S, Hq, Hkv, dh, 1 if causal else 0,
                                     _p(Q), _p(K), _p(V), _p(O)), "attention")
     return O
+
+
+def layernorm(X, gamma, beta, eps=1e-5):
+    """LayerNorm of each row of X [T, d] in fp64 (biased variance, learned scale and
+    shift): (x - mean) / sqrt(var + eps) * gamma + beta."""
+    lib = _load()
+    X = _c(X, np.float64)
+    T, d = X.shape
+    g, b = _c(gamma, np.float64), _c(beta, np.float64)
+    if g.shape != (d,) or b.shape != (d,):
+        raise ValueError("shape mismatch")
+    Y = np.empty((T, d), dtype=np.float64)
+    _check(lib.oracle_layernorm_f64(T, d, _p(X), _p(g), _p(b), float(eps), _p(Y)), "layernorm")
+    return Y
+
+
+def block(X, Hq, Hkv, dh, act, ln1, Wqkv, WO, ln2, W1, W2, S=None, causal=True, eps=1e-5,
+          bqkv=None, bO=None, Wu=None, b1=None, b2=None, rows=None):
+    """One pre-LayerNorm transformer block in fp64, unsharded: X [T, d] (sequences of
+    S tokens, default one of T); ln1 and ln2 are (gamma, beta) pairs; Wqkv [d, (Hq +
+    2 Hkv) dh], WO [Hq dh, d], W1 (and Wu) [d, k], W2 [k, d].  Returns the block output
+    for the token rows listed in `rows` (default all), [len(rows), d]."""
+    lib = _load()
+    X = _c(X, np.float64)
+    T, d = X.shape
+    S = T if S is None else S
+    if S <= 0 and T > 0 or (S > 0 and T % S):
+        raise ValueError("T must be a whole number of sequences")
+    k = W1.shape[1]
+    f = lambda a: _c(a, np.float64)  # noqa: E731
+    args = [f(ln1[0]), f(ln1[1]), f(Wqkv), f(bqkv), f(WO), f(bO), f(ln2[0]), f(ln2[1]), f(W1),
+            f(Wu), f(b1), f(W2), f(b2)]
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = T if r is None else len(r)
+    Out = np.empty((n, d), dtype=np.float64)
+    _check(lib.oracle_block_f64(T // S if S else 0, S, d, Hq, Hkv, dh, k, 1 if causal else 0,
+                                _act(act), float(eps), _p(X), *[_p(a) for a in args], n,
+                                _p(r), _p(Out)), "block")
+    return Out

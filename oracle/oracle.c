@@ -36,6 +36,9 @@
  *       columns (oracle_qkv_shard_f64 below).
  *     - The attention core between the projections, per head with grouped
  *       key/value heads, causal or not (oracle_attention_f64 below).
+ *     - One pre-LayerNorm transformer block (oracle_layernorm_f64 and
+ *       oracle_block_f64 below), unsharded: the reference a sharded block is
+ *       checked against.
  *     - The backward pass of a shard (oracle_mlp_shard_backward_f64 below):
  *       the row-parallel step's input gradient is local, the column-parallel
  *       step's is one term of a sum over the shards.
@@ -588,4 +591,122 @@ int oracle_attention_f64(int64_t nseq, int64_t S, int32_t Hq, int32_t Hkv, int64
     free(sc);
   }
   return 0;
+}
+
+/* ---- one transformer block ------------------------------------------------ */
+
+/*
+ * LayerNorm of each row of X [T,d], fp64: with the row's mean
+ *   mu = (1/d) sum_c x_c   and its (biased) variance   var = (1/d) sum_c (x_c - mu)^2,
+ *   Y[t,c] = (x_c - mu) / sqrt(var + eps) * gamma[c] + beta[c].
+ * The pages name the normalisation only ("Building GPT from Scratch, Part 9",
+ * section "Communication Pattern per Transformer Block": a LayerNorm before
+ * attention and one before the FFN, replicated on every GPU); this is the
+ * standard definition (Ba, Kiros and Hinton, 2016) with a learned scale and
+ * shift.
+ */
+int oracle_layernorm_f64(int64_t T, int64_t d, const double *X, const double *gamma,
+                         const double *beta, double eps, double *Y) {
+  if (T < 0 || d < 1) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    const double *x = X + t * d;
+    double sum = 0.0;
+    for (int64_t c = 0; c < d; ++c) sum += x[c];
+    const double mu = sum / (double)d;
+    double sq = 0.0;
+    for (int64_t c = 0; c < d; ++c) sq += (x[c] - mu) * (x[c] - mu);
+    const double var = sq / (double)d;
+    const double rstd = 1.0 / sqrt(var + eps);
+    for (int64_t c = 0; c < d; ++c) Y[t * d + c] = (x[c] - mu) * rstd * gamma[c] + beta[c];
+  }
+  return 0;
+}
+
+/*
+ * One pre-LayerNorm transformer block, unsharded, fp64, in the order of
+ * "Building GPT from Scratch, Part 9", section "Communication Pattern per
+ * Transformer Block" (LayerNorm, attention, residual add, LayerNorm, FFN,
+ * residual add):
+ *   A   = LN1(X)
+ *   QKV = A Wqkv + bqkv          Wqkv [d, (Hq + 2 Hkv) dh]: all query heads,
+ *                                then all key heads, then all value heads
+ *   O   = attention(Q, K, V)     as oracle_attention_f64 (nseq sequences of S)
+ *   X1  = X + (O WO + bO)        WO [Hq dh, d]
+ *   B   = LN2(X1)
+ *   Out = X1 + MLP(B)            MLP as oracle_mlp_unsharded_f64, with b2
+ * X [T,d] with T = nseq S.  The attention half is computed for every token
+ * (keys come from all of them); the FFN half only for the nrows tokens listed
+ * in rows (rows == NULL: all T, in order).  Out [nrows, d].  bqkv, bO, b1 and
+ * b2 may be NULL (no bias); Wu only for act = OR_ACT_SWIGLU.
+ */
+int oracle_block_f64(int64_t nseq, int64_t S, int64_t d, int32_t Hq, int32_t Hkv, int64_t dh,
+                     int64_t k, int causal, int act, double eps, const double *X,
+                     const double *ln1_g, const double *ln1_b, const double *Wqkv,
+                     const double *bqkv, const double *WO, const double *bO,
+                     const double *ln2_g, const double *ln2_b, const double *W1,
+                     const double *Wu, const double *b1, const double *W2, const double *b2,
+                     int64_t nrows, const int64_t *rows, double *Out) {
+  if (nseq < 0 || S < 0 || d < 1 || Hq < 1 || Hkv < 1 || dh < 1 || k < 1 || Hq % Hkv) return -1;
+  if (act == OR_ACT_SWIGLU && Wu == NULL) return -1;
+  const int64_t T = nseq * S, ncol = ((int64_t)Hq + 2 * (int64_t)Hkv) * dh;
+  const int64_t qw = (int64_t)Hq * dh, kw = (int64_t)Hkv * dh;
+  if (rows == NULL) nrows = T;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (rows && (rows[r] < 0 || rows[r] >= T)) return -1;
+  double *A = (double *)malloc(sizeof(double) * (size_t)(T * d + 1));
+  double *QKV = (double *)malloc(sizeof(double) * (size_t)(T * ncol + 1));
+  double *Q = (double *)malloc(sizeof(double) * (size_t)(T * qw + 1));
+  double *K = (double *)malloc(sizeof(double) * (size_t)(T * kw + 1));
+  double *V = (double *)malloc(sizeof(double) * (size_t)(T * kw + 1));
+  double *O = (double *)malloc(sizeof(double) * (size_t)(T * qw + 1));
+  double *X1 = (double *)malloc(sizeof(double) * (size_t)(nrows * d + 1));
+  double *B = (double *)malloc(sizeof(double) * (size_t)(nrows * d + 1));
+  double *Z = (double *)malloc(sizeof(double) * (size_t)(nrows * d + 1));
+  int rc = -1;
+  if (!A || !QKV || !Q || !K || !V || !O || !X1 || !B || !Z) goto out;
+  if (oracle_layernorm_f64(T, d, X, ln1_g, ln1_b, eps, A)) goto out;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double *q = QKV + t * ncol;
+    for (int64_t n = 0; n < ncol; ++n) q[n] = 0.0;
+    for (int64_t c = 0; c < d; ++c) {
+      const double av = A[t * d + c];
+      const double *w = Wqkv + c * ncol;
+      for (int64_t n = 0; n < ncol; ++n) q[n] += av * w[n];
+    }
+    if (bqkv)
+      for (int64_t n = 0; n < ncol; ++n) q[n] += bqkv[n];
+    memcpy(Q + t * qw, q, sizeof(double) * (size_t)qw);
+    memcpy(K + t * kw, q + qw, sizeof(double) * (size_t)kw);
+    memcpy(V + t * kw, q + qw + kw, sizeof(double) * (size_t)kw);
+  }
+  if (oracle_attention_f64(nseq, S, Hq, Hkv, dh, causal, Q, K, V, O)) goto out;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t t = rows ? rows[r] : r;
+    double *x1 = X1 + r * d;
+    for (int64_t n = 0; n < d; ++n) x1[n] = 0.0;
+    for (int64_t j = 0; j < qw; ++j) {
+      const double ov = O[t * qw + j];
+      const double *w = WO + j * d;
+      for (int64_t n = 0; n < d; ++n) x1[n] += ov * w[n];
+    }
+    for (int64_t n = 0; n < d; ++n) x1[n] = X[t * d + n] + (bO ? x1[n] + bO[n] : x1[n]);
+  }
+  if (oracle_layernorm_f64(nrows, d, X1, ln2_g, ln2_b, eps, B)) goto out;
+  if (oracle_mlp_unsharded_f64(nrows, d, k, B, W1, Wu, b1, act, W2, b2, Z)) goto out;
+  for (int64_t e = 0; e < nrows * d; ++e) Out[e] = X1[e] + Z[e];
+  rc = 0;
+out:
+  free(A);
+  free(QKV);
+  free(Q);
+  free(K);
+  free(V);
+  free(O);
+  free(X1);
+  free(B);
+  free(Z);
+  return rc;
 }

@@ -71,6 +71,20 @@ MUTANTS = [
      "const int64_t nk = causal ? (t > 0 ? t : 1) : S;", 0),
     ("grouped heads interleaved", "const int64_t c = h / group;", "const int64_t c = h % Hkv;", 0),
     ("attention ignores the sequence start", "const int64_t tk = b * S + j;", "const int64_t tk = j;", 0),
+    ("layernorm without the mean", "Y[t * d + c] = (x[c] - mu) * rstd * gamma[c] + beta[c];",
+     "Y[t * d + c] = x[c] * rstd * gamma[c] + beta[c];", 0),
+    ("layernorm unbiased variance", "const double var = sq / (double)d;",
+     "const double var = sq / (double)(d - 1);", 0),
+    ("layernorm eps outside the root", "const double rstd = 1.0 / sqrt(var + eps);",
+     "const double rstd = 1.0 / (sqrt(var) + eps);", 0),
+    ("block drops the attention residual",
+     "x1[n] = X[t * d + n] + (bO ? x1[n] + bO[n] : x1[n]);", "x1[n] = bO ? x1[n] + bO[n] : x1[n];", 0),
+    ("block drops the FFN residual", "Out[e] = X1[e] + Z[e];", "Out[e] = Z[e];", 0),
+    ("block's second LayerNorm takes the first one's parameters",
+     "oracle_layernorm_f64(nrows, d, X1, ln2_g, ln2_b, eps, B)",
+     "oracle_layernorm_f64(nrows, d, X1, ln1_g, ln1_b, eps, B)", 0),
+    ("block's output projection reads WO transposed", "const double *w = WO + j * d;\n      for (int64_t n = 0; n < d; ++n) x1[n] += ov * w[n];",
+     "for (int64_t n = 0; n < d; ++n) x1[n] += ov * WO[n * qw + j];", 0),
 ]
 
 

@@ -765,3 +765,129 @@ def test_attention_heads_split_across_shards():
         Oi = oracle.attention(Q[:, i * qw:(i + 1) * qw], K[:, i * kw:(i + 1) * kw],
                               V[:, i * kw:(i + 1) * kw], Hq // p, Hkv // p, dh)
         assert np.array_equal(Oi, O[:, i * qw:(i + 1) * qw])
+
+
+# ---------------------------------------------------------------- P-13 -------
+# One pre-LayerNorm transformer block ('Building GPT from Scratch, Part 9',
+# section "Communication Pattern per Transformer Block": LayerNorm, attention
+# split by heads, residual, LayerNorm, FFN, residual; two reductions).
+@pytest.mark.parametrize("T,d,eps", [(5, 16, 1e-5), (3, 7, 1e-3), (4, 64, 1e-6)])
+def test_layernorm_against_torch(T, d, eps):
+    """torch's fp64 layer_norm (biased variance, scale and shift)."""
+    rng = np.random.default_rng(T * d)
+    X = rng.standard_normal((T, d)) * 3 + 1
+    g, b = rng.standard_normal(d), rng.standard_normal(d)
+    ref = torch.nn.functional.layer_norm(torch.tensor(X), (d,), torch.tensor(g), torch.tensor(b),
+                                         eps=eps).numpy()
+    assert np.abs(oracle.layernorm(X, g, b, eps) - ref).max() < 1e-12
+
+
+def test_layernorm_closed_forms():
+    """A constant row maps to beta exactly; the row (a, -a) maps to
+    +-a / sqrt(a^2 + eps) * gamma + beta."""
+    g, b = np.array([2.0, -3.0]), np.array([0.5, 0.25])
+    Y = oracle.layernorm(np.array([[7.0, 7.0], [1.5, -1.5]]), g, b, eps=0.25)
+    assert np.array_equal(Y[0], b)
+    r = 1.5 / math.sqrt(1.5 ** 2 + 0.25)
+    assert np.allclose(Y[1], [r * 2.0 + 0.5, -r * -3.0 + 0.25], rtol=0, atol=1e-15)
+
+
+def _block_params(d, Hq, Hkv, dh, k, act, seed, bias=True):
+    rng = np.random.default_rng(seed)
+    ncol = (Hq + 2 * Hkv) * dh
+    P = dict(ln1=(rng.standard_normal(d), rng.standard_normal(d)),
+             ln2=(rng.standard_normal(d), rng.standard_normal(d)),
+             Wqkv=rng.standard_normal((d, ncol)) / math.sqrt(d),
+             WO=rng.standard_normal((Hq * dh, d)) / math.sqrt(Hq * dh),
+             W1=rng.standard_normal((d, k)) / math.sqrt(d),
+             W2=rng.standard_normal((k, d)) / math.sqrt(k))
+    if act == "swiglu":
+        P["Wu"] = rng.standard_normal((d, k)) / math.sqrt(d)
+    if bias:
+        P.update(bqkv=rng.standard_normal(ncol), bO=rng.standard_normal(d), b2=rng.standard_normal(d))
+        if act != "swiglu":
+            P["b1"] = rng.standard_normal(k)
+    return P
+
+
+def _torch_block(X, Hq, Hkv, dh, act, S, causal, eps, P):
+    """The same block from torch's fp64 library routines (layer_norm, matmul,
+    scaled_dot_product_attention, gelu, silu, relu)."""
+    t = lambda a: None if a is None else torch.tensor(a)  # noqa: E731
+    X = t(X)
+    T, d = X.shape
+    g = Hq // Hkv
+    ln = lambda x, gb: torch.nn.functional.layer_norm(x, (d,), t(gb[0]), t(gb[1]), eps=eps)  # noqa
+    A = ln(X, P["ln1"])
+    qkv = A @ t(P["Wqkv"]) + (t(P["bqkv"]) if "bqkv" in P else 0)
+    q, kk, v = qkv[:, :Hq * dh], qkv[:, Hq * dh:(Hq + Hkv) * dh], qkv[:, (Hq + Hkv) * dh:]
+    O = torch.empty(T, Hq * dh, dtype=torch.float64)
+    for b in range(T // S):
+        r = slice(b * S, (b + 1) * S)
+        qh = q[r].reshape(S, Hq, dh).transpose(0, 1)
+        kh = kk[r].reshape(S, Hkv, dh).transpose(0, 1).repeat_interleave(g, dim=0)
+        vh = v[r].reshape(S, Hkv, dh).transpose(0, 1).repeat_interleave(g, dim=0)
+        o = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, is_causal=causal)
+        O[r] = o.transpose(0, 1).reshape(S, Hq * dh)
+    X1 = X + (O @ t(P["WO"]) + (t(P["bO"]) if "bO" in P else 0))
+    B = ln(X1, P["ln2"])
+    H = B @ t(P["W1"])
+    if act == "swiglu":
+        H = torch.nn.functional.silu(H) * (B @ t(P["Wu"]))
+    else:
+        H = H + (t(P["b1"]) if "b1" in P else 0)
+        H = {"gelu_tanh": lambda x: torch.nn.functional.gelu(x, approximate="tanh"),
+             "gelu_erf": torch.nn.functional.gelu, "relu": torch.relu,
+             "none": lambda x: x}[act](H)
+    return (X1 + (H @ t(P["W2"]) + (t(P["b2"]) if "b2" in P else 0))).numpy()
+
+
+@pytest.mark.parametrize("T,S,Hq,Hkv,act,causal", [(12, 12, 4, 2, "gelu_tanh", True),
+                                                   (10, 5, 2, 1, "swiglu", True),
+                                                   (8, 4, 4, 4, "gelu_erf", False),
+                                                   (6, 6, 2, 2, "relu", True)])
+def test_block_against_torch(T, S, Hq, Hkv, act, causal):
+    d, dh, k = 16, 4, 24
+    P = _block_params(d, Hq, Hkv, dh, k, act, T * 7 + Hq)
+    X = np.random.default_rng(T).standard_normal((T, d))
+    out = oracle.block(X, Hq, Hkv, dh, act, S=S, causal=causal, eps=1e-5, **P)
+    ref = _torch_block(X, Hq, Hkv, dh, act, S, causal, 1e-5, P)
+    assert rel_fro(out, ref) < 1e-12
+
+
+def test_block_residual_passthrough_and_rows():
+    """With zero output projections and no biases after them the block returns its
+    input exactly (both residual paths carry X through); the rows option gives
+    exactly those rows of the full result."""
+    d, Hq, Hkv, dh, k, T = 16, 4, 2, 4, 24, 9
+    P = _block_params(d, Hq, Hkv, dh, k, "gelu_tanh", 3)
+    X = np.random.default_rng(5).standard_normal((T, d))
+    Z = dict(P, WO=np.zeros_like(P["WO"]), W2=np.zeros_like(P["W2"]), bO=np.zeros(d), b2=np.zeros(d))
+    assert np.array_equal(oracle.block(X, Hq, Hkv, dh, "gelu_tanh", **Z), X)
+    full = oracle.block(X, Hq, Hkv, dh, "gelu_tanh", **P)
+    rows = [8, 0, 3]
+    assert np.array_equal(oracle.block(X, Hq, Hkv, dh, "gelu_tanh", rows=rows, **P), full[rows])
+
+
+@pytest.mark.parametrize("act,p", [("gelu_tanh", 2), ("swiglu", 4)])
+def test_block_equals_its_tensor_parallel_split(act, p):
+    """The block computed shard by shard — per shard its heads' QKV columns, the
+    attention of those heads, the W_O row block, then the sum of the partials; the
+    MLP shards likewise — equals the unsharded block (the two reductions of the
+    page's communication pattern)."""
+    d, Hq, Hkv, dh, k, T = 16, 8, 4, 4, 32, 7
+    P = _block_params(d, Hq, Hkv, dh, k, act, 11)
+    X = np.random.default_rng(13).standard_normal((T, d))
+    A = oracle.layernorm(X, *P["ln1"])
+    qw, kw = Hq * dh // p, Hkv * dh // p
+    parts = []
+    for i in range(p):
+        qkv = oracle.qkv_shard(A, P["Wqkv"], Hq, Hkv, dh, i, p, bqkv=P["bqkv"])
+        Oi = oracle.attention(qkv[:, :qw], qkv[:, qw:qw + kw], qkv[:, qw + kw:], Hq // p, Hkv // p, dh)
+        parts.append(oracle.row_shard(Oi, P["WO"], i, p))
+    X1 = X + oracle.partial_sum(parts, P["bO"])
+    B = oracle.layernorm(X1, *P["ln2"])
+    parts = [oracle.mlp_shard(B, P["W1"], P["W2"], i, p, act, b1=P.get("b1"), Wu=P.get("Wu"))[1]
+             for i in range(p)]
+    out = X1 + oracle.partial_sum(parts, P["b2"])
+    assert rel_fro(out, oracle.block(X, Hq, Hkv, dh, act, **P)) < 1e-12
