@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 4
+#define TPMLP_ABI_VERSION 5
 #define TP_MAX_SHARDS 64
 
 typedef enum {
@@ -321,6 +321,78 @@ tp_status tp_attention(tp_dtype dt, int64_t nseq, int64_t S, int32_t Hq, int32_t
  * invalid arguments); the same contract as tp_workspace_bytes. */
 size_t tp_qkv_workspace_bytes(tp_dtype dt, int64_t T, int64_t d, int32_t Hq, int32_t Hkv,
                               int64_t dh, int32_t p);
+
+/*
+ * Row step of a transformer block ("Building GPT from Scratch, Part 9",
+ * section "Communication Pattern per Transformer Block": each half of the
+ * block ends in an all-reduce of the row-parallel partials and a residual
+ * add, and each half begins with a LayerNorm every GPU applies to the full
+ * row).  For every token row t:
+ *   x = (((parts[0][t] + parts[1][t]) + ...) + bias) + R[t]
+ *       fp32, added left to right in that order; absent terms are skipped
+ *       (p = 0: no partials; bias or R NULL), at least one term is present
+ *   X[t] = x                                     if X != NULL   (fp32)
+ *   A[t] = (x - mean) / sqrt(var + eps) * gamma + beta
+ *       if A != NULL (bf16, rounded once), with the mean and the biased
+ *       variance over the row's d elements; gamma, beta [d] fp32
+ *   T >= 0, 8 <= d <= 16384 and d a multiple of 8; p in [0, TP_MAX_SHARDS];
+ *   parts: host array of p device pointers to [T, d] fp32 (ldp); R [T, d]
+ *   fp32 (ldr); X [T, d] fp32 (ldx), may alias R or parts[0] (in place);
+ *   A [T, d] bf16 (lda), the input of the next half's GEMMs.
+ * gamma, beta and A are given together or not at all; eps finite and >= 0.
+ * With T = 0 nothing is read or written and the buffers may be NULL.
+ * The X it writes equals the same left-to-right fp32 sum bit for bit.
+ * Errors as elsewhere (TP_ERR_BAD_SHAPE, TP_ERR_MISALIGNED,
+ * TP_ERR_NULL_POINTER, TP_ERR_BAD_SHARD); nothing is launched on error.
+ */
+tp_status tp_residual_layernorm(int64_t T, int64_t d, int32_t p, const float *const *parts,
+                                int64_t ldp, const float *bias, const float *R, int64_t ldr,
+                                float *X, int64_t ldx, const float *gamma, const float *beta,
+                                float eps, void *A, int64_t lda, void *stream);
+
+/*
+ * One pre-LayerNorm transformer block of p tensor-parallel shards, all run on
+ * this GPU (bf16 weights and GEMM inputs, fp32 residual stream), in the order
+ * of "Building GPT from Scratch, Part 9", section "Communication Pattern per
+ * Transformer Block":
+ *   A    = LN1(X)
+ *   for shard i: QKV_i = A Wqkv[:, heads of i] + bqkv   (as tp_qkv_linear)
+ *                O_i   = attention of shard i's heads   (as tp_attention)
+ *                P_i   = O_i WO[rows of i's heads, :]   (as tp_row_linear)
+ *   X1   = ((P_0 + P_1) + ...) + bO + X                  (reduction #1)
+ *   A    = LN2(X1)
+ *   for shard i: Z_i = act(A W1_i + b1_i) W2_i (or SwiGLU), as tp_mlp_simulated
+ *   Out  = ((Z_0 + Z_1) + ...) + b2 + X1                 (reduction #2)
+ * The two sums stand for the two all-reduces of the block; every step runs
+ * in this library's kernels (tp_residual_layernorm's for the sums and the
+ * LayerNorms).
+ *   T = nseq * S tokens (nseq sequences of S; attention causal when causal
+ *   != 0); X, Out [T, d] fp32 (ldx, ldout), Out may alias X;
+ *   ln1_g, ln1_b, ln2_g, ln2_b [d] fp32; eps as in tp_residual_layernorm;
+ *   Wqkv [d, (Hq + 2 Hkv) dh] packed as for tp_qkv_linear (ldwqkv), bqkv
+ *   [(Hq + 2 Hkv) dh] or NULL; WO [Hq dh, d] (ldwo), bO [d] fp32 or NULL;
+ *   W1 (and Wu for TP_ACT_SWIGLU) [d, k], b1 [k] or NULL (not with SwiGLU),
+ *   W2 [k, d], b2 [d] fp32 or NULL.
+ * dt must be TP_BF16; dh 64 or 128; Hq, Hkv and k divisible by p and Hq by
+ * Hkv (TP_ERR_NOT_DIVISIBLE); 8 <= d <= 16384, a multiple of 8.  Workspace:
+ * at least tp_block_workspace_bytes (the shared layout: zeroed counter area,
+ * then scratch; it holds A, the shard's QKV and attention output, the p
+ * hidden shards and p fp32 [T, d] partials).  Nothing is launched on error.
+ */
+tp_status tp_block_simulated(tp_dtype dt, tp_act act, int64_t nseq, int64_t S, int64_t d,
+                             int32_t Hq, int32_t Hkv, int64_t dh, int64_t k, int32_t p,
+                             int32_t causal, float eps, const float *X, int64_t ldx,
+                             const float *ln1_g, const float *ln1_b, const void *Wqkv,
+                             int64_t ldwqkv, const void *bqkv, const void *WO, int64_t ldwo,
+                             const float *bO, const float *ln2_g, const float *ln2_b,
+                             const void *W1, int64_t ldw1, const void *Wu, int64_t ldwu,
+                             const void *b1, const void *W2, int64_t ldw2, const float *b2,
+                             float *Out, int64_t ldout, void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of workspace tp_block_simulated needs for these sizes (0 for invalid
+ * arguments or no tokens). */
+size_t tp_block_workspace_bytes(tp_dtype dt, tp_act act, int64_t nseq, int64_t S, int64_t d,
+                                int32_t Hq, int32_t Hkv, int64_t dh, int64_t k, int32_t p);
 
 /* Shard bookkeeping on the host: shard i of p of a dimension of size k owns
  * [*c0, *c0 + *s) with s = k/p and c0 = i*s (Day 41 post, "Simulating column

@@ -1,8 +1,9 @@
 """MI355X-native tensor-parallel MLP shard (column-parallel linear + local
 GeLU/SwiGLU, row-parallel linear to an fp32 partial, on-device partial sum),
-the shard's backward pass, and the attention projections of one head shard
-(QKV column-parallel by heads; the output projection is the row-parallel
-linear).
+the shard's backward pass, the attention of one head shard (QKV
+column-parallel by heads, the attention core, the output projection as the
+row-parallel linear), and a whole pre-LayerNorm transformer block of p shards
+with its two reductions.
 
 This package is a thin ctypes binding over ``libtpmlp.so`` (declared in
 ``include/tpmlp.h``, with a measurement aid in ``include/tpmlp_calib.h``): it
@@ -22,6 +23,8 @@ from ._binding import (  # noqa: F401
     tp_abi_version,
     tp_attention,
     tp_backward_workspace_bytes,
+    tp_block_simulated,
+    tp_block_workspace_bytes,
     tp_calib_mfma_bf16,
     tp_col_linear,
     tp_col_linear_train,
@@ -31,6 +34,7 @@ from ._binding import (  # noqa: F401
     tp_partial_sum,
     tp_qkv_linear,
     tp_qkv_workspace_bytes,
+    tp_residual_layernorm,
     tp_row_linear,
     tp_shard_bounds,
     tp_workspace_bytes,
@@ -39,8 +43,9 @@ from ._binding import (  # noqa: F401
 
 __all__ = [
     "ACT", "DTYPE", "TpError", "library", "library_path", "tp_abi_version", "tp_attention",
-    "tp_backward_workspace_bytes", "tp_calib_mfma_bf16", "tp_col_linear", "tp_col_linear_train",
+    "tp_backward_workspace_bytes", "tp_block_simulated", "tp_block_workspace_bytes",
+    "tp_calib_mfma_bf16", "tp_col_linear", "tp_col_linear_train",
     "tp_mlp_shard", "tp_mlp_shard_backward", "tp_mlp_simulated", "tp_partial_sum", "tp_qkv_linear",
-    "tp_qkv_workspace_bytes", "tp_row_linear", "tp_shard_bounds", "tp_workspace_bytes",
+    "tp_qkv_workspace_bytes", "tp_residual_layernorm", "tp_row_linear", "tp_shard_bounds", "tp_workspace_bytes",
     "workspace",
 ]

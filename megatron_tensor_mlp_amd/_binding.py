@@ -80,9 +80,18 @@ def library():
                                  vp, i64, vp]
     lib.tp_backward_workspace_bytes.argtypes = [ci, ci, i64, i64, i64, i32, i32]
     lib.tp_backward_workspace_bytes.restype = sz
+    cf = ctypes.c_float
+    lib.tp_residual_layernorm.argtypes = [i64, i64, i32, ctypes.POINTER(vp), i64, vp, vp, i64, vp,
+                                          i64, vp, vp, cf, vp, i64, vp]
+    lib.tp_block_simulated.argtypes = [ci, ci, i64, i64, i64, i32, i32, i64, i64, i32, i32, cf,
+                                       vp, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp, vp, vp, i64,
+                                       vp, i64, vp, vp, i64, vp, vp, i64, vp, sz, vp]
+    lib.tp_block_workspace_bytes.argtypes = [ci, ci, i64, i64, i64, i32, i32, i64, i64, i32]
+    lib.tp_block_workspace_bytes.restype = sz
     for name in ("tp_col_linear", "tp_row_linear", "tp_mlp_shard", "tp_partial_sum",
                  "tp_mlp_simulated", "tp_shard_bounds", "tp_calib_mfma_bf16", "tp_qkv_linear",
-                 "tp_col_linear_train", "tp_mlp_shard_backward", "tp_attention"):
+                 "tp_col_linear_train", "tp_mlp_shard_backward", "tp_attention",
+                 "tp_residual_layernorm", "tp_block_simulated"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -378,3 +387,87 @@ def tp_attention(Q, K, V, O, Hq: int, Hkv: int, dh: int, S: int | None = None, c
     _check(library().tp_attention(_dt(Q), nseq, S, Hq, Hkv, dh, 1 if causal else 0, _ptr(Q), ldq,
                                   _ptr(K), ldk, _ptr(V), ldv, _ptr(O), ldo, _stream(stream)))
     return O
+
+
+def _vec(t, n: int, name: str):
+    """A 1-D fp32 parameter vector of at least n elements, or None."""
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{name} must be a contiguous fp32 vector of at least {n} elements")
+    return t
+
+
+def tp_residual_layernorm(parts=(), X=None, A=None, bias=None, R=None, gamma=None, beta=None,
+                          eps: float = 1e-5, stream=None):
+    """x = (((parts[0] + ...) + bias) + R) in fp32, left to right; X <- x (fp32 [T, d]);
+    A <- LayerNorm(x) * gamma + beta (bf16 [T, d]).  Returns (X, A)."""
+    ref = next((t for t in (list(parts) + [R, X, A]) if t is not None), None)
+    if ref is None:
+        raise ValueError("no tensor to take the shape from")
+    T, d = ref.shape
+    p = len(parts)
+    ldp = _ld(parts[0], T, d, "parts[0]") if p else d
+    for q, t in enumerate(parts):
+        if t.dtype != torch.float32 or _ld(t, T, d, f"parts[{q}]") != ldp:
+            raise ValueError("partials must be fp32 and share one leading dimension")
+    ldr = _ld(R, T, d, "R") if R is not None else d
+    ldx = _ld(X, T, d, "X") if X is not None else d
+    lda = _ld(A, T, d, "A") if A is not None else d
+    for name, t in (("R", R), ("X", X)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be fp32")
+    if A is not None and A.dtype != torch.bfloat16:
+        raise ValueError("A must be bf16")
+    _vec(bias, d, "bias"), _vec(gamma, d, "gamma"), _vec(beta, d, "beta")
+    arr = (ctypes.c_void_p * max(p, 1))(*[t.data_ptr() for t in parts])
+    _check(library().tp_residual_layernorm(T, d, p, arr, ldp, _ptr(bias), _ptr(R), ldr, _ptr(X),
+                                           ldx, _ptr(gamma), _ptr(beta), float(eps), _ptr(A), lda,
+                                           _stream(stream)))
+    return X, A
+
+
+def tp_block_workspace_bytes(dtype, act, nseq: int, S: int, d: int, Hq: int, Hkv: int, dh: int,
+                             k: int, p: int) -> int:
+    dt = DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return library().tp_block_workspace_bytes(dt, _act(act), nseq, S, d, Hq, Hkv, dh, k, p)
+
+
+def tp_block_simulated(X, Hq: int, Hkv: int, dh: int, p: int, ln1, Wqkv, WO, ln2, W1, W2, Out,
+                       S=None, causal=True, eps: float = 1e-5, act="gelu_tanh", bqkv=None,
+                       bO=None, Wu=None, b1=None, b2=None, ws=None, stream=None):
+    """One pre-LayerNorm transformer block of p tensor-parallel shards on this device.
+    X, Out fp32 [T, d] (T = nseq * S); ln1, ln2 = (gamma, beta) fp32 [d]; Wqkv, WO, W1,
+    (Wu,) W2 bf16 full matrices; bO, b2 fp32 [d] or None; bqkv, b1 bf16 or None."""
+    T, d = X.shape
+    S = T if S is None else S
+    if S <= 0 or T % S:
+        raise ValueError("T must be a whole number of sequences of S tokens")
+    nseq = T // S
+    k = W1.shape[1]
+    a = _act(act)
+    ncol = (Hq + 2 * Hkv) * dh
+    if X.dtype != torch.float32 or Out.dtype != torch.float32:
+        raise ValueError("X and Out must be fp32")
+    ldx = _ld(X, T, d, "X")
+    ldout = _ld(Out, T, d, "Out")
+    ldq = _ld(Wqkv, d, ncol, "Wqkv")
+    ldo = _ld(WO, Hq * dh, d, "WO")
+    ldw1 = _ld(W1, d, k, "W1")
+    ldwu = _ld(Wu, d, k, "Wu") if Wu is not None else 0
+    ldw2 = _ld(W2, k, d, "W2")
+    for name, t, n in (("ln1 gamma", ln1[0], d), ("ln1 beta", ln1[1], d), ("ln2 gamma", ln2[0], d),
+                       ("ln2 beta", ln2[1], d), ("bO", bO, d), ("b2", b2, d)):
+        _vec(t, n, name)
+    if bqkv is not None and bqkv.numel() < ncol:
+        raise ValueError("bqkv is shorter than (Hq + 2 Hkv) dh")
+    if b1 is not None and b1.numel() < k:
+        raise ValueError("b1 is shorter than k")
+    need = tp_block_workspace_bytes(Wqkv.dtype, a, nseq, S, d, Hq, Hkv, dh, k, p)
+    wsp, wsn = _ws_args(ws, need, X.device)
+    _check(library().tp_block_simulated(
+        _dt(Wqkv), a, nseq, S, d, Hq, Hkv, dh, k, p, 1 if causal else 0, float(eps), _ptr(X), ldx,
+        _ptr(ln1[0]), _ptr(ln1[1]), _ptr(Wqkv), ldq, _ptr(bqkv), _ptr(WO), ldo, _ptr(bO),
+        _ptr(ln2[0]), _ptr(ln2[1]), _ptr(W1), ldw1, _ptr(Wu), ldwu, _ptr(b1), _ptr(W2), ldw2,
+        _ptr(b2), _ptr(Out), ldout, wsp, wsn, _stream(stream)))
+    return Out

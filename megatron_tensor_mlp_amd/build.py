@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libtpmlp.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "gemm_tiled.hip", "gemm_decode.hip", "gemm_f32.hip", "partial_sum.hip",
-           "calib.hip", "colsum.hip", "attention.hip"]
+           "calib.hip", "colsum.hip", "attention.hip", "residual_ln.hip"]
 
 # Packed fp32 VALU ops are disabled for all device code; hipcc's host pass
 # warns that it does not know the feature, which is harmless.

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "../../include/tpmlp.h"
 #include "../../include/tpmlp_calib.h"
@@ -558,6 +559,112 @@ QkvCall make_qkv(tp_dtype dt, int64_t T, int64_t d, int32_t Hq, int32_t Hkv, int
   return c;
 }
 
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of the simulated transformer block, in byte offsets: the counter
+// area (and the few-token GEMMs' scratch) first, as for every entry point,
+// then the block's own buffers.
+struct BlockLayout {
+  size_t a, qkv, o, y, x1, parts, total;
+};
+BlockLayout block_layout(size_t gemm_ws, int64_t T, int64_t d, int64_t nqkv, int64_t qw, int64_t s,
+                         int32_t p) {
+  BlockLayout L;
+  size_t off = up256(max_sz(gemm_ws, kWsCounterBytes));
+  L.a = off;
+  off += up256((size_t)(T * d) * 2);
+  L.qkv = off;
+  off += up256((size_t)(T * nqkv) * 2);
+  L.o = off;
+  off += up256((size_t)(T * qw) * 2);
+  L.y = off;
+  off += up256((size_t)p * (size_t)(T * s) * 2);
+  L.x1 = off;
+  off += up256((size_t)(T * d) * 4);
+  L.parts = off;
+  off += up256((size_t)p * (size_t)(T * d) * 4);
+  L.total = off;
+  return L;
+}
+
+tp_status run_rownorm(const RowNormArgs &a, hipStream_t st) {
+  const hipError_t e = launch_residual_ln(a, st);
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return TP_OK;
+}
+
+tp_status check_eps(float eps) {
+  if (!(eps >= 0.0f) || !__builtin_isfinite(eps))
+    return fail(TP_ERR_BAD_SHAPE, "eps = %g must be finite and >= 0", (double)eps);
+  return TP_OK;
+}
+
+// The GEMM descriptors of the simulated block and the workspace they and the
+// block's buffers need; `ws` may be NULL for a size query.
+struct BlockPlan {
+  tp_status st;
+  int64_t T, qw, kw, nqkv, s;
+  BlockLayout L;
+  size_t gemm_ws;
+};
+BlockPlan plan_block(tp_dtype dt, tp_act act, int64_t nseq, int64_t S, int64_t d, int32_t Hq,
+                     int32_t Hkv, int64_t dh, int64_t k, int32_t p) {
+  BlockPlan P{};
+  P.st = TP_OK;
+  auto bad = [&](tp_status st) {
+    P.st = st;
+    return P;
+  };
+  if (dt != TP_BF16)
+    return bad(fail(TP_ERR_BAD_DTYPE, "the transformer block runs in bf16 only (dtype %d)",
+                    (int)dt));
+  if (check_dtype_act(dt, act) != TP_OK) return bad(TP_ERR_BAD_ACT);
+  if (nseq < 0 || S < 0)
+    return bad(fail(TP_ERR_BAD_SHAPE, "nseq = %lld and S = %lld must be >= 0", (long long)nseq,
+                    (long long)S));
+  if (d < 8 || d > kRowNormMaxD || d % 8)
+    return bad(fail(d % 8 ? TP_ERR_MISALIGNED : TP_ERR_BAD_SHAPE,
+                    "d = %lld must be a multiple of 8 in [8, %lld]", (long long)d,
+                    (long long)kRowNormMaxD));
+  if (Hq < 1 || Hkv < 1)
+    return bad(fail(TP_ERR_BAD_SHAPE, "Hq = %d and Hkv = %d must be >= 1", Hq, Hkv));
+  if (Hq % Hkv)
+    return bad(fail(TP_ERR_NOT_DIVISIBLE, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv));
+  if (dh != 64 && dh != 128)
+    return bad(fail(TP_ERR_BAD_SHAPE, "head width dh = %lld: 64 and 128 are supported",
+                    (long long)dh));
+  if (p < 1 || p > TP_MAX_SHARDS)
+    return bad(fail(TP_ERR_BAD_SHARD, "p = %d outside [1, %d]", p, TP_MAX_SHARDS));
+  if (Hq % p || Hkv % p || k < 1 || k % p)
+    return bad(fail(TP_ERR_NOT_DIVISIBLE, "Hq = %d, Hkv = %d and k = %lld must be divisible by p = %d",
+                    Hq, Hkv, (long long)k, p));
+  if (nseq > 0 && S > (int64_t(1) << 40) / nseq)
+    return bad(fail(TP_ERR_BAD_SHAPE, "nseq * S is too large"));
+  P.T = nseq * S;
+  P.qw = (int64_t)Hq * dh / p;
+  P.kw = (int64_t)Hkv * dh / p;
+  P.nqkv = P.qw + 2 * P.kw;
+  P.s = k / p;
+  // Scratch of the few-token GEMMs (zero with more than 64 tokens): the
+  // largest of the block's four GEMM shapes; buffers are placeholders here.
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  const int64_t T = P.T;
+  const QkvCall qc = make_qkv(dt, T, d, Hq, Hkv, dh, 0, p, dummy, d, dummy,
+                              ((int64_t)Hq + 2 * (int64_t)Hkv) * dh, nullptr, (void *)dummy,
+                              P.nqkv);
+  const RowCall ro = make_row(dt, T, d, (int64_t)Hq * dh, 0, p, dummy, P.qw, dummy, d,
+                              (float *)dummy, d);
+  const ColCall c = make_col(dt, act, T, d, k, 0, p, dummy, d, dummy, k, dummy, k, nullptr,
+                             (void *)dummy, P.s);
+  const RowCall r = make_row(dt, T, d, k, 0, p, dummy, P.s, dummy, d, (float *)dummy, d);
+  size_t g = gemm_ws_bytes(dt, qkv_gemm(qc));
+  g = max_sz(g, gemm_ws_bytes(dt, row_gemm(ro, 1, 0, 0)));
+  g = max_sz(g, gemm_ws_bytes(dt, col_gemm(c, p, T * P.s)));
+  g = max_sz(g, gemm_ws_bytes(dt, row_gemm(r, p, T * P.s, T * d)));
+  P.gemm_ws = g;
+  P.L = block_layout(g, T, d, P.nqkv, P.qw, P.s, p);
+  return P;
+}
 }  // namespace
 
 extern "C" {
@@ -852,6 +959,215 @@ size_t tp_qkv_workspace_bytes(tp_dtype dt, int64_t T, int64_t d, int32_t Hq, int
   g_msg = keep;
   if (st != TP_OK) return 0;
   return gemm_ws_bytes(dt, qkv_gemm(c));
+}
+
+tp_status tp_residual_layernorm(int64_t T, int64_t d, int32_t p, const float *const *parts,
+                                int64_t ldp, const float *bias, const float *R, int64_t ldr,
+                                float *X, int64_t ldx, const float *gamma, const float *beta,
+                                float eps, void *A, int64_t lda, void *stream) {
+  if (T < 0) return fail(TP_ERR_BAD_SHAPE, "T = %lld < 0", (long long)T);
+  if (d < 1 || d > kRowNormMaxD)
+    return fail(TP_ERR_BAD_SHAPE, "d = %lld outside [1, %lld]", (long long)d,
+                (long long)kRowNormMaxD);
+  if (d % 8) return fail(TP_ERR_MISALIGNED, "d = %lld is not a multiple of 8", (long long)d);
+  if (p < 0 || p > TP_MAX_SHARDS)
+    return fail(TP_ERR_BAD_SHARD, "p = %d outside [0, %d]", p, TP_MAX_SHARDS);
+  if (p > 0 && !parts) return fail(TP_ERR_NULL_POINTER, "parts is NULL");
+  TRY(check_eps(eps));
+  if (p > 0) TRY(check_ld("ldp", ldp, d, TP_F32));
+  if (R) TRY(check_ld("ldr", ldr, d, TP_F32));
+  if (X) TRY(check_ld("ldx", ldx, d, TP_F32));
+  if (A) TRY(check_ld("lda", lda, d, TP_BF16));
+  if (T == 0) return ok();  // nothing is read or written; buffers may be NULL
+  if (p == 0 && !bias && !R)
+    return fail(TP_ERR_BAD_SHAPE, "nothing to add: no partials, no bias and no residual");
+  if (!X && !A) return fail(TP_ERR_BAD_SHAPE, "no output: X and A are both NULL");
+  if ((gamma != nullptr) != (A != nullptr) || (gamma != nullptr) != (beta != nullptr))
+    return fail(TP_ERR_NULL_POINTER, "gamma, beta and A are given together or not at all");
+  RowNormArgs a{};
+  for (int q = 0; q < p; ++q) {
+    char name[32];
+    snprintf(name, sizeof name, "parts[%d]", q);
+    TRY(check_ptr(name, parts[q]));
+    a.parts[q] = parts[q];
+  }
+  if (bias) TRY(check_ptr("bias", bias));
+  if (R) TRY(check_ptr("R", R));
+  if (X) TRY(check_ptr("X", X));
+  if (A) {
+    TRY(check_ptr("gamma", gamma));
+    TRY(check_ptr("beta", beta));
+    TRY(check_ptr("A", A));
+  }
+  a.p = p;
+  a.T = T;
+  a.d = d;
+  a.ldp = ldp;
+  a.bias = bias;
+  a.R = R;
+  a.ldr = ldr;
+  a.X = X;
+  a.ldx = ldx;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.eps = eps;
+  a.A = A;
+  a.lda = lda;
+  TRY(run_rownorm(a, (hipStream_t)stream));
+  return ok();
+}
+
+size_t tp_block_workspace_bytes(tp_dtype dt, tp_act act, int64_t nseq, int64_t S, int64_t d,
+                                int32_t Hq, int32_t Hkv, int64_t dh, int64_t k, int32_t p) {
+  const std::string keep = g_msg;  // a size query leaves the last error message alone
+  const BlockPlan P = plan_block(dt, act, nseq, S, d, Hq, Hkv, dh, k, p);
+  g_msg = keep;
+  if (P.st != TP_OK || P.T == 0) return 0;
+  return P.L.total;
+}
+
+tp_status tp_block_simulated(tp_dtype dt, tp_act act, int64_t nseq, int64_t S, int64_t d,
+                             int32_t Hq, int32_t Hkv, int64_t dh, int64_t k, int32_t p,
+                             int32_t causal, float eps, const float *X, int64_t ldx,
+                             const float *ln1_g, const float *ln1_b, const void *Wqkv,
+                             int64_t ldwqkv, const void *bqkv, const void *WO, int64_t ldwo,
+                             const float *bO, const float *ln2_g, const float *ln2_b,
+                             const void *W1, int64_t ldw1, const void *Wu, int64_t ldwu,
+                             const void *b1, const void *W2, int64_t ldw2, const float *b2,
+                             float *Out, int64_t ldout, void *ws, size_t ws_bytes, void *stream) {
+  const BlockPlan P = plan_block(dt, act, nseq, S, d, Hq, Hkv, dh, k, p);
+  if (P.st != TP_OK) return P.st;
+  const int64_t T = P.T;
+  TRY(check_eps(eps));
+  TRY(check_ptr("ln1_gamma", ln1_g));
+  TRY(check_ptr("ln1_beta", ln1_b));
+  TRY(check_ptr("ln2_gamma", ln2_g));
+  TRY(check_ptr("ln2_beta", ln2_b));
+  if (bO) TRY(check_ptr("bO", bO));
+  if (b2) TRY(check_ptr("b2", b2));
+  TRY(check_ld("ldx", ldx, d, TP_F32));
+  TRY(check_ld("ldout", ldout, d, TP_F32));
+  if (T > 0) {
+    TRY(check_ptr("X", X));
+    TRY(check_ptr("Out", Out));
+  }
+  // The GEMMs of shard 0 stand for all shards (the others differ by block
+  // offsets only); their checks run on the real buffers once the workspace is
+  // known, or on placeholders when there are no tokens.
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  const BlockLayout &L = P.L;
+  if (T > 0) TRY(check_ws(L.total, ws, ws_bytes));
+  char *w = T > 0 ? (char *)ws : (char *)dummy;
+  QkvCall qc = make_qkv(dt, T, d, Hq, Hkv, dh, 0, p, dummy, d, Wqkv, ldwqkv, bqkv,
+                        (void *)dummy, P.nqkv);
+  ColCall c = make_col(dt, act, T, d, k, 0, p, dummy, d, W1, ldw1, Wu, ldwu, b1, (void *)dummy,
+                       P.s);
+  RowCall ro = make_row(dt, T, d, (int64_t)Hq * dh, 0, p, dummy, P.qw, WO, ldwo, (float *)dummy, d);
+  RowCall r = make_row(dt, T, d, k, 0, p, dummy, P.s, W2, ldw2, (float *)dummy, d);
+  if (T > 0) {
+    qc.X = w + L.a;
+    qc.QKV = w + L.qkv;
+    c.X = w + L.a;
+    c.Y = w + L.y;
+    ro.Y = w + L.o;
+    ro.Z = (float *)(w + L.parts);
+    r.Y = w + L.y;
+    r.Z = (float *)(w + L.parts);
+  }
+  TRY(validate_qkv(qc));
+  TRY(validate_col(c));
+  TRY(validate_row(ro));
+  TRY(validate_row(r));
+  if (T == 0) return ok();
+  const hipStream_t st = (hipStream_t)stream;
+  float *parts = (float *)(w + L.parts);
+  float *X1 = (float *)(w + L.x1);
+  AttnArgs at{};
+  at.nseq = nseq;
+  at.S = S;
+  at.Hq = Hq / p;
+  at.Hkv = Hkv / p;
+  at.dh = (int)dh;
+  at.causal = causal ? 1 : 0;
+  at.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)dh));
+  at.Q = w + L.qkv;
+  at.K = w + L.qkv + P.qw * 2;
+  at.V = w + L.qkv + (P.qw + P.kw) * 2;
+  at.O = w + L.o;
+  at.ldq = at.ldk = at.ldv = P.nqkv;
+  at.ldo = P.qw;
+  if (!attention_supported(at))
+    return fail(TP_ERR_BAD_SHAPE, "attention shape beyond the kernel's range");
+  std::vector<GemmArgs> qg(p), og(p);
+  for (int32_t i = 0; i < p; ++i) {
+    QkvCall qi = qc;
+    qi.i = i;
+    qg[i] = qkv_gemm(qi);
+    RowCall ri = ro;
+    ri.i = i;
+    ri.Z = parts + (int64_t)i * T * d;
+    og[i] = row_gemm(ri, 1, 0, 0);
+    TRY(check_gemm(dt, qg[i]));
+    TRY(check_gemm(dt, og[i]));
+  }
+  const GemmArgs cg = col_gemm(c, p, T * P.s), rg = row_gemm(r, p, T * P.s, T * d);
+  TRY(check_gemm(dt, cg));
+  TRY(check_gemm(dt, rg));
+
+  // A = LN1(X)
+  RowNormArgs n1{};
+  n1.p = 0;
+  n1.T = T;
+  n1.d = d;
+  n1.R = X;
+  n1.ldr = ldx;
+  n1.gamma = ln1_g;
+  n1.beta = ln1_b;
+  n1.eps = eps;
+  n1.A = w + L.a;
+  n1.lda = d;
+  TRY(run_rownorm(n1, st));
+  // Attention, shard by shard: QKV_i, the core on its heads, the W_O row block.
+  for (int32_t i = 0; i < p; ++i) {
+    TRY(run_gemm(dt, qg[i], ws, st));
+    const hipError_t e = launch_attention(at, st);
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    TRY(run_gemm(dt, og[i], ws, st));
+  }
+  // X1 = sum of the partials + bO + X;  A = LN2(X1)
+  RowNormArgs n2{};
+  for (int32_t i = 0; i < p; ++i) n2.parts[i] = parts + (int64_t)i * T * d;
+  n2.p = p;
+  n2.T = T;
+  n2.d = d;
+  n2.ldp = d;
+  n2.bias = bO;
+  n2.R = X;
+  n2.ldr = ldx;
+  n2.X = X1;
+  n2.ldx = d;
+  n2.gamma = ln2_g;
+  n2.beta = ln2_b;
+  n2.eps = eps;
+  n2.A = w + L.a;
+  n2.lda = d;
+  TRY(run_rownorm(n2, st));
+  // The FFN of all p shards (grouped launches), then Out = sum + b2 + X1.
+  TRY(run_gemm(dt, cg, ws, st));
+  TRY(run_gemm(dt, rg, ws, st));
+  RowNormArgs n3{};
+  for (int32_t i = 0; i < p; ++i) n3.parts[i] = parts + (int64_t)i * T * d;
+  n3.p = p;
+  n3.T = T;
+  n3.d = d;
+  n3.ldp = d;
+  n3.bias = b2;
+  n3.R = X1;
+  n3.ldr = d;
+  n3.X = Out;
+  n3.ldx = ldout;
+  TRY(run_rownorm(n3, st));
+  return ok();
 }
 
 tp_status tp_shard_bounds(int64_t k, int32_t i, int32_t p, int64_t *c0, int64_t *s) {

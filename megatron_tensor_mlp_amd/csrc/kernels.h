@@ -131,4 +131,24 @@ struct PartSumArgs {
 };
 hipError_t launch_partial_sum(const PartSumArgs &a, hipStream_t s);
 
+// Row step of a transformer block: x = (((parts[0] + ...) + bias) + R) in
+// fp32 (absent terms skipped), written to X if given, and LayerNorm(x) in
+// bf16 to A if gamma is given.  One row per workgroup, held in registers.
+constexpr int64_t kRowNormMaxD = 16384;
+struct RowNormArgs {
+  const float *parts[kMaxParts];
+  int p;
+  int64_t T, d, ldp;
+  const float *bias;
+  const float *R;
+  int64_t ldr;
+  float *X;
+  int64_t ldx;
+  const float *gamma, *beta;
+  float eps;
+  void *A;
+  int64_t lda;
+};
+hipError_t launch_residual_ln(const RowNormArgs &a, hipStream_t s);
+
 }  // namespace tpmlp

@@ -201,3 +201,45 @@ def attn_output(T: int, width: int, seed: int = 48):
     """A stand-in for one shard's attention output [T, width], bf16 N(0, 1): the
     input of the row-parallel output projection."""
     return gaussian_bf16((T, width), seed)
+
+
+def layernorm_params(d: int, seed: int, std: float = 0.1):
+    """LayerNorm scale and shift [d], fp32 CPU tensors: 1 + N(0, std^2) from seed, and
+    N(0, std^2) from seed + 1."""
+    import torch
+
+    g = 1.0 + gaussian_f32((d,), seed, std)
+    b = gaussian_f32((d,), seed + 1, std)
+    return torch.from_numpy(g.astype(np.float32)), torch.from_numpy(b)
+
+
+def block_case(T: int, d: int, Hq: int, Hkv: int, dh: int, k: int, act: str, seed: int,
+               bias: bool = True, full_weights: bool = False):
+    """Inputs of one pre-LayerNorm transformer block (CPU tensors): the residual stream
+    X [T, d] fp32 N(0, 1); the two LayerNorms' (scale, shift); the packed QKV weight
+    [d, (Hq + 2 Hkv) dh] and the output projection [Hq dh, d]; the FFN weights W1 (gate)
+    and Wu [d, k] (Wu for SwiGLU only) and W2 [k, d]; weights bf16 N(0, 0.02^2).
+    Biases (if `bias`): bqkv and b1 bf16 N(0, 0.02^2), bO and b2 fp32 N(0, 0.02^2) (no
+    b1 with SwiGLU).  With full_weights the weights are the Llama-70B draws (attention
+    seeds 46/47, FFN seeds 43-45) instead of seed-derived ones."""
+    import torch
+
+    X = torch.from_numpy(gaussian_f32((T, d), seed))
+    if full_weights:
+        Wqkv, WO = attn_weights(d, Hq, Hkv, dh)
+        W1, Wu, W2 = llama_full_weights(d, k)
+        Wu = Wu if act == "swiglu" else None
+    else:
+        Wqkv, WO = attn_weights(d, Hq, Hkv, dh, seed + 1)
+        W1 = gaussian_bf16((d, k), seed + 3, WEIGHT_STD)
+        Wu = gaussian_bf16((d, k), seed + 4, WEIGHT_STD) if act == "swiglu" else None
+        W2 = gaussian_bf16((k, d), seed + 5, WEIGHT_STD)
+    case = dict(X=X, ln1=layernorm_params(d, seed + 6), ln2=layernorm_params(d, seed + 8),
+                Wqkv=Wqkv, WO=WO, W1=W1, Wu=Wu, W2=W2)
+    if bias:
+        case["bqkv"] = gaussian_bf16(((Hq + 2 * Hkv) * dh,), seed + 10, WEIGHT_STD)
+        case["bO"] = torch.from_numpy(gaussian_f32((d,), seed + 11, WEIGHT_STD))
+        case["b2"] = torch.from_numpy(gaussian_f32((d,), seed + 12, WEIGHT_STD))
+        if act != "swiglu":
+            case["b1"] = gaussian_bf16((k,), seed + 13, WEIGHT_STD)
+    return case

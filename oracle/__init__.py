@@ -82,7 +82,10 @@ def _load():
         cd = ctypes.c_double
         lib.oracle_layernorm_f64.argtypes = [i64, i64, vp, vp, vp, cd, vp]
         lib.oracle_block_f64.argtypes = [i64, i64, i64, i32, i32, i64, i64, ci, ci, cd, vp, vp, vp,
-                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp]
+                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, i64, vp,
+                                         vp]
+        lib.oracle_round_bf16_f64.argtypes = [i64, vp, vp]
+        lib.oracle_round_bf16_f64.restype = None
         for name in ("oracle_col_shard_f64", "oracle_row_shard_f64", "oracle_partial_sum_f64",
                      "oracle_mlp_unsharded_f64", "oracle_linear_f32", "oracle_col_shard_f32",
                      "oracle_partial_sum_f32", "oracle_num_threads", "oracle_qkv_shard_f64",
@@ -304,11 +307,13 @@ def layernorm(X, gamma, beta, eps=1e-5):
 
 
 def block(X, Hq, Hkv, dh, act, ln1, Wqkv, WO, ln2, W1, W2, S=None, causal=True, eps=1e-5,
-          bqkv=None, bO=None, Wu=None, b1=None, b2=None, rows=None):
+          bqkv=None, bO=None, Wu=None, b1=None, b2=None, rows=None, mirror=False):
     """One pre-LayerNorm transformer block in fp64, unsharded: X [T, d] (sequences of
     S tokens, default one of T); ln1 and ln2 are (gamma, beta) pairs; Wqkv [d, (Hq +
     2 Hkv) dh], WO [Hq dh, d], W1 (and Wu) [d, k], W2 [k, d].  Returns the block output
-    for the token rows listed in `rows` (default all), [len(rows), d]."""
+    for the token rows listed in `rows` (default all), [len(rows), d].  mirror=True is
+    a diagnostic: the activations a bf16 implementation stores (the LayerNorm outputs,
+    QKV, the attention output, the FFN hidden activation) are rounded to bf16."""
     lib = _load()
     X = _c(X, np.float64)
     T, d = X.shape
@@ -323,6 +328,15 @@ def block(X, Hq, Hkv, dh, act, ln1, Wqkv, WO, ln2, W1, W2, S=None, causal=True, 
     n = T if r is None else len(r)
     Out = np.empty((n, d), dtype=np.float64)
     _check(lib.oracle_block_f64(T // S if S else 0, S, d, Hq, Hkv, dh, k, 1 if causal else 0,
-                                _act(act), float(eps), _p(X), *[_p(a) for a in args], n,
-                                _p(r), _p(Out)), "block")
+                                _act(act), float(eps), _p(X), *[_p(a) for a in args],
+                                1 if mirror else 0, n, _p(r), _p(Out)), "block")
     return Out
+
+
+def round_bf16(x):
+    """x rounded to fp32, then to the nearest bf16 (ties to even), as fp64."""
+    lib = _load()
+    x = _c(x, np.float64)
+    y = np.empty_like(x)
+    lib.oracle_round_bf16_f64(x.size, _p(x), _p(y))
+    return y

@@ -624,6 +624,28 @@ int oracle_layernorm_f64(int64_t T, int64_t d, const double *X, const double *ga
 }
 
 /*
+ * Rounding to bf16 for the block's mirror mode (a diagnostic, off by
+ * default): the value is rounded to fp32 (the precision the GPU's
+ * accumulators hold), then to the nearest bf16 with ties to even -- add half
+ * of the dropped 16 bits' range, less one, plus the lowest kept bit, and drop
+ * those bits.  Non-finite values pass through.
+ */
+static double bf16_round(double x) {
+  float f = (float)x;
+  if (!isfinite(f)) return f;
+  uint32_t b;
+  memcpy(&b, &f, 4);
+  b += 0x7fffu + ((b >> 16) & 1u);
+  b &= 0xffff0000u;
+  memcpy(&f, &b, 4);
+  return (double)f;
+}
+
+void oracle_round_bf16_f64(int64_t n, const double *x, double *y) {
+  for (int64_t e = 0; e < n; ++e) y[e] = bf16_round(x[e]);
+}
+
+/*
  * One pre-LayerNorm transformer block, unsharded, fp64, in the order of
  * "Building GPT from Scratch, Part 9", section "Communication Pattern per
  * Transformer Block" (LayerNorm, attention, residual add, LayerNorm, FFN,
@@ -639,6 +661,9 @@ int oracle_layernorm_f64(int64_t T, int64_t d, const double *X, const double *ga
  * (keys come from all of them); the FFN half only for the nrows tokens listed
  * in rows (rows == NULL: all T, in order).  Out [nrows, d].  bqkv, bO, b1 and
  * b2 may be NULL (no bias); Wu only for act = OR_ACT_SWIGLU.
+ * mirror != 0 (diagnostic only) rounds to bf16 the activations a bf16
+ * implementation stores: A, QKV, O, B and the FFN hidden activation; the
+ * residual stream and everything else stay fp64.
  */
 int oracle_block_f64(int64_t nseq, int64_t S, int64_t d, int32_t Hq, int32_t Hkv, int64_t dh,
                      int64_t k, int causal, int act, double eps, const double *X,
@@ -646,7 +671,7 @@ int oracle_block_f64(int64_t nseq, int64_t S, int64_t d, int32_t Hq, int32_t Hkv
                      const double *bqkv, const double *WO, const double *bO,
                      const double *ln2_g, const double *ln2_b, const double *W1,
                      const double *Wu, const double *b1, const double *W2, const double *b2,
-                     int64_t nrows, const int64_t *rows, double *Out) {
+                     int mirror, int64_t nrows, const int64_t *rows, double *Out) {
   if (nseq < 0 || S < 0 || d < 1 || Hq < 1 || Hkv < 1 || dh < 1 || k < 1 || Hq % Hkv) return -1;
   if (act == OR_ACT_SWIGLU && Wu == NULL) return -1;
   const int64_t T = nseq * S, ncol = ((int64_t)Hq + 2 * (int64_t)Hkv) * dh;
@@ -666,6 +691,8 @@ int oracle_block_f64(int64_t nseq, int64_t S, int64_t d, int32_t Hq, int32_t Hkv
   int rc = -1;
   if (!A || !QKV || !Q || !K || !V || !O || !X1 || !B || !Z) goto out;
   if (oracle_layernorm_f64(T, d, X, ln1_g, ln1_b, eps, A)) goto out;
+  if (mirror)
+    for (int64_t e = 0; e < T * d; ++e) A[e] = bf16_round(A[e]);
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t) {
     double *q = QKV + t * ncol;
@@ -677,11 +704,15 @@ int oracle_block_f64(int64_t nseq, int64_t S, int64_t d, int32_t Hq, int32_t Hkv
     }
     if (bqkv)
       for (int64_t n = 0; n < ncol; ++n) q[n] += bqkv[n];
+    if (mirror)
+      for (int64_t n = 0; n < ncol; ++n) q[n] = bf16_round(q[n]);
     memcpy(Q + t * qw, q, sizeof(double) * (size_t)qw);
     memcpy(K + t * kw, q + qw, sizeof(double) * (size_t)kw);
     memcpy(V + t * kw, q + qw + kw, sizeof(double) * (size_t)kw);
   }
   if (oracle_attention_f64(nseq, S, Hq, Hkv, dh, causal, Q, K, V, O)) goto out;
+  if (mirror)
+    for (int64_t e = 0; e < T * qw; ++e) O[e] = bf16_round(O[e]);
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < nrows; ++r) {
     const int64_t t = rows ? rows[r] : r;
@@ -695,7 +726,40 @@ int oracle_block_f64(int64_t nseq, int64_t S, int64_t d, int32_t Hq, int32_t Hkv
     for (int64_t n = 0; n < d; ++n) x1[n] = X[t * d + n] + (bO ? x1[n] + bO[n] : x1[n]);
   }
   if (oracle_layernorm_f64(nrows, d, X1, ln2_g, ln2_b, eps, B)) goto out;
-  if (oracle_mlp_unsharded_f64(nrows, d, k, B, W1, Wu, b1, act, W2, b2, Z)) goto out;
+  if (mirror)
+    for (int64_t e = 0; e < nrows * d; ++e) B[e] = bf16_round(B[e]);
+  /* The FFN of the listed rows: Y = act(B W1 + b1) (or SiLU(B Wg) * (B Wu)),
+     Z = Y W2 + b2, each dot product over its index ascending. */
+#pragma omp parallel
+  {
+    double *hid = (double *)malloc(sizeof(double) * (size_t)k);
+    double *up = (double *)malloc(sizeof(double) * (size_t)k);
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+      for (int64_t j = 0; j < k; ++j) hid[j] = up[j] = 0.0;
+      for (int64_t c = 0; c < d; ++c) {
+        const double bv = B[r * d + c];
+        for (int64_t j = 0; j < k; ++j) hid[j] += bv * W1[c * k + j];
+        if (act == OR_ACT_SWIGLU)
+          for (int64_t j = 0; j < k; ++j) up[j] += bv * Wu[c * k + j];
+      }
+      for (int64_t j = 0; j < k; ++j) {
+        const double y = act == OR_ACT_SWIGLU ? act_scalar_f64(OR_ACT_SWIGLU, hid[j]) * up[j]
+                                              : act_scalar_f64(act, b1 ? hid[j] + b1[j] : hid[j]);
+        hid[j] = mirror ? bf16_round(y) : y;
+      }
+      double *z = Z + r * d;
+      for (int64_t n = 0; n < d; ++n) z[n] = 0.0;
+      for (int64_t j = 0; j < k; ++j) {
+        const double *w = W2 + j * d;
+        for (int64_t n = 0; n < d; ++n) z[n] += hid[j] * w[n];
+      }
+      if (b2)
+        for (int64_t n = 0; n < d; ++n) z[n] += b2[n];
+    }
+    free(hid);
+    free(up);
+  }
   for (int64_t e = 0; e < nrows * d; ++e) Out[e] = X1[e] + Z[e];
   rc = 0;
 out:

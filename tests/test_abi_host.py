@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
     for n in ("tp_col_linear", "tp_row_linear", "tp_mlp_shard", "tp_partial_sum",
               "tp_mlp_simulated", "tp_workspace_bytes", "tp_shard_bounds", "tp_status_string",
               "tp_last_error_message", "tp_abi_version", "tp_calib_mfma_bf16", "tp_qkv_linear",
-              "tp_qkv_workspace_bytes"):
+              "tp_qkv_workspace_bytes", "tp_attention", "tp_residual_layernorm",
+              "tp_block_simulated", "tp_block_workspace_bytes"):
         assert n in names
 
 
@@ -377,3 +378,94 @@ def test_attention_rejects(kw, expect):
 def test_attention_empty_is_ok():
     assert status_name(attn(nseq=0, Q=None, K=None, V=None, O=None)) == "TP_OK"
     assert status_name(attn(S=0, Q=None, K=None, V=None, O=None)) == "TP_OK"
+
+
+def rln(T=4, d=64, p=2, parts=(A, A), ldp=64, bias=None, R=A, ldr=64, X=A, ldx=64, gamma=A,
+        beta=A, eps=1e-5, Aout=A, lda=64):
+    arr = (P * max(len(parts), 1))(*[P(x) for x in parts])
+    return tp.library().tp_residual_layernorm(T, d, p, arr if parts is not None else None, ldp,
+                                              P(bias), P(R), ldr, P(X), ldx, P(gamma), P(beta),
+                                              eps, P(Aout), lda, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(T=-1), "TP_ERR_BAD_SHAPE"),
+    (dict(d=0), "TP_ERR_BAD_SHAPE"),
+    (dict(d=16392, ldp=16392, ldr=16392, ldx=16392, lda=16392), "TP_ERR_BAD_SHAPE"),  # > 16384
+    (dict(d=60), "TP_ERR_MISALIGNED"),
+    (dict(p=65), "TP_ERR_BAD_SHARD"),
+    (dict(p=-1), "TP_ERR_BAD_SHARD"),
+    (dict(p=0, parts=(), R=None), "TP_ERR_BAD_SHAPE"),          # nothing to add
+    (dict(X=None, Aout=None, gamma=None, beta=None), "TP_ERR_BAD_SHAPE"),  # no output
+    (dict(gamma=None), "TP_ERR_NULL_POINTER"),                  # A without gamma
+    (dict(beta=None), "TP_ERR_NULL_POINTER"),
+    (dict(eps=-1.0), "TP_ERR_BAD_SHAPE"),
+    (dict(eps=float("inf")), "TP_ERR_BAD_SHAPE"),
+    (dict(ldp=60), "TP_ERR_BAD_SHAPE"),
+    (dict(lda=68), "TP_ERR_MISALIGNED"),
+    (dict(parts=(A, None)), "TP_ERR_NULL_POINTER"),
+    (dict(R=MIS), "TP_ERR_MISALIGNED"),
+    (dict(bias=MIS), "TP_ERR_MISALIGNED"),
+])
+def test_residual_layernorm_rejects(kw, expect):
+    assert status_name(rln(**kw)) == expect
+
+
+@no_gpu
+def test_residual_layernorm_empty_is_ok():
+    assert status_name(rln(T=0, parts=(None, None), R=None, X=None, Aout=A)) == "TP_OK"
+    assert status_name(rln(T=0, parts=(None, None), R=None, X=None, Aout=None, gamma=None,
+                           beta=None)) == "TP_OK"
+
+
+def blk(dt=1, act=2, nseq=1, S=64, d=64, Hq=4, Hkv=2, dh=64, k=128, p=2, causal=1, eps=1e-5,
+        X=A, ldx=64, g1=A, b1n=A, Wqkv=A, ldq=512, bqkv=None, WO=A, ldo=64, bO=None, g2=A, b2n=A,
+        W1=A, ldw1=128, Wu=None, ldwu=0, b1=None, W2=A, ldw2=64, b2=None, Out=A, ldout=64,
+        ws=A, wsb=1 << 40):
+    return tp.library().tp_block_simulated(
+        dt, act, nseq, S, d, Hq, Hkv, dh, k, p, causal, eps, P(X), ldx, P(g1), P(b1n), P(Wqkv),
+        ldq, P(bqkv), P(WO), ldo, P(bO), P(g2), P(b2n), P(W1), ldw1, P(Wu), ldwu, P(b1), P(W2),
+        ldw2, P(b2), P(Out), ldout, P(ws), wsb, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dt=0), "TP_ERR_BAD_DTYPE"),
+    (dict(act=9), "TP_ERR_BAD_ACT"),
+    (dict(S=-1), "TP_ERR_BAD_SHAPE"),
+    (dict(dh=96, ldq=768), "TP_ERR_BAD_SHAPE"),
+    (dict(Hkv=3, ldq=640), "TP_ERR_NOT_DIVISIBLE"),            # Hq % Hkv
+    (dict(p=4, Hq=4, Hkv=2), "TP_ERR_NOT_DIVISIBLE"),          # Hkv % p
+    (dict(k=129, ldw1=136), "TP_ERR_NOT_DIVISIBLE"),
+    (dict(p=0), "TP_ERR_BAD_SHARD"),
+    (dict(d=60, ldx=64, ldo=64, ldw2=64, ldout=64), "TP_ERR_MISALIGNED"),
+    (dict(d=16392, ldx=16392, ldo=16392, ldw2=16392, ldout=16392), "TP_ERR_BAD_SHAPE"),
+    (dict(g2=None), "TP_ERR_NULL_POINTER"),
+    (dict(X=None), "TP_ERR_NULL_POINTER"),
+    (dict(Out=MIS), "TP_ERR_MISALIGNED"),
+    (dict(eps=-1.0), "TP_ERR_BAD_SHAPE"),
+    (dict(ldq=500), "TP_ERR_BAD_SHAPE"),                       # below (Hq + 2 Hkv) dh
+    (dict(ldout=60), "TP_ERR_BAD_SHAPE"),
+    (dict(act=4), "TP_ERR_NULL_POINTER"),                      # SwiGLU without Wu
+    (dict(act=4, Wu=A, ldwu=128, b1=A), "TP_ERR_BAD_ACT"),     # column bias with SwiGLU
+    (dict(ws=None, wsb=0), "TP_ERR_WORKSPACE"),
+    (dict(wsb=1024), "TP_ERR_WORKSPACE"),
+])
+def test_block_rejects(kw, expect):
+    assert status_name(blk(**kw)) == expect
+
+
+@no_gpu
+def test_block_empty_is_ok_and_workspace_sizes():
+    assert status_name(blk(S=0, X=None, Out=None, ws=None, wsb=0)) == "TP_OK"
+    bf16 = torch.bfloat16
+    # T = 4096: counter area, LN output, QKV and attention output of one shard, the 8 hidden
+    # shards and the 8 partials plus X1 (all 256-byte multiples here)
+    T, d, s = 4096, 8192, 3584
+    expect = (256 << 10) + T * d * 2 + T * 1280 * 2 + T * 1024 * 2 + 8 * T * s * 2 + T * d * 4 \
+        + 8 * T * d * 4
+    assert tp.tp_block_workspace_bytes(bf16, "swiglu", 1, T, d, 64, 8, 128, 28672, 8) == expect
+    assert tp.tp_block_workspace_bytes(bf16, "swiglu", 1, 0, d, 64, 8, 128, 28672, 8) == 0
+    assert tp.tp_block_workspace_bytes(torch.float32, "swiglu", 1, T, d, 64, 8, 128, 28672, 8) == 0
+    assert tp.tp_block_workspace_bytes(bf16, "swiglu", 1, T, d, 64, 8, 96, 28672, 8) == 0

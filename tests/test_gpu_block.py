@@ -1,0 +1,195 @@
+"""GPU parity of the transformer block: the row step (tp_residual_layernorm: the
+sum of the partials, the bias and the residual, then LayerNorm) and the whole
+pre-LayerNorm block of p shards on one GPU (tp_block_simulated), through the C
+ABI, against the CPU oracle on the same seeded inputs.  The residual sums are
+compared bit for bit with a left-to-right fp32 sum; LayerNorm and block
+outputs within the bf16 bar."""
+import numpy as np
+import pytest
+import torch
+
+import megatron_tensor_mlp_amd as tp
+import oracle
+from megatron_tensor_mlp_amd import synth
+from tests.helpers import BF16_REL_FRO, assert_bf16_close, errors, f64, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def fp32_sum(parts, bias, R):
+    """((parts[0] + ...) + bias) + R in fp32, left to right: the oracle's fp32
+    partial sum, then one IEEE fp32 add of the residual."""
+    terms = list(parts)
+    if terms:
+        x = oracle.partial_sum_f32([t.numpy() for t in terms], None if bias is None else bias.numpy())
+    elif bias is not None:
+        x = np.broadcast_to(bias.numpy(), R.shape).astype(np.float32)
+    else:
+        x = None
+    if R is not None:
+        x = R.numpy() if x is None else (x.astype(np.float32) + R.numpy()).astype(np.float32)
+    return np.asarray(x, dtype=np.float32)
+
+
+# (T, d, p, bias, residual, layernorm, what)
+ROW_CASES = [
+    (7, 264, 3, True, True, True, "three partials, bias, residual, LayerNorm"),
+    (300, 8192, 8, True, True, True, "Llama width, 8 partials"),
+    (1, 16384, 2, False, True, True, "widest row, one token"),
+    (33, 8, 1, True, False, True, "8 columns: most threads hold nothing"),
+    (65, 1032, 0, False, True, True, "no partials: LayerNorm of the residual"),
+    (17, 520, 4, True, True, False, "sum only, no LayerNorm"),
+    (5, 264, 0, True, True, False, "bias + residual"),
+]
+
+
+@pytest.mark.parametrize("T,d,p,bias,res,ln,what", ROW_CASES)
+def test_residual_layernorm(T, d, p, bias, res, ln, what):
+    say(f"residual_layernorm T={T} d={d} p={p} bias={bias} R={res} LN={ln}: {what}")
+    parts = [torch.from_numpy(synth.gaussian_f32((T, d), 100 + q)) for q in range(p)]
+    b = torch.from_numpy(synth.gaussian_f32((d,), 90, 0.5)) if bias else None
+    R = torch.from_numpy(synth.gaussian_f32((T, d), 91, 2.0)) if res else None
+    g, be = synth.layernorm_params(d, 92)
+    # padded leading dimensions; the padding is NaN and must stay NaN
+    Pd = [dev(torch.nn.functional.pad(t, (0, 8), value=float("nan")))[:, :d] for t in parts]
+    Xb = torch.full((T, d + 8), float("nan"), device=DEV)
+    Ab = torch.full((T, d + 16), float("nan"), dtype=torch.bfloat16, device=DEV)
+    X, A = Xb[:, :d], Ab[:, :d]
+    tp.tp_residual_layernorm(Pd, X=X, A=A if ln else None, bias=dev(b), R=dev(R),
+                             gamma=dev(g) if ln else None, beta=dev(be) if ln else None, eps=1e-5)
+    torch.cuda.synchronize()
+    ref = fp32_sum(parts, b, R)
+    assert np.array_equal(X.cpu().numpy(), ref), "residual sum differs from the fp32 sum"
+    assert torch.isnan(Xb[:, d:]).all()
+    if ln:
+        assert_bf16_close(A, oracle.layernorm(ref.astype(np.float64), f64(g), f64(be), 1e-5), "A")
+        assert torch.isnan(Ab[:, d:]).all()
+    else:
+        assert torch.isnan(Ab).all()
+
+
+def test_residual_layernorm_in_place_and_empty():
+    """X may alias the residual (the residual stream updated in place); T = 0
+    touches nothing."""
+    T, d = 9, 264
+    parts = [torch.from_numpy(synth.gaussian_f32((T, d), 110 + q)) for q in range(2)]
+    R = torch.from_numpy(synth.gaussian_f32((T, d), 112))
+    ref = fp32_sum(parts, None, R)
+    Rd = dev(R)
+    tp.tp_residual_layernorm([dev(t) for t in parts], X=Rd, R=Rd)
+    torch.cuda.synchronize()
+    assert np.array_equal(Rd.cpu().numpy(), ref)
+    E = torch.full((0, d), 1.0, device=DEV)
+    tp.tp_residual_layernorm([E], X=E)
+
+
+def run_block(c, Hq, Hkv, dh, p, act, S, causal=True):
+    T, d = c["X"].shape
+    Out = torch.full((T, d), float("nan"), device=DEV)
+    tp.tp_block_simulated(dev(c["X"]), Hq, Hkv, dh, p, tuple(dev(t) for t in c["ln1"]),
+                          dev(c["Wqkv"]), dev(c["WO"]), tuple(dev(t) for t in c["ln2"]),
+                          dev(c["W1"]), dev(c["W2"]), Out, S=S, causal=causal, act=act,
+                          bqkv=dev(c.get("bqkv")), bO=dev(c.get("bO")), Wu=dev(c.get("Wu")),
+                          b1=dev(c.get("b1")), b2=dev(c.get("b2")))
+    torch.cuda.synchronize()
+    return Out
+
+
+def oracle_block(c, Hq, Hkv, dh, act, S, causal=True, rows=None, mirror=False):
+    o = lambda t: None if t is None else f64(t)  # noqa: E731
+    return oracle.block(f64(c["X"]), Hq, Hkv, dh, act, (o(c["ln1"][0]), o(c["ln1"][1])),
+                        o(c["Wqkv"]), o(c["WO"]), (o(c["ln2"][0]), o(c["ln2"][1])), o(c["W1"]),
+                        o(c["W2"]), S=S, causal=causal, eps=1e-5, bqkv=o(c.get("bqkv")),
+                        bO=o(c.get("bO")), Wu=o(c.get("Wu")), b1=o(c.get("b1")),
+                        b2=o(c.get("b2")), rows=rows, mirror=mirror)
+
+
+def check_block(out, c, Hq, Hkv, dh, act, S, causal=True, rows=None, what="block"):
+    """The block's update (output minus the residual input), checked two ways:
+    against the oracle with the activations a bf16 implementation stores (the
+    LayerNorm outputs, QKV, the attention output, the FFN hidden activation)
+    rounded to bf16 at the same points, within the bf16 bar; and against the
+    exact oracle, within the bar plus the error those roundings alone cause (the
+    distance between the two oracle results)."""
+    X = f64(c["X"]) if rows is None else f64(c["X"])[rows]
+    ref = oracle_block(c, Hq, Hkv, dh, act, S, causal, rows) - X
+    mir = oracle_block(c, Hq, Hkv, dh, act, S, causal, rows, mirror=True) - X
+    got = f64(out) - X
+    q_fro, _ = errors(mir, ref)
+    m_fro, m_mx = assert_bf16_close(got, mir, what + " update vs bf16-mirrored oracle")
+    fro, mx = errors(got, ref)
+    say(f"  {what}: update vs mirrored oracle rel_fro={m_fro:.2e} max_rel={m_mx:.2e}; "
+        f"vs exact oracle {fro:.2e} (bf16 storage alone: {q_fro:.2e})")
+    assert fro <= BF16_REL_FRO + q_fro, f"{what}: rel_fro={fro:.3e} vs the exact oracle"
+
+
+# (nseq, S, d, Hq, Hkv, dh, k, p, act, causal, what)
+BLOCK_CASES = [
+    (1, 200, 256, 8, 2, 64, 512, 2, "gelu_tanh", True, "tiled GEMMs, ragged sequence"),
+    (2, 97, 264, 4, 4, 64, 544, 4, "swiglu", True, "two sequences, 4 shards, k/p = 136"),
+    (1, 130, 512, 4, 2, 128, 1024, 1, "gelu_erf", False, "one shard (p = 1), no mask"),
+    (1, 5, 256, 8, 2, 64, 512, 2, "swiglu", True, "five tokens: the few-token GEMMs"),
+    (3, 20, 264, 8, 8, 64, 512, 8, "relu", True, "60 tokens in three sequences, 8 shards"),
+]
+
+
+@pytest.mark.parametrize("nseq,S,d,Hq,Hkv,dh,k,p,act,causal,what", BLOCK_CASES)
+def test_block_simulated(nseq, S, d, Hq, Hkv, dh, k, p, act, causal, what):
+    say(f"block nseq={nseq} S={S} d={d} heads {Hq}/{Hkv}x{dh} k={k} p={p} {act}: {what}")
+    c = synth.block_case(nseq * S, d, Hq, Hkv, dh, k, act, seed=200 + S)
+    out = run_block(c, Hq, Hkv, dh, p, act, S, causal)
+    check_block(out, c, Hq, Hkv, dh, act, S, causal)
+
+
+def test_block_without_biases_and_in_place():
+    """No biases anywhere; Out aliasing X (the residual stream updated in place)."""
+    nseq, S, d, Hq, Hkv, dh, k, p = 1, 150, 256, 4, 2, 64, 512, 2
+    c = synth.block_case(S, d, Hq, Hkv, dh, k, "gelu_tanh", seed=31, bias=False)
+    Xd = dev(c["X"])
+    tp.tp_block_simulated(Xd, Hq, Hkv, dh, p, tuple(dev(t) for t in c["ln1"]), dev(c["Wqkv"]),
+                          dev(c["WO"]), tuple(dev(t) for t in c["ln2"]), dev(c["W1"]),
+                          dev(c["W2"]), Xd, S=S, act="gelu_tanh")
+    torch.cuda.synchronize()
+    check_block(Xd, c, Hq, Hkv, dh, "gelu_tanh", S, what="in-place block")
+
+
+def test_block_workspace_shared_with_few_token_calls():
+    """The block's workspace keeps its counter area intact: a few-token column step
+    run afterwards on the same buffer is still correct."""
+    nseq, S, d, Hq, Hkv, dh, k, p = 1, 100, 256, 8, 2, 64, 512, 2
+    c = synth.block_case(S, d, Hq, Hkv, dh, k, "swiglu", seed=41)
+    need = tp.tp_block_workspace_bytes(torch.bfloat16, "swiglu", nseq, S, d, Hq, Hkv, dh, k, p)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    Out = torch.empty(S, d, device=DEV)
+    tp.tp_block_simulated(dev(c["X"]), Hq, Hkv, dh, p, tuple(dev(t) for t in c["ln1"]),
+                          dev(c["Wqkv"]), dev(c["WO"]), tuple(dev(t) for t in c["ln2"]),
+                          dev(c["W1"]), dev(c["W2"]), Out, S=S, act="swiglu", Wu=dev(c["Wu"]),
+                          bqkv=dev(c["bqkv"]), bO=dev(c["bO"]), b2=dev(c["b2"]), ws=ws)
+    X8, Wg, Wu, _, _ = synth.small_case(8, 256, 512, 43, True, False)
+    Y = torch.empty(8, 256, dtype=torch.bfloat16, device=DEV)
+    tp.tp_col_linear(dev(X8), dev(Wg), 0, 2, Y, act="swiglu", Wu=dev(Wu), ws=ws)
+    torch.cuda.synchronize()
+    check_block(Out, c, Hq, Hkv, dh, "swiglu", S)
+    assert_bf16_close(Y, oracle.col_shard(f64(X8), f64(Wg), 0, 2, "swiglu", Wu=f64(Wu)), "Y")
+
+
+@pytest.mark.parametrize("S", [128, 1])
+def test_llama_block_full_width(S):
+    """Llama-70B width (d = 8192, 64 query and 8 key/value heads of 128, SwiGLU FFN
+    k = 28672) over 8 simulated shards with the full weights, one causal sequence of
+    S tokens; the FFN half checked on sampled rows (the oracle computes every
+    token's attention half, the FFN only for those rows)."""
+    d, Hq, Hkv, dh, k, p = 8192, 64, 8, 128, 28672, 8
+    say(f"llama block full width S={S}")
+    c = synth.block_case(S, d, Hq, Hkv, dh, k, "swiglu", seed=42, full_weights=True)
+    out = run_block(c, Hq, Hkv, dh, p, "swiglu", S)
+    rows = [0, S - 1] if S > 1 else [0]
+    if S > 2:
+        rows.insert(1, S // 2)
+    check_block(out[rows], c, Hq, Hkv, dh, "swiglu", S, rows=rows, what="llama block")

@@ -83,6 +83,9 @@ MUTANTS = [
     ("block's second LayerNorm takes the first one's parameters",
      "oracle_layernorm_f64(nrows, d, X1, ln2_g, ln2_b, eps, B)",
      "oracle_layernorm_f64(nrows, d, X1, ln1_g, ln1_b, eps, B)", 0),
+    ("block's FFN swaps gate and up", "act_scalar_f64(OR_ACT_SWIGLU, hid[j]) * up[j]",
+     "act_scalar_f64(OR_ACT_SWIGLU, up[j]) * hid[j]", 0),
+    ("bf16 rounding truncates", "b += 0x7fffu + ((b >> 16) & 1u);", "", 0),
     ("block's output projection reads WO transposed", "const double *w = WO + j * d;\n      for (int64_t n = 0; n < d; ++n) x1[n] += ov * w[n];",
      "for (int64_t n = 0; n < d; ++n) x1[n] += ov * WO[n * qw + j];", 0),
 ]

@@ -810,16 +810,18 @@ def _block_params(d, Hq, Hkv, dh, k, act, seed, bias=True):
     return P
 
 
-def _torch_block(X, Hq, Hkv, dh, act, S, causal, eps, P):
+def _torch_block(X, Hq, Hkv, dh, act, S, causal, eps, P, mirror=False):
     """The same block from torch's fp64 library routines (layer_norm, matmul,
-    scaled_dot_product_attention, gelu, silu, relu)."""
+    scaled_dot_product_attention, gelu, silu, relu); with mirror, the stored
+    activations go through torch's fp32 -> bf16 conversion."""
     t = lambda a: None if a is None else torch.tensor(a)  # noqa: E731
+    q16 = (lambda a: a.float().bfloat16().double()) if mirror else (lambda a: a)  # noqa: E731
     X = t(X)
     T, d = X.shape
     g = Hq // Hkv
     ln = lambda x, gb: torch.nn.functional.layer_norm(x, (d,), t(gb[0]), t(gb[1]), eps=eps)  # noqa
-    A = ln(X, P["ln1"])
-    qkv = A @ t(P["Wqkv"]) + (t(P["bqkv"]) if "bqkv" in P else 0)
+    A = q16(ln(X, P["ln1"]))
+    qkv = q16(A @ t(P["Wqkv"]) + (t(P["bqkv"]) if "bqkv" in P else 0))
     q, kk, v = qkv[:, :Hq * dh], qkv[:, Hq * dh:(Hq + Hkv) * dh], qkv[:, (Hq + Hkv) * dh:]
     O = torch.empty(T, Hq * dh, dtype=torch.float64)
     for b in range(T // S):
@@ -829,8 +831,8 @@ def _torch_block(X, Hq, Hkv, dh, act, S, causal, eps, P):
         vh = v[r].reshape(S, Hkv, dh).transpose(0, 1).repeat_interleave(g, dim=0)
         o = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, is_causal=causal)
         O[r] = o.transpose(0, 1).reshape(S, Hq * dh)
-    X1 = X + (O @ t(P["WO"]) + (t(P["bO"]) if "bO" in P else 0))
-    B = ln(X1, P["ln2"])
+    X1 = X + (q16(O) @ t(P["WO"]) + (t(P["bO"]) if "bO" in P else 0))
+    B = q16(ln(X1, P["ln2"]))
     H = B @ t(P["W1"])
     if act == "swiglu":
         H = torch.nn.functional.silu(H) * (B @ t(P["Wu"]))
@@ -839,7 +841,7 @@ def _torch_block(X, Hq, Hkv, dh, act, S, causal, eps, P):
         H = {"gelu_tanh": lambda x: torch.nn.functional.gelu(x, approximate="tanh"),
              "gelu_erf": torch.nn.functional.gelu, "relu": torch.relu,
              "none": lambda x: x}[act](H)
-    return (X1 + (H @ t(P["W2"]) + (t(P["b2"]) if "b2" in P else 0))).numpy()
+    return (X1 + (q16(H) @ t(P["W2"]) + (t(P["b2"]) if "b2" in P else 0))).numpy()
 
 
 @pytest.mark.parametrize("T,S,Hq,Hkv,act,causal", [(12, 12, 4, 2, "gelu_tanh", True),
@@ -891,3 +893,31 @@ def test_block_equals_its_tensor_parallel_split(act, p):
              for i in range(p)]
     out = X1 + oracle.partial_sum(parts, P["b2"])
     assert rel_fro(out, oracle.block(X, Hq, Hkv, dh, act, **P)) < 1e-12
+
+
+def test_round_bf16_against_torch():
+    """The oracle's round-to-nearest-even bf16 (through fp32) equals torch's
+    conversion, on random values over many binades, exact ties and specials."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(20000) * np.exp2(rng.integers(-60, 60, 20000))
+    ties = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 2.0 ** -130, 0.0,
+                     -0.0, 3.3895313892515355e38, np.inf, -np.inf])
+    x = np.concatenate([x, ties])
+    ref = torch.tensor(x).float().bfloat16().double().numpy()
+    got = oracle.round_bf16(x)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "swiglu"])
+def test_block_mirror_mode_against_torch(act):
+    """Mirror mode (a diagnostic) rounds exactly the stored activations: it equals
+    the torch composition with torch's bf16 conversion at the same points, and it
+    differs from the exact block."""
+    T, S, Hq, Hkv, d, dh, k = 10, 5, 4, 2, 16, 4, 24
+    P = _block_params(d, Hq, Hkv, dh, k, act, 77)
+    X = np.random.default_rng(78).standard_normal((T, d))
+    got = oracle.block(X, Hq, Hkv, dh, act, S=S, mirror=True, **P)
+    ref = _torch_block(X, Hq, Hkv, dh, act, S, True, 1e-5, P, mirror=True)
+    assert rel_fro(got, ref) < 1e-12
+    assert rel_fro(got, oracle.block(X, Hq, Hkv, dh, act, S=S, **P)) > 1e-5
