@@ -375,6 +375,63 @@ def attention_bench(torch, tp, synth, steps, warmup, rotate_bytes=600 << 20):
     return out
 
 
+def transformer_block_bench(torch, tp, synth, steps, warmup):
+    """One pre-LayerNorm Llama-70B transformer block (d = 8192, 64 query and 8
+    key/value heads of 128, SwiGLU FFN k = 28672) of 8 tensor-parallel shards
+    simulated on this GPU (tp_block_simulated, full weights): prefill, one
+    causal sequence of 4096 tokens, and decode, one token.  The row steps
+    (tp_residual_layernorm) are timed alone as well: LN1 of the residual stream,
+    and the sum of the 8 partials with the bias and the residual followed by LN2.
+    HIP-graph replay."""
+    dev = "cuda:0"
+    d, Hq, Hkv, dh, k, p = 8192, 64, 8, 128, 28672, 8
+    ncol = (Hq + 2 * Hkv) * dh
+    out = {"workload": "llama70b_block_tp8 (8 shards simulated)"}
+    c = None
+    for T in (4096, 1):
+        c = synth.block_case(T, d, Hq, Hkv, dh, k, "swiglu", seed=42, full_weights=True) \
+            if c is None else dict(c, X=torch.from_numpy(synth.gaussian_f32((T, d), 42)))
+        g = {n: (tuple(x.to(dev) for x in v) if isinstance(v, tuple) else
+                 (v.to(dev) if v is not None else None)) for n, v in c.items()}
+        Out = torch.empty(T, d, device=dev)
+        ws = tp.workspace(tp.tp_block_workspace_bytes(torch.bfloat16, "swiglu", 1, T, d, Hq, Hkv,
+                                                      dh, k, p), dev)
+        f = lambda T=T, g=g, Out=Out, ws=ws: tp.tp_block_simulated(  # noqa: E731
+            g["X"], Hq, Hkv, dh, p, g["ln1"], g["Wqkv"], g["WO"], g["ln2"], g["W1"], g["W2"], Out,
+            S=T, act="swiglu", bqkv=g["bqkv"], bO=g["bO"], Wu=g["Wu"], b2=g["b2"], ws=ws)
+        ramp(torch, [f])
+        t = time_graph(torch, [f], max(3, steps), warmup, per_replay=2)
+        flops = (2.0 * T * d * ncol + 4.0 * dh * Hq * T * (T + 1) / 2 + 2.0 * T * Hq * dh * d
+                 + 6.0 * T * d * k)
+        wbytes = 2.0 * (d * ncol + Hq * dh * d + 3 * d * k)
+        key = "prefill" if T > 1 else "decode"
+        out[key] = {"T": T, "us": round(t * 1e6, 1), "TFLOPs": round(flops / t / 1e12, 1),
+                    "frac_mfma": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "weight_GBps": round(wbytes / t / 1e9, 1), "flops": flops,
+                    "weight_bytes": wbytes, "spread": LAST_SPREAD}
+        if T > 1:
+            Xr, Ab, X1 = g["X"], torch.empty(T, d, dtype=torch.bfloat16, device=dev), \
+                torch.empty(T, d, device=dev)
+            parts = [torch.empty(T, d, device=dev).normal_() for _ in range(p)]
+            ln1 = lambda: tp.tp_residual_layernorm((), A=Ab, R=Xr, gamma=g["ln1"][0],  # noqa
+                                                   beta=g["ln1"][1])
+            red = lambda: tp.tp_residual_layernorm(parts, X=X1, A=Ab, bias=g["bO"], R=Xr,  # noqa
+                                                   gamma=g["ln2"][0], beta=g["ln2"][1])
+            t1 = time_graph(torch, [ln1], max(5, steps), warmup)
+            t2 = time_graph(torch, [red], max(5, steps), warmup)
+            b1 = T * d * (4 + 2)
+            b2 = T * d * (4 * p + 4 + 4 + 2)
+            out["row_steps"] = {
+                "layernorm_us": round(t1 * 1e6, 1), "layernorm_GBps": round(b1 / t1 / 1e9, 1),
+                "reduce8_residual_layernorm_us": round(t2 * 1e6, 1),
+                "reduce8_residual_layernorm_GBps": round(b2 / t2 / 1e9, 1),
+                "bytes": {"layernorm": b1, "reduce8_residual_layernorm": b2}}
+            del parts, X1, Ab
+        del g, Out
+    out["timing"] = "HIP graph replay"
+    return out
+
+
 def backward_bench(torch, tp, synth, steps, warmup):
     """Training step of the Llama-70B SwiGLU shard at TP = 8, T = 4096: the
     training forward of the column step (Y and the kept [G | U]), the row step,
@@ -493,7 +550,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline only")
     ap.add_argument("--sections",
-                    default="decode,partial_sum,simulated_block,gpt,attention,backward,calibration",
+                    default="decode,partial_sum,simulated_block,gpt,attention,block,backward,calibration",
                     help="comma list of the secondary sections to run (without --quick)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 256 MiB device copy (the reference for HBM byte counters)")
@@ -561,6 +618,10 @@ def main():
         log("bench: attention projections")
         result["attention_projections"] = attention_bench(torch, tp, synth,
                                                           max(5, args.steps // 2), 3)
+    if "block" in sections:
+        log("bench: transformer block")
+        result["transformer_block"] = transformer_block_bench(torch, tp, synth,
+                                                              max(3, args.steps // 10), 2)
     if "backward" in sections:
         log("bench: training step (backward)")
         result["training_step"] = backward_bench(torch, tp, synth, max(5, args.steps // 4), 2)

@@ -365,7 +365,11 @@ tp_status tp_residual_layernorm(int64_t T, int64_t d, int32_t p, const float *co
  *   Out  = ((Z_0 + Z_1) + ...) + b2 + X1                 (reduction #2)
  * The two sums stand for the two all-reduces of the block; every step runs
  * in this library's kernels (tp_residual_layernorm's for the sums and the
- * LayerNorms).
+ * LayerNorms).  The p shards' QKV column blocks together are the whole
+ * projection and are computed by one launch, the attention core runs over all
+ * heads in one launch, and the W_O row blocks and the FFN shards are grouped
+ * launches that write one partial per shard; each element is computed as in
+ * the shard's own launch.
  *   T = nseq * S tokens (nseq sequences of S; attention causal when causal
  *   != 0); X, Out [T, d] fp32 (ldx, ldout), Out may alias X;
  *   ln1_g, ln1_b, ln2_g, ln2_b [d] fp32; eps as in tp_residual_layernorm;
@@ -376,8 +380,8 @@ tp_status tp_residual_layernorm(int64_t T, int64_t d, int32_t p, const float *co
  * dt must be TP_BF16; dh 64 or 128; Hq, Hkv and k divisible by p and Hq by
  * Hkv (TP_ERR_NOT_DIVISIBLE); 8 <= d <= 16384, a multiple of 8.  Workspace:
  * at least tp_block_workspace_bytes (the shared layout: zeroed counter area,
- * then scratch; it holds A, the shard's QKV and attention output, the p
- * hidden shards and p fp32 [T, d] partials).  Nothing is launched on error.
+ * then scratch; it holds A, the QKV projection and attention output of all
+ * heads, the p hidden shards and p fp32 [T, d] partials).  Nothing is launched on error.
  */
 tp_status tp_block_simulated(tp_dtype dt, tp_act act, int64_t nseq, int64_t S, int64_t d,
                              int32_t Hq, int32_t Hkv, int64_t dh, int64_t k, int32_t p,

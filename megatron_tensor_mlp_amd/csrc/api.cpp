@@ -6,7 +6,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
-#include <vector>
 
 #include "../../include/tpmlp.h"
 #include "../../include/tpmlp_calib.h"
@@ -603,7 +602,7 @@ tp_status check_eps(float eps) {
 // block's buffers need; `ws` may be NULL for a size query.
 struct BlockPlan {
   tp_status st;
-  int64_t T, qw, kw, nqkv, s;
+  int64_t T, qw, nqkv, s;
   BlockLayout L;
   size_t gemm_ws;
 };
@@ -641,28 +640,26 @@ BlockPlan plan_block(tp_dtype dt, tp_act act, int64_t nseq, int64_t S, int64_t d
   if (nseq > 0 && S > (int64_t(1) << 40) / nseq)
     return bad(fail(TP_ERR_BAD_SHAPE, "nseq * S is too large"));
   P.T = nseq * S;
-  P.qw = (int64_t)Hq * dh / p;
-  P.kw = (int64_t)Hkv * dh / p;
-  P.nqkv = P.qw + 2 * P.kw;
+  P.qw = (int64_t)Hq * dh / p;  // one shard's attention-output columns (W_O rows)
+  P.nqkv = ((int64_t)Hq + 2 * (int64_t)Hkv) * dh;  // all shards' QKV columns
   P.s = k / p;
   // Scratch of the few-token GEMMs (zero with more than 64 tokens): the
   // largest of the block's four GEMM shapes; buffers are placeholders here.
   static const char dummy[16] __attribute__((aligned(16))) = {0};
   const int64_t T = P.T;
-  const QkvCall qc = make_qkv(dt, T, d, Hq, Hkv, dh, 0, p, dummy, d, dummy,
-                              ((int64_t)Hq + 2 * (int64_t)Hkv) * dh, nullptr, (void *)dummy,
-                              P.nqkv);
-  const RowCall ro = make_row(dt, T, d, (int64_t)Hq * dh, 0, p, dummy, P.qw, dummy, d,
-                              (float *)dummy, d);
+  const QkvCall qc = make_qkv(dt, T, d, Hq, Hkv, dh, 0, 1, dummy, d, dummy, P.nqkv, nullptr,
+                              (void *)dummy, P.nqkv);
+  const RowCall ro = make_row(dt, T, d, (int64_t)Hq * dh, 0, p, dummy, (int64_t)Hq * dh, dummy,
+                              d, (float *)dummy, d);
   const ColCall c = make_col(dt, act, T, d, k, 0, p, dummy, d, dummy, k, dummy, k, nullptr,
                              (void *)dummy, P.s);
   const RowCall r = make_row(dt, T, d, k, 0, p, dummy, P.s, dummy, d, (float *)dummy, d);
   size_t g = gemm_ws_bytes(dt, qkv_gemm(qc));
-  g = max_sz(g, gemm_ws_bytes(dt, row_gemm(ro, 1, 0, 0)));
+  g = max_sz(g, gemm_ws_bytes(dt, row_gemm(ro, p, P.qw, T * d)));
   g = max_sz(g, gemm_ws_bytes(dt, col_gemm(c, p, T * P.s)));
   g = max_sz(g, gemm_ws_bytes(dt, row_gemm(r, p, T * P.s, T * d)));
   P.gemm_ws = g;
-  P.L = block_layout(g, T, d, P.nqkv, P.qw, P.s, p);
+  P.L = block_layout(g, T, d, P.nqkv, (int64_t)Hq * dh, P.s, p);
   return P;
 }
 }  // namespace
@@ -1051,18 +1048,24 @@ tp_status tp_block_simulated(tp_dtype dt, tp_act act, int64_t nseq, int64_t S, i
     TRY(check_ptr("X", X));
     TRY(check_ptr("Out", Out));
   }
-  // The GEMMs of shard 0 stand for all shards (the others differ by block
-  // offsets only); their checks run on the real buffers once the workspace is
-  // known, or on placeholders when there are no tokens.
+  // In this simulated mode the p shards' column blocks of the QKV projection
+  // together are the whole projection: one GEMM computes all of them (every
+  // output element is the same dot product, in the same order, as in the
+  // shard's own launch), the attention core runs over all heads at once
+  // (heads never mix), and the W_O row blocks are one grouped launch that
+  // writes one fp32 partial per shard; likewise the FFN shards.  The checks
+  // run on the real buffers once the workspace is known, or on placeholders
+  // when there are no tokens.
   static const char dummy[16] __attribute__((aligned(16))) = {0};
   const BlockLayout &L = P.L;
   if (T > 0) TRY(check_ws(L.total, ws, ws_bytes));
   char *w = T > 0 ? (char *)ws : (char *)dummy;
-  QkvCall qc = make_qkv(dt, T, d, Hq, Hkv, dh, 0, p, dummy, d, Wqkv, ldwqkv, bqkv,
+  QkvCall qc = make_qkv(dt, T, d, Hq, Hkv, dh, 0, 1, dummy, d, Wqkv, ldwqkv, bqkv,
                         (void *)dummy, P.nqkv);
   ColCall c = make_col(dt, act, T, d, k, 0, p, dummy, d, W1, ldw1, Wu, ldwu, b1, (void *)dummy,
                        P.s);
-  RowCall ro = make_row(dt, T, d, (int64_t)Hq * dh, 0, p, dummy, P.qw, WO, ldwo, (float *)dummy, d);
+  RowCall ro = make_row(dt, T, d, (int64_t)Hq * dh, 0, p, dummy, (int64_t)Hq * dh, WO, ldwo,
+                        (float *)dummy, d);
   RowCall r = make_row(dt, T, d, k, 0, p, dummy, P.s, W2, ldw2, (float *)dummy, d);
   if (T > 0) {
     qc.X = w + L.a;
@@ -1085,31 +1088,22 @@ tp_status tp_block_simulated(tp_dtype dt, tp_act act, int64_t nseq, int64_t S, i
   AttnArgs at{};
   at.nseq = nseq;
   at.S = S;
-  at.Hq = Hq / p;
-  at.Hkv = Hkv / p;
+  at.Hq = Hq;
+  at.Hkv = Hkv;
   at.dh = (int)dh;
   at.causal = causal ? 1 : 0;
   at.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)dh));
   at.Q = w + L.qkv;
-  at.K = w + L.qkv + P.qw * 2;
-  at.V = w + L.qkv + (P.qw + P.kw) * 2;
+  at.K = w + L.qkv + (int64_t)Hq * dh * 2;
+  at.V = w + L.qkv + ((int64_t)Hq + Hkv) * dh * 2;
   at.O = w + L.o;
   at.ldq = at.ldk = at.ldv = P.nqkv;
-  at.ldo = P.qw;
+  at.ldo = (int64_t)Hq * dh;
   if (!attention_supported(at))
     return fail(TP_ERR_BAD_SHAPE, "attention shape beyond the kernel's range");
-  std::vector<GemmArgs> qg(p), og(p);
-  for (int32_t i = 0; i < p; ++i) {
-    QkvCall qi = qc;
-    qi.i = i;
-    qg[i] = qkv_gemm(qi);
-    RowCall ri = ro;
-    ri.i = i;
-    ri.Z = parts + (int64_t)i * T * d;
-    og[i] = row_gemm(ri, 1, 0, 0);
-    TRY(check_gemm(dt, qg[i]));
-    TRY(check_gemm(dt, og[i]));
-  }
+  const GemmArgs qg = qkv_gemm(qc), og = row_gemm(ro, p, P.qw, T * d);
+  TRY(check_gemm(dt, qg));
+  TRY(check_gemm(dt, og));
   const GemmArgs cg = col_gemm(c, p, T * P.s), rg = row_gemm(r, p, T * P.s, T * d);
   TRY(check_gemm(dt, cg));
   TRY(check_gemm(dt, rg));
@@ -1127,13 +1121,11 @@ tp_status tp_block_simulated(tp_dtype dt, tp_act act, int64_t nseq, int64_t S, i
   n1.A = w + L.a;
   n1.lda = d;
   TRY(run_rownorm(n1, st));
-  // Attention, shard by shard: QKV_i, the core on its heads, the W_O row block.
-  for (int32_t i = 0; i < p; ++i) {
-    TRY(run_gemm(dt, qg[i], ws, st));
-    const hipError_t e = launch_attention(at, st);
-    if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    TRY(run_gemm(dt, og[i], ws, st));
-  }
+  // Attention of all shards: QKV, the core over every head, the W_O row blocks.
+  TRY(run_gemm(dt, qg, ws, st));
+  const hipError_t e = launch_attention(at, st);
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  TRY(run_gemm(dt, og, ws, st));
   // X1 = sum of the partials + bO + X;  A = LN2(X1)
   RowNormArgs n2{};
   for (int32_t i = 0; i < p; ++i) n2.parts[i] = parts + (int64_t)i * T * d;

@@ -460,10 +460,10 @@ def test_block_rejects(kw, expect):
 def test_block_empty_is_ok_and_workspace_sizes():
     assert status_name(blk(S=0, X=None, Out=None, ws=None, wsb=0)) == "TP_OK"
     bf16 = torch.bfloat16
-    # T = 4096: counter area, LN output, QKV and attention output of one shard, the 8 hidden
+    # T = 4096: counter area, LN output, QKV and attention output of all heads, the 8 hidden
     # shards and the 8 partials plus X1 (all 256-byte multiples here)
     T, d, s = 4096, 8192, 3584
-    expect = (256 << 10) + T * d * 2 + T * 1280 * 2 + T * 1024 * 2 + 8 * T * s * 2 + T * d * 4 \
+    expect = (256 << 10) + T * d * 2 + T * 10240 * 2 + T * 8192 * 2 + 8 * T * s * 2 + T * d * 4 \
         + 8 * T * d * 4
     assert tp.tp_block_workspace_bytes(bf16, "swiglu", 1, T, d, 64, 8, 128, 28672, 8) == expect
     assert tp.tp_block_workspace_bytes(bf16, "swiglu", 1, 0, d, 64, 8, 128, 28672, 8) == 0
