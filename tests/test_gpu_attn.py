@@ -306,3 +306,16 @@ def test_llama_attention_core_full_size():
     cols = np.concatenate([np.arange(h * dh, (h + 1) * dh) for h in heads])
     ref = oracle.attention(f64(Q)[:, cols], f64(K), f64(V), len(heads), hkv, dh)
     assert_bf16_close(f64(O)[:, cols], ref, "O")
+
+
+def test_attention_long_sequence():
+    """One causal sequence of 16384 tokens (256 query blocks per head, 257 key tiles
+    per block pair): two query heads on one key/value head, against the oracle."""
+    S, hq, hkv, dh = 16384, 2, 1, 128
+    Q, K, V = attn_inputs(S, hq, hkv, dh, 90)
+    say(f"attention long sequence S={S}")
+    O = torch.empty(S, hq * dh, dtype=torch.bfloat16, device=DEV)
+    tp.tp_attention(dev(Q), dev(K), dev(V), O, hq, hkv, dh)
+    torch.cuda.synchronize()
+    ref = oracle.attention(f64(Q), f64(K), f64(V), hq, hkv, dh)
+    assert_bf16_close(O, ref, "O")

@@ -359,3 +359,23 @@ def test_llama_block_simulated_tp8():
     assert_bf16_close(Z[rows], Zr, "Z")
     ref = oracle.partial_sum_f32([Zp[i].cpu().numpy() for i in range(W.p)])
     assert np.array_equal(Z.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("T,ldx", [(300, (1 << 21) - 8), (17, (1 << 23) - 8)])
+def test_largest_supported_leading_dimension(T, ldx):
+    """X as a view of a buffer with the largest leading dimension each path
+    accepts (below 2^21 elements with more than 64 tokens, below 2^23 with 64 or
+    fewer): the per-lane 32-bit offsets stay in range (NaN fills the rest)."""
+    X, W1, Wu, _, W2 = synth.small_case(T, 264, 1024, 19, True, False)
+    buf = torch.full((T, ldx), float("nan"), dtype=torch.bfloat16, device=DEV)
+    buf[:, :264] = dev(X)
+    Xv = buf[:, :264]
+    s = 1024 // 4
+    Y = torch.empty(T, s, dtype=torch.bfloat16, device=DEV)
+    Z = torch.empty(T, 264, device=DEV)
+    say(f"largest leading dimension: T={T} ldx={ldx}")
+    tp.tp_mlp_shard(Xv, dev(W1), dev(W2), 2, 4, Y, Z, act="swiglu", Wu=dev(Wu))
+    torch.cuda.synchronize()
+    Yr, Zr = oracle.mlp_shard(f64(X), f64(W1), f64(W2), 2, 4, "swiglu", Wu=f64(Wu))
+    assert_bf16_close(Y, Yr, "Y")
+    assert_bf16_close(Z, Zr, "Z")
