@@ -11,7 +11,9 @@ function computes and which page passage it follows.
 
 Parity unpinned: nothing here.  Every function is pinned by the CPU tests in
 ``tests/test_oracle_pins.py`` (printed value, identities, closed forms,
-brute force with exact rationals, library routines).
+brute force with exact rationals, library routines), the fp32 activations of
+the fp32 instances included (against Python's math module in fp64 within the
+fp32 evaluation bound, and against torch's fp32 activations).
 """
 from __future__ import annotations
 

@@ -86,6 +86,10 @@ MUTANTS = [
     ("block's FFN swaps gate and up", "act_scalar_f64(OR_ACT_SWIGLU, hid[j]) * up[j]",
      "act_scalar_f64(OR_ACT_SWIGLU, up[j]) * hid[j]", 0),
     ("bf16 rounding truncates", "b += 0x7fffu + ((b >> 16) & 1u);", "", 0),
+    ("fp32 gelu_tanh drops the cubic term", "tanhf(c * (x + 0.044715f * x * x * x))",
+     "tanhf(c * x)", 0),
+    ("fp32 silu wrong sign", "return x / (1.0f + expf(-x));", "return x / (1.0f + expf(x));", 0),
+    ("fp32 gelu_erf wrong scale", "erff(x / sqrtf(2.0f))", "erff(x / 2.0f)", 0),
     ("block's output projection reads WO transposed", "const double *w = WO + j * d;\n      for (int64_t n = 0; n < d; ++n) x1[n] += ov * w[n];",
      "for (int64_t n = 0; n < d; ++n) x1[n] += ov * WO[n * qw + j];", 0),
 ]

@@ -238,6 +238,63 @@ def test_activations_against_library_routines():
             v * 0.5 * (1 + math.tanh(v / 2)), rel=1e-13, abs=1e-15)
 
 
+F32_GRID = np.concatenate([GRID, np.linspace(-40.0, 40.0, 641), [-88.5, -90.0, -100.0, 88.0]])
+
+
+def _math_gelu_tanh(v):
+    c = math.sqrt(2.0 / math.pi)
+    return 0.5 * v * (1.0 + math.tanh(c * (v + 0.044715 * v ** 3)))
+
+
+def _math_silu(v):
+    # x * sigmoid(x) through the identity sigmoid(x) = (1 + tanh(x/2)) / 2
+    return v * 0.5 * (1.0 + math.tanh(v / 2.0))
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "gelu_erf", "swiglu"])
+def test_fp32_activations_against_fp64_library(act):
+    """The fp32 path's activations (Day 41 post, 'Simulating column parallel
+    linear', in fp32) against Python's math module in fp64 at the same fp32
+    inputs.  The bound is a few fp32 ulps of |y| + |x|: the GeLU forms compute
+    0.5 x (1 + F) with F near -1 for negative x, so their fp32 evaluation can
+    lose all of its relative accuracy but never more than ulp(1) in the factor
+    (1 + F); an absolute floor of 1e-30 covers SiLU's tail, where the true value
+    underflows fp32.  A dropped term or a flipped sign misses by orders of
+    magnitude more (checked by planted mistakes).  The inputs reach
+    the activation exactly: X = [[1]] and W = the grid, so X W + b = the grid in
+    fp32 with no rounding.  Both fp32 entry points (unsharded and one shard of 4)
+    are checked; the gated variant's up factor is 1."""
+    h = F32_GRID.astype(np.float32)
+    n = h.size - (h.size % 4)
+    h = h[:n]
+    X = np.ones((1, 1), np.float32)
+    W = h.reshape(1, n)
+    if act == "gelu_tanh":
+        ref = np.array([_math_gelu_tanh(float(v)) for v in h])
+    elif act == "gelu_erf":
+        ref = np.array([0.5 * float(v) * math.erfc(-float(v) / math.sqrt(2.0)) for v in h])
+    else:
+        ref = np.array([_math_silu(float(v)) for v in h])
+    if act == "swiglu":  # the unsharded fp32 linear has no gated form: one shard of one
+        ones = np.ones_like(W)
+        got_full = oracle.col_shard_f32(X, W, 0, 1, act, Wu=ones)[0].astype(np.float64)
+        shards = [oracle.col_shard_f32(X, W, i, 4, act, Wu=ones) for i in range(4)]
+    else:
+        got_full = oracle.linear_f32(X, W, None, act)[0].astype(np.float64)
+        shards = [oracle.col_shard_f32(X, W, i, 4, act) for i in range(4)]
+    got_shard = np.concatenate(shards, axis=1)[0].astype(np.float64)
+    tol = 8 * 2.0 ** -24 * (np.abs(ref) + np.abs(h.astype(np.float64))) + 1e-30
+    for got in (got_full, got_shard):
+        bad = np.abs(got - ref) > tol
+        assert not bad.any(), (act, h[bad][:5], got[bad][:5], ref[bad][:5])
+    # torch's fp32 activations agree too (an independent fp32 implementation)
+    ht = torch.from_numpy(h)
+    tref = {"gelu_tanh": lambda t: torch.nn.functional.gelu(t, approximate="tanh"),
+            "gelu_erf": lambda t: torch.nn.functional.gelu(t, approximate="none"),
+            "swiglu": torch.nn.functional.silu}[act](ht).double().numpy()
+    assert np.all(np.abs(got_full - tref) <= 2 * tol)
+
+
 def test_activation_odd_part_identities():
     """act(x) - act(-x) = x for both GeLU forms and SiLU (each is x times a
     function F with F(x) + F(-x) = 1); GeLU(0) = SiLU(0) = 0; large |x| limits."""
