@@ -243,3 +243,54 @@ def block_case(T: int, d: int, Hq: int, Hkv: int, dh: int, k: int, act: str, see
         if act != "swiglu":
             case["b1"] = gaussian_bf16((k,), seed + 13, WEIGHT_STD)
     return case
+
+
+def attn_scaled(T: int, Hq: int, Hkv: int, dh: int, seed: int, score_std: float):
+    """Q, K, V for the attention core with scores of a chosen spread: Q and K
+    N(0, score_std) (so that q.k / sqrt(dh) has standard deviation score_std), V
+    N(0, 1); bf16 CPU tensors from seeds seed, seed + 1, seed + 2."""
+    a = float(np.sqrt(score_std))
+    return (gaussian_bf16((T, Hq * dh), seed, a), gaussian_bf16((T, Hkv * dh), seed + 1, a),
+            gaussian_bf16((T, Hkv * dh), seed + 2))
+
+
+def attn_ramp(nseq: int, S: int, Hq: int, Hkv: int, dh: int, seed: int, slope: float):
+    """Q, K, V whose scores move steadily along each sequence: every query is
+    1 + N(0, 1) in each head dimension, key j of a sequence is slope * j +
+    N(0, 0.25) in each, so the score of key j grows (slope > 0) or falls
+    (slope < 0) by about sqrt(dh) * slope per key.  V N(0, 1).  bf16 CPU
+    tensors (seeds seed, seed + 1, seed + 2)."""
+    import torch
+
+    T = nseq * S
+    q = 1.0 + gaussian_f32((T, Hq * dh), seed)
+    pos = np.tile(np.arange(S, dtype=np.float32), nseq)[:, None]
+    k = np.float32(slope) * pos + gaussian_f32((T, Hkv * dh), seed + 1, 0.5)
+    return (torch.from_numpy(q).to(torch.bfloat16), torch.from_numpy(k).to(torch.bfloat16),
+            gaussian_bf16((T, Hkv * dh), seed + 2))
+
+
+def attn_dominant(nseq: int, S: int, Hq: int, Hkv: int, dh: int, seed: int, causal: bool,
+                  gain: float = 3.0):
+    """Q, K, V in which every query has one key far above the others: K and V
+    N(0, 1); query t of head h is gain times the key row of a key j*(t, h) drawn
+    uniformly from the keys it sees (j* <= t under the causal mask), plus
+    N(0, 0.1^2).  Its score with j* is about gain * sqrt(dh), the others about
+    N(0, gain^2).  Returns the bf16 CPU tensors and j* [T, Hq] (positions within
+    the sequence)."""
+    import torch
+
+    T = nseq * S
+    grp = Hq // Hkv
+    K = gaussian_f32((T, Hkv * dh), seed + 1)
+    rng = np.random.default_rng(seed)
+    t_in = np.tile(np.arange(S), nseq)
+    hi = (t_in + 1) if causal else np.full(T, S)
+    jstar = np.floor(rng.random((T, Hq)) * hi[:, None]).astype(np.int64)
+    q = gaussian_f32((T, Hq * dh), seed + 3, 0.1)
+    base = (np.arange(T) // S) * S
+    for h in range(Hq):
+        c = h // grp
+        q[:, h * dh:(h + 1) * dh] += np.float32(gain) * K[base + jstar[:, h], c * dh:(c + 1) * dh]
+    return (torch.from_numpy(q).to(torch.bfloat16), torch.from_numpy(K).to(torch.bfloat16),
+            gaussian_bf16((T, Hkv * dh), seed + 2), jstar)
