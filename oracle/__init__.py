@@ -342,3 +342,59 @@ def round_bf16(x):
     y = np.empty_like(x)
     lib.oracle_round_bf16_f64(x.size, _p(x), _p(y))
     return y
+
+
+def block_storage_error(X, Hq, Hkv, dh, act, ln1, Wqkv, WO, ln2, W1, W2, S=None, causal=True,
+                        eps=1e-5, bqkv=None, bO=None, Wu=None, b1=None, b2=None, rows=None,
+                        rel=2.0 ** -8, draws=2, seed=0):
+    """An a-priori estimate of the error that storing a block's activations in bf16
+    causes in the block's update (output minus input), computed from the exact
+    oracle's own activations.
+
+    The block is composed from this module's functions exactly as ``block`` computes
+    it (LayerNorm, the full QKV projection, attention, the output projection plus its
+    bias and the residual, LayerNorm, the FFN, its bias and the residual), once as is
+    and ``draws`` more times with every activation a bf16 implementation stores -- the
+    two LayerNorm outputs, Q, K, V, the attention output and the FFN hidden activation
+    -- multiplied element-wise by (1 + rel * xi), xi independent and uniform on
+    [-1, 1] (numpy default_rng(seed + draw)).  rel = 2^-8 is bf16's unit roundoff,
+    the largest relative error a round to nearest bf16 makes; this is a model of the
+    size of that error, not the rounding itself.
+
+    Returns (U, e_fro, e_max): the exact update for the token rows listed in ``rows``
+    (default all), and the root mean square over the draws of the perturbed updates'
+    relative Frobenius distance ||dU|| / ||U|| and relative largest distance
+    max|dU| / max|U| from it."""
+    X = _c(X, np.float64)
+    T, d = X.shape
+    S = T if S is None else S
+    r = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    f = lambda a: None if a is None else _c(a, np.float64)  # noqa: E731
+    Wqkv, WO, W1, W2, Wu = f(Wqkv), f(WO), f(W1), f(W2), f(Wu)
+    bqkv, bO, b1, b2 = f(bqkv), f(bO), f(b1), f(b2)
+    qw, kw = Hq * dh, Hkv * dh
+
+    def run(pert):
+        A1 = pert(layernorm(X, ln1[0], ln1[1], eps))
+        QKV = qkv_shard(A1, Wqkv, Hq, Hkv, dh, 0, 1, bqkv=bqkv)
+        Q, K, V = (pert(np.ascontiguousarray(QKV[:, a:b]))
+                   for a, b in ((0, qw), (qw, qw + kw), (qw + kw, qw + 2 * kw)))
+        O = pert(attention(Q, K, V, Hq, Hkv, dh, causal=causal, S=S))
+        P = row_shard(O[r], WO, 0, 1)
+        X1 = X[r] + (P + bO if bO is not None else P)
+        A2 = pert(layernorm(X1, ln2[0], ln2[1], eps))
+        Y = pert(col_shard(A2, W1, 0, 1, act, b1=b1, Wu=Wu))
+        Z = row_shard(Y, W2, 0, 1)
+        if b2 is not None:
+            Z = Z + b2
+        return (X1 + Z) - X[r]
+
+    U = run(lambda a: a)
+    nu, mu = float(np.linalg.norm(U)), float(np.max(np.abs(U))) if U.size else 0.0
+    e_fro = e_max = 0.0
+    for q in range(draws):
+        rng = np.random.default_rng(seed + q)
+        dU = run(lambda a: a * (1.0 + rel * rng.uniform(-1.0, 1.0, a.shape))) - U
+        e_fro += (float(np.linalg.norm(dU)) / max(nu, 1e-300)) ** 2
+        e_max += (float(np.max(np.abs(dU))) / max(mu, 1e-300) if dU.size else 0.0) ** 2
+    return U, (e_fro / max(draws, 1)) ** 0.5, (e_max / max(draws, 1)) ** 0.5

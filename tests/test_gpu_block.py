@@ -2,8 +2,9 @@
 sum of the partials, the bias and the residual, then LayerNorm) and the whole
 pre-LayerNorm block of p shards on one GPU (tp_block_simulated), through the C
 ABI, against the CPU oracle on the same seeded inputs.  The residual sums are
-compared bit for bit with a left-to-right fp32 sum; LayerNorm and block
-outputs within the bf16 bar."""
+compared bit for bit with a left-to-right fp32 sum; LayerNorm outputs within
+the bf16 bar; the block's update against the exact oracle within the bf16 bar
+or the modelled error of bf16 storage, whichever is larger (check_block)."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +12,7 @@ import torch
 import megatron_tensor_mlp_amd as tp
 import oracle
 from megatron_tensor_mlp_amd import synth
-from tests.helpers import BF16_REL_FRO, assert_bf16_close, errors, f64, say
+from tests.helpers import BF16_MAX_REL, BF16_REL_FRO, assert_bf16_close, errors, f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -110,23 +111,42 @@ def oracle_block(c, Hq, Hkv, dh, act, S, causal=True, rows=None, mirror=False):
                         b2=o(c.get("b2")), rows=rows, mirror=mirror)
 
 
-def check_block(out, c, Hq, Hkv, dh, act, S, causal=True, rows=None, what="block"):
-    """The block's update (output minus the residual input), checked two ways:
-    against the oracle with the activations a bf16 implementation stores (the
-    LayerNorm outputs, QKV, the attention output, the FFN hidden activation)
-    rounded to bf16 at the same points, within the bf16 bar; and against the
-    exact oracle, within the bar plus the error those roundings alone cause (the
-    distance between the two oracle results)."""
+# How far the block's update may be from the exact oracle.  A block chains
+# bf16-in / fp32-accumulate steps, and storing its activations in bf16 (the
+# LayerNorm outputs, Q, K, V, the attention output, the FFN hidden activation)
+# moves the update by an amount that depends on the block's own values: the
+# softmax turns a relative error in Q and K into an absolute error in the
+# scores of about that error times the scores' spread.  The bar is therefore
+# the bf16 bar or 1.5 times that storage error as the a-priori model
+# oracle.block_storage_error estimates it from the exact oracle's activations,
+# whichever is larger; the largest element error may be 4 times the bar, the
+# ratio of the two bf16 bars.
+MODEL_MARGIN = 1.5
+
+
+def check_block(out, c, Hq, Hkv, dh, act, S, causal=True, rows=None, what="block", mirror=False):
+    """The block's update (output minus the residual input) against the exact
+    oracle, within max(bf16 bar, MODEL_MARGIN * modelled bf16 storage error).
+    With mirror, the distance to the oracle that rounds the stored activations
+    to bf16 is printed as a diagnostic (it is not part of the check)."""
+    o = lambda t: None if t is None else f64(t)  # noqa: E731
     X = f64(c["X"]) if rows is None else f64(c["X"])[rows]
-    ref = oracle_block(c, Hq, Hkv, dh, act, S, causal, rows) - X
-    mir = oracle_block(c, Hq, Hkv, dh, act, S, causal, rows, mirror=True) - X
+    ref, e_fro, e_max = oracle.block_storage_error(
+        f64(c["X"]), Hq, Hkv, dh, act, (o(c["ln1"][0]), o(c["ln1"][1])), o(c["Wqkv"]),
+        o(c["WO"]), (o(c["ln2"][0]), o(c["ln2"][1])), o(c["W1"]), o(c["W2"]), S=S,
+        causal=causal, bqkv=o(c.get("bqkv")), bO=o(c.get("bO")), Wu=o(c.get("Wu")),
+        b1=o(c.get("b1")), b2=o(c.get("b2")), rows=rows)
     got = f64(out) - X
-    q_fro, _ = errors(mir, ref)
-    m_fro, m_mx = assert_bf16_close(got, mir, what + " update vs bf16-mirrored oracle")
     fro, mx = errors(got, ref)
-    say(f"  {what}: update vs mirrored oracle rel_fro={m_fro:.2e} max_rel={m_mx:.2e}; "
-        f"vs exact oracle {fro:.2e} (bf16 storage alone: {q_fro:.2e})")
-    assert fro <= BF16_REL_FRO + q_fro, f"{what}: rel_fro={fro:.3e} vs the exact oracle"
+    bar = max(BF16_REL_FRO, MODEL_MARGIN * e_fro)
+    bar_max = bar * (BF16_MAX_REL / BF16_REL_FRO)
+    note = ""
+    if mirror:
+        m_fro, _ = errors(got, oracle_block(c, Hq, Hkv, dh, act, S, causal, rows, mirror=True) - X)
+        note = f"; diagnostic: vs bf16-mirrored oracle {m_fro:.2e}"
+    say(f"  {what}: update vs exact oracle rel_fro={fro:.2e} max_rel={mx:.2e}; modelled bf16 "
+        f"storage error {e_fro:.2e} (max {e_max:.2e}); bar {bar:.2e} / {bar_max:.2e}{note}")
+    assert fro <= bar and mx <= bar_max, f"{what}: rel_fro={fro:.3e} max_rel={mx:.3e} vs {bar:.3e}"
 
 
 # (nseq, S, d, Hq, Hkv, dh, k, p, act, causal, what)
@@ -144,7 +164,7 @@ def test_block_simulated(nseq, S, d, Hq, Hkv, dh, k, p, act, causal, what):
     say(f"block nseq={nseq} S={S} d={d} heads {Hq}/{Hkv}x{dh} k={k} p={p} {act}: {what}")
     c = synth.block_case(nseq * S, d, Hq, Hkv, dh, k, act, seed=200 + S)
     out = run_block(c, Hq, Hkv, dh, p, act, S, causal)
-    check_block(out, c, Hq, Hkv, dh, act, S, causal)
+    check_block(out, c, Hq, Hkv, dh, act, S, causal, mirror=True)
 
 
 def test_block_without_biases_and_in_place():

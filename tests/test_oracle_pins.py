@@ -978,3 +978,62 @@ def test_block_mirror_mode_against_torch(act):
     ref = _torch_block(X, Hq, Hkv, dh, act, S, True, 1e-5, P, mirror=True)
     assert rel_fro(got, ref) < 1e-12
     assert rel_fro(got, oracle.block(X, Hq, Hkv, dh, act, S=S, **P)) > 1e-5
+
+
+# ---------------------------------------------------------- block error model ----
+@pytest.mark.parametrize("act,causal,S", [("gelu_tanh", True, 5), ("swiglu", False, 10)])
+def test_block_storage_error_composition(act, causal, S):
+    """The error model's unperturbed composition is the block itself (equal to the
+    oracle block and to torch's fp64 composition), for all rows and a row subset;
+    with rel = 0 it reports no error."""
+    T, Hq, Hkv, d, dh, k = 10, 4, 2, 16, 4, 24
+    P = _block_params(d, Hq, Hkv, dh, k, act, 91)
+    X = np.random.default_rng(92).standard_normal((T, d))
+    ref = oracle.block(X, Hq, Hkv, dh, act, S=S, causal=causal, **P) - X
+    U, ef, em = oracle.block_storage_error(X, Hq, Hkv, dh, act, S=S, causal=causal, rel=0.0, **P)
+    assert rel_fro(U, ref) < 1e-13 and ef == 0.0 and em == 0.0
+    ref_t = _torch_block(X, Hq, Hkv, dh, act, S, causal, 1e-5, P) - X
+    assert rel_fro(U, ref_t) < 1e-12
+    rows = [9, 2, 4]
+    Ur, _, _ = oracle.block_storage_error(X, Hq, Hkv, dh, act, S=S, causal=causal, rows=rows,
+                                          rel=0.0, **P)
+    assert rel_fro(Ur, ref[rows]) < 1e-13
+
+
+def test_block_storage_error_linear_closed_form():
+    """With W_O = 0 the attention half adds only b_O, and with no activation the FFN
+    is linear: U = B W1 W2 + b_O + b2 with B = LayerNorm(X + b_O).  To first order the
+    model's perturbations of B (by B * rel * xi1) and of the hidden activation
+    Y = B W1 (by Y * rel * xi2) change U by (B xi1 rel) W1 W2 + (Y xi2 rel) W2, whose
+    expected squared norm for independent xi uniform on [-1, 1] (variance 1/3) is
+    rel^2 / 3 * (sum_tc B_tc^2 ||(W1 W2)_c||^2 + sum_tj Y_tj^2 ||(W2)_j||^2).  The
+    model's Monte Carlo estimate matches this expectation."""
+    T, Hq, Hkv, d, dh, k = 64, 2, 1, 32, 8, 48
+    P = _block_params(d, Hq, Hkv, dh, k, "none", 93)
+    P["WO"] = np.zeros_like(P["WO"])
+    P.pop("b1", None)
+    X = np.random.default_rng(94).standard_normal((T, d))
+    rel = 2.0 ** -8
+    U, ef, _ = oracle.block_storage_error(X, Hq, Hkv, dh, "none", rel=rel, draws=16, seed=3, **P)
+    B = oracle.layernorm(X + P["bO"], *P["ln2"])
+    Y = B @ P["W1"]
+    M = P["W1"] @ P["W2"]
+    expect = rel ** 2 / 3.0 * (np.sum(B ** 2 * np.sum(M ** 2, axis=1)[None, :])
+                               + np.sum(Y ** 2 * np.sum(P["W2"] ** 2, axis=1)[None, :]))
+    got = (ef * np.linalg.norm(U)) ** 2
+    assert abs(got / expect - 1.0) < 0.1, (got, expect)
+    np.testing.assert_allclose(U, B @ M + P["bO"] + P["b2"], rtol=1e-12, atol=1e-12)
+
+
+def test_block_storage_error_is_first_order():
+    """Halving the relative perturbation halves the modelled error (the model stays
+    in the linear regime of the block), and a different draw gives nearly the same
+    figure (the estimate averages over every element of the update)."""
+    T, S, Hq, Hkv, d, dh, k = 24, 12, 4, 2, 32, 8, 48
+    P = _block_params(d, Hq, Hkv, dh, k, "swiglu", 95)
+    X = np.random.default_rng(96).standard_normal((T, d))
+    _, e1, _ = oracle.block_storage_error(X, Hq, Hkv, dh, "swiglu", S=S, rel=2.0 ** -8, **P)
+    _, e2, _ = oracle.block_storage_error(X, Hq, Hkv, dh, "swiglu", S=S, rel=2.0 ** -9, **P)
+    _, e3, _ = oracle.block_storage_error(X, Hq, Hkv, dh, "swiglu", S=S, rel=2.0 ** -8, seed=7, **P)
+    assert e1 > 0 and abs(e2 / e1 - 0.5) < 0.02
+    assert abs(e3 / e1 - 1.0) < 0.2
