@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TPMLP_ABI_VERSION 5
+#define TPMLP_ABI_VERSION 6
 #define TP_MAX_SHARDS 64
 
 typedef enum {
@@ -145,6 +145,31 @@ tp_status tp_mlp_shard(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k,
                        const void *Wu, int64_t ldwu, const void *b1, const void *W2,
                        int64_t ldw2, void *Y, int64_t ldy, float *Z, int64_t ldz, void *ws,
                        size_t ws_bytes, void *stream);
+
+/*
+ * tp_mlp_shard for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments (without ws/ws_bytes), results and checks
+ * as tp_mlp_shard.  The scratch the few-token (T <= 64, bf16) path needs -- its
+ * arrival counters and split-K partials -- lives in a library-owned static
+ * device array of TP_STATIC_SCRATCH_BYTES on each GPU the library runs on,
+ * held until the process ends; its address is looked up, and its counter area
+ * cleared by a fill kernel on `stream`, at the first call on each device.  The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library call).
+ *   - Sizes whose scratch need exceeds TP_STATIC_SCRATCH_BYTES (the need
+ *     tp_workspace_bytes reports) return TP_ERR_WORKSPACE, with nothing
+ *     launched.
+ *   - Every call on one GPU shares that GPU's array, whose content carries
+ *     over from call to call (each call leaves the counters zero again):
+ *     calls that overlap on one GPU -- on different streams, or from several
+ *     host threads without ordering -- race and give wrong results.
+ */
+#define TP_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+tp_status tp_mlp_shard_noalloc(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t i,
+                               int32_t p, const void *X, int64_t ldx, const void *W1,
+                               int64_t ldw1, const void *Wu, int64_t ldwu, const void *b1,
+                               const void *W2, int64_t ldw2, void *Y, int64_t ldy, float *Z,
+                               int64_t ldz, void *stream);
 
 /*
  * The reduction of p partials (what the all-reduce computes), on one device:

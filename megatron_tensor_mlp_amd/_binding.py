@@ -54,6 +54,8 @@ def library():
                                   vp]
     lib.tp_mlp_shard.argtypes = [ci, ci, i64, i64, i64, i32, i32, vp, i64, vp, i64, vp, i64, vp,
                                  vp, i64, vp, i64, vp, i64, vp, sz, vp]
+    lib.tp_mlp_shard_noalloc.argtypes = [ci, ci, i64, i64, i64, i32, i32, vp, i64, vp, i64, vp,
+                                         i64, vp, vp, i64, vp, i64, vp, i64, vp]
     lib.tp_partial_sum.argtypes = [i64, i64, i32, ctypes.POINTER(vp), i64, vp, vp, i64, vp]
     lib.tp_mlp_simulated.argtypes = [ci, ci, i64, i64, i64, i32, vp, i64, vp, i64, vp, i64, vp,
                                      vp, i64, vp, vp, vp, vp, i64, vp, sz, vp]
@@ -240,6 +242,28 @@ def tp_mlp_shard(X, W1, W2, i: int, p: int, Y, Z, act="gelu_tanh", Wu=None, b1=N
     _check(library().tp_mlp_shard(_dt(X), a, T, d, k, i, p, _ptr(X), ldx, _ptr(W1), ldw1,
                                   _ptr(Wu), ldwu, _ptr(b1), _ptr(W2), ldw2, _ptr(Y), ldy,
                                   _ptr(Z), ldz, wsp, wsn, _stream(stream)))
+    return Y, Z
+
+
+def tp_mlp_shard_noalloc(X, W1, W2, i: int, p: int, Y, Z, act="gelu_tanh", Wu=None, b1=None,
+                         stream=None):
+    """tp_mlp_shard with the library's static scratch instead of a workspace (for
+    callers that cannot allocate): Y <- column step of shard i, Z <- row step."""
+    T, d = X.shape
+    k = W1.shape[1]
+    s = k // p if p > 0 else 0
+    a = _act(act)
+    ldx = _ld(X, T, d, "X")
+    ldw1 = _ld(W1, d, k, "W1")
+    ldwu = _ld(Wu, d, k, "Wu") if Wu is not None else 0
+    ldw2 = _ld(W2, k, d, "W2")
+    ldy = _ld(Y, T, s, "Y")
+    ldz = _ld(Z, T, d, "Z")
+    if b1 is not None and b1.numel() < k:
+        raise ValueError("b1 is shorter than k")
+    _check(library().tp_mlp_shard_noalloc(_dt(X), a, T, d, k, i, p, _ptr(X), ldx, _ptr(W1), ldw1,
+                                          _ptr(Wu), ldwu, _ptr(b1), _ptr(W2), ldw2, _ptr(Y), ldy,
+                                          _ptr(Z), ldz, _stream(stream)))
     return Y, Z
 
 

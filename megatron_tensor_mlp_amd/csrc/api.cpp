@@ -712,6 +712,36 @@ tp_status tp_mlp_shard(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k,
   return ok();
 }
 
+tp_status tp_mlp_shard_noalloc(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t i,
+                               int32_t p, const void *X, int64_t ldx, const void *W1,
+                               int64_t ldw1, const void *Wu, int64_t ldwu, const void *b1,
+                               const void *W2, int64_t ldw2, void *Y, int64_t ldy, float *Z,
+                               int64_t ldz, void *stream) {
+  static_assert(kStaticScratchBytes == TP_STATIC_SCRATCH_BYTES, "scratch size");
+  const ColCall c = make_col(dt, act, T, d, k, i, p, X, ldx, W1, ldw1, Wu, ldwu, b1, Y, ldy);
+  TRY(validate_col(c));
+  const RowCall r = make_row(dt, T, d, k, i, p, Y, ldy, W2, ldw2, Z, ldz);
+  TRY(validate_row(r));
+  if (T == 0) return ok();
+  const GemmArgs ac = col_gemm(c, 1, 0), ar = row_gemm(r, 1, 0, 0);
+  TRY(check_gemm(dt, ac));
+  TRY(check_gemm(dt, ar));
+  const size_t need = max_sz(gemm_ws_bytes(dt, ac), gemm_ws_bytes(dt, ar));
+  if (need > kStaticScratchBytes)
+    return fail(TP_ERR_WORKSPACE,
+                "these sizes need %zu bytes of scratch; the static scratch holds %zu", need,
+                kStaticScratchBytes);
+  void *ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = static_scratch((hipStream_t)stream, &ws);
+    if (e != hipSuccess)
+      return fail(TP_ERR_HIP, "static scratch set-up failed: %s", hipGetErrorString(e));
+  }
+  TRY(run_gemm(dt, ac, ws, (hipStream_t)stream));
+  TRY(run_gemm(dt, ar, ws, (hipStream_t)stream));
+  return ok();
+}
+
 tp_status tp_partial_sum(int64_t T, int64_t d, int32_t p, const float *const *parts, int64_t ldp,
                          const float *b2, float *Z, int64_t ldz, void *stream) {
   if (T < 0) return fail(TP_ERR_BAD_SHAPE, "T = %lld < 0", (long long)T);

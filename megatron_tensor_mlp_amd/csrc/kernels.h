@@ -85,6 +85,13 @@ hipError_t launch_gemm_bf16_tiled(const GemmArgs &a, hipStream_t s);
 constexpr int64_t kWsMaxBlocks = 65536;  // few-token column blocks per call
 constexpr size_t kWsCounterBytes = kWsMaxBlocks * sizeof(unsigned);
 
+// Library-owned scratch for callers that cannot allocate: a static device
+// array of kStaticScratchBytes per GPU in the workspace layout above.  Returns
+// its address on the current device, looked up (and its counter area zeroed on
+// `stream`) at the first call on that device.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+hipError_t static_scratch(hipStream_t stream, void **ptr);
+
 // Few-token path (M <= 64): weight-streaming split-K GEMM (LAY_NN; EPI_ACT,
 // EPI_SWIGLU and EPI_F32).  `ws` must hold
 // decode_workspace_bytes(a) zero-initialised bytes (or 0 bytes if that is 0).

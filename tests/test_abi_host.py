@@ -469,3 +469,42 @@ def test_block_empty_is_ok_and_workspace_sizes():
     assert tp.tp_block_workspace_bytes(bf16, "swiglu", 1, 0, d, 64, 8, 128, 28672, 8) == 0
     assert tp.tp_block_workspace_bytes(torch.float32, "swiglu", 1, T, d, 64, 8, 128, 28672, 8) == 0
     assert tp.tp_block_workspace_bytes(bf16, "swiglu", 1, T, d, 64, 8, 96, 28672, 8) == 0
+
+
+# --- the entry point that allocates nothing ---------------------------------
+def noalloc(dt=1, act=4, T=64, d=8192, k=65536, i=0, p=1, X=A, ldx=8192, W1=A, ldw1=65536, Wu=A,
+            ldwu=65536, b1=None, W2=A, ldw2=8192, Y=A, ldy=65536, Z=A, ldz=8192):
+    return tp.library().tp_mlp_shard_noalloc(dt, act, T, d, k, i, p, P(X), ldx, P(W1), ldw1,
+                                             P(Wu), ldwu, P(b1), P(W2), ldw2, P(Y), ldy, P(Z),
+                                             ldz, None)
+
+
+def test_static_scratch_limit_is_declared():
+    m = re.search(r"#define TP_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == 16 << 20
+
+
+@no_gpu
+def test_noalloc_rejects_sizes_beyond_the_static_scratch():
+    """A SwiGLU few-token shard with 65536 hidden columns needs 32.25 MiB of split-K
+    scratch (tp_workspace_bytes), more than the 16 MiB static array: TP_ERR_WORKSPACE
+    before anything is touched; 16384 columns fit (and T = 0 launches nothing)."""
+    assert tp.tp_workspace_bytes(torch.bfloat16, "swiglu", 64, 8192, 65536, 1) > 16 << 20
+    rc = noalloc()
+    assert status_name(rc) == "TP_ERR_WORKSPACE"
+    assert "static scratch" in tp.library().tp_last_error_message().decode()
+    assert status_name(noalloc(T=0, X=None, Y=None, Z=None)) == "TP_OK"
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(p=3), "TP_ERR_NOT_DIVISIBLE"),
+    (dict(i=1), "TP_ERR_BAD_SHARD"),
+    (dict(Wu=None), "TP_ERR_NULL_POINTER"),
+    (dict(W2=MIS), "TP_ERR_MISALIGNED"),
+    (dict(ldz=8000), "TP_ERR_BAD_SHAPE"),
+    (dict(act=2, b1=A, Wu=None, ldwu=0, T=-1), "TP_ERR_BAD_SHAPE"),
+])
+def test_noalloc_validates_like_the_workspace_entry_point(kw, expect):
+    assert status_name(noalloc(**kw)) == expect
