@@ -15,9 +15,12 @@ flops per GEMM, three GEMMs).  Secondary fields report the few-token (decode)
 shard in GB/s of weights streamed, the on-device partial sum in GB/s, the
 simulated TP = 8 block, the GPT-style GeLU shard, the attention projections
 of one head shard (QKV and output projection) and the shard's training step
-(forward that keeps the pre-activation, and the backward pass).  `roofline` covers the
-dominant kernel (the SwiGLU column GEMM), `cpu_baseline` the CPU oracle timed
-on a bounded row sample of the same workload.
+(forward that keeps the pre-activation, and the backward pass), and the MFMA
+and HBM calibrations.  `roofline` covers the dominant kernel (the SwiGLU column
+GEMM), `roofline_decode` and `roofline_partial_sum` the HBM-bound steps;
+`cpu_baseline` is the CPU oracle timed on a bounded row sample of the same
+workload, and (`configs`) on a sample of every other configuration next to the
+GPU path's errors against it there.
 """
 from __future__ import annotations
 
@@ -128,6 +131,34 @@ def time_each(torch, fn_list, n, warmup):
     return [ev[r].elapsed_time(ev[r + 1]) / 1e3 for r in range(n)]
 
 
+def time_legs(torch, fn_list, n, warmup):
+    """Per-launch durations inside n steps of the launches in fn_list: an event
+    on the launch stream before the first launch of a step and after each
+    launch, so the legs of a step add up to the step.  Returns one list of n
+    durations (seconds) per launch, and the n step durations."""
+    for _ in range(warmup):
+        for fn in fn_list:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fn_list) + 1)]
+          for _ in range(n)]
+    for r in range(n):
+        ev[r][0].record()
+        for j, fn in enumerate(fn_list):
+            fn()
+            ev[r][j + 1].record()
+    torch.cuda.synchronize()
+    legs = [[ev[r][j].elapsed_time(ev[r][j + 1]) / 1e3 for r in range(n)]
+            for j in range(len(fn_list))]
+    steps = [ev[r][0].elapsed_time(ev[r][-1]) / 1e3 for r in range(n)]
+    return legs, steps
+
+
+def median(xs):
+    t = sorted(xs)
+    return t[len(t) // 2]
+
+
 def time_steps(torch, fn_list, steps, warmup):
     """Wall time of `steps` rounds of the launches in fn_list (after `warmup`),
     bracketed by a synchronisation and an event pair on the current stream."""
@@ -177,17 +208,15 @@ def headline(torch, tp, synth, steps, warmup):
     row = lambda: tp.tp_row_linear(Y, W2, 0, 1, Z)  # noqa: E731
     ramp(torch, [col, row])
     total = time_steps(torch, [col, row], steps, warmup)
-    step_spread = spread(time_each(torch, [col, row], 50, 10))
-    reps = max(2, steps // 4)
-    t_col = time_graph(torch, [col], reps, 1, per_replay=4)
-    col_spread = LAST_SPREAD
-    t_row = time_graph(torch, [row], reps, 1, per_replay=4)
-    row_spread = LAST_SPREAD
+    # The same steps again, with an event after each launch: the per-kernel
+    # durations of the steady state the timed steps ran in.
+    legs, steps_ev = time_legs(torch, [col, row], 50, 0)
     flops_col = 2.0 * W.T * W.d * W.s * 2
     flops_row = 2.0 * W.T * W.d * W.s
-    return dict(W=W, total=total, t_col=t_col, t_row=t_row, step_spread=step_spread,
-                col_spread=col_spread, row_spread=row_spread, flops_col=flops_col,
-                flops_row=flops_row, step_flops=flops_col + flops_row)
+    return dict(W=W, total=total, t_col=median(legs[0]), t_row=median(legs[1]),
+                step_spread=spread(steps_ev), col_spread=spread(legs[0]),
+                row_spread=spread(legs[1]), flops_col=flops_col, flops_row=flops_row,
+                step_flops=flops_col + flops_row)
 
 
 def decode_bench(torch, tp, synth, steps, warmup, rotate_bytes=600 << 20):
@@ -230,6 +259,7 @@ def decode_bench(torch, tp, synth, steps, warmup, rotate_bytes=600 << 20):
             "us_per_step": round(step * 1e6, 2),
             "GBps": round(alg_bytes / step / 1e9, 1),
             "frac_hbm": round(alg_bytes / step / 1e9 / PEAK_HBM_GBS, 4),
+            "alg_bytes": alg_bytes,
             "step_spread": step_spread,
             "col_us": round(t_col * 1e6, 2), "row_us": round(t_row * 1e6, 2),
             "col_GBps": round((2 * W.d * W.s * 2) / t_col / 1e9, 1),
@@ -257,6 +287,31 @@ def partial_sum_bench(torch, tp, steps, warmup, copies=4):
     return {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
             "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4), "bytes": nbytes,
             "spread": sp, "rotation_copies": copies, "timing": "HIP graph replay"}
+
+
+def hbm_calibration(torch, tp, steps, warmup, rotate_bytes=600 << 20):
+    """Per-launch streaming-read rate of a plain read kernel (tp_calib_hbm_read)
+    at the sizes the few-token kernels stream (the column step's 117 MB of gate
+    and up weights, the row step's 59 MB) and at 2 GiB, buffers rotating past
+    the Infinity Cache: the ceiling a single launch of that size reaches, ramp
+    and drain included."""
+    dev = "cuda:0"
+    nwg = 256 * 8
+    sink = torch.zeros(nwg, dtype=torch.int32, device=dev)
+    out = {}
+    for name, nbytes in (("col_117MB", 2 * 8192 * 3584 * 2), ("row_59MB", 3584 * 8192 * 2),
+                         ("2GiB", 2 << 30)):
+        copies = max(1, -(-rotate_bytes // nbytes))
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(copies)]
+        fns = [lambda b=b: tp.tp_calib_hbm_read(b, sink) for b in bufs]
+        t = time_graph(torch, fns, max(10, steps), warmup, per_replay=2) / copies
+        out[name] = {"bytes": nbytes, "us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+                     "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
+                     "rotation_copies": copies}
+        del bufs, fns
+    out["kernel"] = ("tp_calib_hbm_read: 2048 workgroups x 256 threads, 16-byte nontemporal "
+                     "loads, 4 in flight per thread; HIP-graph replay")
+    return out
 
 
 def simulated_block_bench(torch, tp, synth, steps, warmup):
@@ -504,6 +559,111 @@ def mfma_calibration(torch, tp, iters=20000, nwg=1024):
     return out
 
 
+def _errors(np, got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    d = got - ref
+    return (float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300)),
+            float(np.max(np.abs(d)) / max(np.max(np.abs(ref)), 1e-300)))
+
+
+def oracle_configs(torch, tp, synth):
+    """Every workload configuration: the oracle's wall time on a stated sample,
+    and the GPU path's error against the oracle on that sample (relative
+    Frobenius and largest error relative to the largest reference value)."""
+    import numpy as np
+
+    import oracle
+
+    dev = "cuda:0"
+    f = lambda t: t.detach().to("cpu").to(torch.float64).numpy()  # noqa: E731
+    out = {}
+
+    def entry(name, sample, dt, pairs, bar):
+        e = {"sample": sample, "oracle_s": round(dt, 3), "bar": bar}
+        for what, got, ref in pairs:
+            fro, mx = _errors(np, got, ref)
+            e[what] = {"rel_fro": float(f"{fro:.3e}"), "max_rel": float(f"{mx:.3e}")}
+        out[name] = e
+
+    # tiny fp32, p = 4 simulated: every output, against the unsharded oracle
+    X, W1, b1, W2 = synth.tiny_f32_inputs()
+    tt = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    Yd = torch.empty(4, 4, 512, device=dev)
+    Zp = torch.empty(4, 4, 512, device=dev)
+    Zd = torch.empty(4, 512, device=dev)
+    tp.tp_mlp_simulated(tt(X), tt(W1), tt(W2), 4, Yd, Zp, Zd, act="gelu_tanh", b1=tt(b1))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    Zr = oracle.mlp_unsharded(X, W1, W2, "gelu_tanh", b1=b1)
+    entry("tiny_f32_p4", "all 4 rows (unsharded oracle)", time.perf_counter() - t0,
+          [("Z", f(Zd), Zr)], "rel_fro <= 1e-5")
+
+    bf_bar = "rel_fro <= 5e-3 and max_rel <= 2e-2"
+    # GPT-style GeLU shard, p = 4: the GPU computes every row, the oracle the first 32
+    W = synth.WORKLOADS["gpt_gelu_p4"]
+    X, W1, b1, W2 = synth.gpt_gelu_shard_inputs(W.T, W.d, W.s)
+    Y = torch.empty(W.T, W.s, dtype=torch.bfloat16, device=dev)
+    Z = torch.empty(W.T, W.d, device=dev)
+    tp.tp_mlp_shard(X.to(dev), W1.to(dev), W2.to(dev), 0, 1, Y, Z, act="gelu_tanh",
+                    b1=b1.to(dev))
+    torch.cuda.synchronize()
+    r = 32
+    t0 = time.perf_counter()
+    Yr, Zr = oracle.mlp_shard(f(X[:r]), f(W1), f(W2), 0, 1, "gelu_tanh", b1=f(b1))
+    entry(W.name, f"first {r} of {W.T} token rows", time.perf_counter() - t0,
+          [("Y", f(Y[:r]), Yr), ("Z", f(Z[:r]), Zr)], bf_bar)
+    del Y, Z
+
+    # Llama-70B prefill shard: every row on the GPU, the first 16 in the oracle
+    W = synth.WORKLOADS["llama70b_prefill_tp8"]
+    Wg, Wu, W2 = synth.llama_shard_weights(W.d, W.s)
+    Wgd, Wud, W2d = Wg.to(dev), Wu.to(dev), W2.to(dev)
+    Wg64, Wu64, W264 = f(Wg), f(Wu), f(W2)
+    X = synth.llama_tokens(W.T, W.d)
+    Y = torch.empty(W.T, W.s, dtype=torch.bfloat16, device=dev)
+    Z = torch.empty(W.T, W.d, device=dev)
+    tp.tp_mlp_shard(X.to(dev), Wgd, W2d, 0, 1, Y, Z, act="swiglu", Wu=Wud)
+    torch.cuda.synchronize()
+    r = 16
+    t0 = time.perf_counter()
+    Yr, Zr = oracle.mlp_shard(f(X[:r]), Wg64, W264, 0, 1, "swiglu", Wu=Wu64)
+    entry(W.name, f"first {r} of {W.T} token rows", time.perf_counter() - t0,
+          [("Y", f(Y[:r]), Yr), ("Z", f(Z[:r]), Zr)], bf_bar)
+    del Y, Z
+
+    # decode, T = 1, 8, 64: every row
+    for T in synth.WORKLOADS["llama70b_decode_tp8"].Ts:
+        Xt = synth.llama_tokens(T, W.d)
+        Y = torch.empty(T, W.s, dtype=torch.bfloat16, device=dev)
+        Z = torch.empty(T, W.d, device=dev)
+        tp.tp_mlp_shard(Xt.to(dev), Wgd, W2d, 0, 1, Y, Z, act="swiglu", Wu=Wud)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        Yr, Zr = oracle.mlp_shard(f(Xt), Wg64, W264, 0, 1, "swiglu", Wu=Wu64)
+        entry(f"llama70b_decode_tp8_T{T}", f"all {T} token rows", time.perf_counter() - t0,
+              [("Y", f(Y), Yr), ("Z", f(Z), Zr)], bf_bar)
+    del Wgd, Wud, W2d, Wg64, Wu64, W264
+
+    # simulated TP = 8 block, T = 512: the 8 shards and the reduction on the
+    # GPU; the unsharded oracle on 4 rows
+    W = synth.WORKLOADS["llama70b_block_sim_tp8"]
+    Wg, Wu, W2 = synth.llama_full_weights(W.d, W.k)
+    X = synth.llama_tokens(W.T, W.d)
+    Yp = torch.empty(W.p, W.T, W.s, dtype=torch.bfloat16, device=dev)
+    Zp = torch.empty(W.p, W.T, W.d, device=dev)
+    Z = torch.empty(W.T, W.d, device=dev)
+    tp.tp_mlp_simulated(X.to(dev), Wg.to(dev), W2.to(dev), W.p, Yp, Zp, Z, act="swiglu",
+                        Wu=Wu.to(dev))
+    torch.cuda.synchronize()
+    rows = [0, 171, 342, W.T - 1]
+    Wg64, Wu64, W264 = f(Wg), f(Wu), f(W2)
+    t0 = time.perf_counter()
+    Zr = oracle.mlp_unsharded(f(X[rows]), Wg64, W264, "swiglu", Wu=Wu64)
+    entry(W.name, f"token rows {rows} of {W.T} (unsharded oracle)", time.perf_counter() - t0,
+          [("Z", f(Z[rows]), Zr)], bf_bar)
+    return out
+
+
 def cpu_baseline(synth, target_s=12.0):
     """The CPU oracle, untuned, on a bounded sample of the headline workload:
     the first R token rows of one shard forward (rows are independent)."""
@@ -596,9 +756,10 @@ def main():
         "row_gemm": {"us": round(h["t_row"] * 1e6, 2),
                      "TFLOPs": round(h["flops_row"] / h["t_row"] / 1e12, 2)},
         "timing": {"clock_ramp_s": RAMP_S,
-                   "step": dict(h["step_spread"], method="event pair around each step, eager"),
-                   "col_gemm": dict(h["col_spread"], method="HIP-graph replays of 4 launches"),
-                   "row_gemm": dict(h["row_spread"], method="HIP-graph replays of 4 launches")},
+                   "step": dict(h["step_spread"], method="events around each launch of 50 "
+                                "steps right after the timed region, eager"),
+                   "col_gemm": dict(h["col_spread"], method="the column launch of those steps"),
+                   "row_gemm": dict(h["row_spread"], method="the row launch of those steps")},
     }
     sections = set() if args.quick else set(args.sections.split(","))
     if "decode" in sections:
@@ -628,6 +789,21 @@ def main():
     if "calibration" in sections:
         log("bench: mfma calibration")
         result["mfma_calibration"] = mfma_calibration(torch, tp)
+        log("bench: hbm calibration")
+        result["hbm_calibration"] = hbm_calibration(torch, tp, max(5, args.steps // 2), 2)
+    if "decode" in result:
+        d1 = result["decode"]["T1"]
+        result["roofline_decode"] = {
+            "bound": "hbm", "achieved": d1["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": d1["frac_hbm"], "traffic": None,
+            "kernel": "gemm_bf16_decode_kernel (column step + row step, T = 1)",
+            "step_us": d1["us_per_step"], "bytes_per_step": d1["alg_bytes"]}
+    if "partial_sum" in result:
+        ps = result["partial_sum"]
+        result["roofline_partial_sum"] = {
+            "bound": "hbm", "achieved": ps["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": ps["frac_hbm"], "traffic": None, "kernel": "partial_sum_kernel (8 x fp32 "
+            "[512, 8192] -> [512, 8192])", "kernel_us": ps["us"], "bytes_per_launch": ps["bytes"]}
     if args.copy_calibration:
         a = torch.empty(64 << 20, device="cuda:0")
         b = torch.empty_like(a)
@@ -636,6 +812,9 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(synth)
+        if not args.quick:
+            log("bench: oracle on every configuration")
+            result["cpu_baseline"]["configs"] = oracle_configs(torch, tp, synth)
     print(json.dumps(result), flush=True)
 
 

@@ -1,7 +1,8 @@
 /*
  * tpmlp_calib.h -- measurement aids for the MI355X (gfx950) shard kernels.
  * Not part of the method: these calls help read the kernels' numbers against
- * the hardware, for benchmarks and profiling.
+ * the hardware (the MFMA rate at the clock the power limit allows, the
+ * streaming-read rate of HBM), for benchmarks and profiling.
  */
 #ifndef TPMLP_CALIB_H
 #define TPMLP_CALIB_H
@@ -33,6 +34,23 @@ extern "C" {
  */
 tp_status tp_calib_mfma_bf16(int32_t gaussian, int64_t iters, uint64_t *stats, int32_t nwg,
                              void *stream);
+
+/*
+ * Streaming-read rate of HBM: `nwg` workgroups of 256 threads read `bytes`
+ * (a multiple of 16) of device memory at `buf` exactly once, 16 bytes per load
+ * with the nontemporal hint, the way the few-token kernels stream weights, and
+ * write (almost) nothing.  Timing one launch gives the per-launch read ceiling
+ * of a kernel that streams that many bytes (ramp and drain included); the
+ * caller rotates buffers larger than the 256 MB Infinity Cache to measure HBM.
+ *   sink: device buffer of nwg uint32 (caller-owned; written only in the
+ *         unlikely case that the data folds to one particular word).
+ * Errors: TP_ERR_BAD_SHAPE for nwg < 1 or bytes not a non-negative multiple of
+ * 16, TP_ERR_NULL_POINTER for sink = NULL or buf = NULL with bytes > 0,
+ * TP_ERR_MISALIGNED for buf not 16-byte aligned, TP_ERR_HIP if the launch
+ * fails; nothing is launched on an error, or when bytes = 0.
+ */
+tp_status tp_calib_hbm_read(const void *buf, int64_t bytes, uint32_t *sink, int32_t nwg,
+                            void *stream);
 
 #ifdef __cplusplus
 }

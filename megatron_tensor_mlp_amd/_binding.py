@@ -69,6 +69,7 @@ def library():
     lib.tp_abi_version.argtypes = []
     lib.tp_abi_version.restype = i32
     lib.tp_calib_mfma_bf16.argtypes = [i32, i64, vp, i32, vp]
+    lib.tp_calib_hbm_read.argtypes = [vp, i64, vp, i32, vp]
     lib.tp_qkv_linear.argtypes = [ci, i64, i64, i32, i32, i64, i32, i32, vp, i64, vp, i64, vp,
                                   vp, i64, vp, sz, vp]
     lib.tp_qkv_workspace_bytes.argtypes = [ci, i64, i64, i32, i32, i64, i32]
@@ -147,6 +148,16 @@ def tp_calib_mfma_bf16(gaussian: bool, iters: int, stats, stream=None):
         raise ValueError("stats must be a device int64 tensor of even length")
     _check(library().tp_calib_mfma_bf16(1 if gaussian else 0, iters, _ptr(stats),
                                         stats.numel() // 2, _stream(stream)))
+
+
+def tp_calib_hbm_read(buf, sink, nbytes: int | None = None, stream=None):
+    """Enqueue the streaming-read calibration kernel (include/tpmlp_calib.h) over
+    the first nbytes (default all) of the device tensor `buf`; one workgroup per
+    entry of `sink` (a device int32 tensor)."""
+    if not sink.is_cuda or sink.dtype != torch.int32:
+        raise ValueError("sink must be a device int32 tensor")
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    _check(library().tp_calib_hbm_read(_ptr(buf), n, _ptr(sink), sink.numel(), _stream(stream)))
 
 
 def tp_shard_bounds(k: int, i: int, p: int):

@@ -1241,3 +1241,16 @@ extern "C" tp_status tp_calib_mfma_bf16(int32_t gaussian, int64_t iters, uint64_
   if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
+
+extern "C" tp_status tp_calib_hbm_read(const void *buf, int64_t bytes, uint32_t *sink, int32_t nwg,
+                                       void *stream) {
+  if (nwg < 1 || bytes < 0 || bytes % 16)
+    return fail(TP_ERR_BAD_SHAPE, "nwg = %d must be >= 1 and bytes = %lld a multiple of 16", nwg,
+                (long long)bytes);
+  if (!sink) return fail(TP_ERR_NULL_POINTER, "sink is NULL");
+  if (bytes > 0) TRY(check_ptr("buf", buf));
+  if (bytes == 0) return ok();
+  const hipError_t e = launch_calib_hbm_read(buf, bytes, sink, nwg, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}

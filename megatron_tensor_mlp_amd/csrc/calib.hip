@@ -1,5 +1,7 @@
-// MFMA throughput and shader-clock calibration (a measurement aid, not part of
-// the method).  Each wavefront issues v_mfma_f32_32x32x16_bf16 back to back on
+// Calibration kernels (measurement aids, not part of the method): MFMA
+// throughput with the shader clock, and the streaming-read rate of HBM.
+//
+// MFMA throughput and shader-clock calibration.  Each wavefront issues v_mfma_f32_32x32x16_bf16 back to back on
 // four independent accumulators, its A and B operands cycling through eight
 // register sets so that consecutive products see different data; the
 // workgroup records the shader-clock cycles (s_memtime) and the 100 MHz
@@ -65,7 +67,42 @@ __global__ __launch_bounds__(CAL_THREADS) void calib_mfma_kernel(int gaussian, i
   if (s != s) stats[2 * blockIdx.x] = 0;
 }
 
+// Streaming read of `n16` 16-byte chunks: each thread takes 4 chunks per
+// round, a grid-stride apart, with the nontemporal hint (as the few-token
+// kernels read weights), and folds them into one word; the word is stored
+// only when it equals one particular value, so the loads cannot be dropped
+// and (almost) nothing is written.
+constexpr int HBM_THREADS = 256;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(HBM_THREADS) void calib_hbm_read_kernel(const u32x4 *p, int64_t n16,
+                                                                     uint32_t *sink) {
+  const int64_t stride = (int64_t)gridDim.x * HBM_THREADS;
+  uint32_t acc = 0;
+  int64_t i = (int64_t)blockIdx.x * HBM_THREADS + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(p + i + j * stride);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_calib_hbm_read(const void *buf, int64_t bytes, uint32_t *sink, int nwg,
+                                 hipStream_t s) {
+  hipLaunchKernelGGL(calib_hbm_read_kernel, dim3((unsigned)nwg), dim3(HBM_THREADS), 0, s,
+                     (const u32x4 *)buf, bytes / 16, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_calib_mfma(int gaussian, int64_t iters, uint64_t *stats, int nwg, hipStream_t s) {
   hipLaunchKernelGGL(calib_mfma_kernel, dim3((unsigned)nwg), dim3(CAL_THREADS), 0, s, gaussian,

@@ -52,8 +52,18 @@ constexpr int CPOL_SC1 = 16;
 constexpr int NWAVE = 8;
 constexpr int RC = 16 * NWAVE;  // columns per workgroup
 constexpr int RP = RC * 2;      // bytes per weight row in LDS
-// The split aims at about one workgroup per CU of a 256-CU device.
-constexpr int TARGET_WGS = 256;
+// The split aims at about one workgroup per CU of a 256-CU device: the
+// streaming rate of a CU is what one workgroup reaches, so a CU given two
+// takes twice as long (measured: 448 or 504 workgroups are slower than 224).
+// TPMLP_DECODE_TARGET overrides it, for sweeps (read once).
+int target_wgs() {
+  static int v = [] {
+    const char *e = getenv("TPMLP_DECODE_TARGET");
+    const int t = e ? atoi(e) : 0;
+    return t > 0 ? t : 256;
+  }();
+  return v;
+}
 constexpr int MIN_STAGES = 4;   // fewest k-steps a workgroup streams
 // The workspace starts with a counter area of fixed size, so that calls with
 // different plans (or other entry points) reusing one workspace never take
@@ -127,7 +137,7 @@ DecodePlan make_plan(const GemmArgs &a) {
   pl.bk = pl.mb == 4 ? 64 : 32;
   pl.nblk = (a.N + RC - 1) / RC;
   const int64_t steps = (a.K + pl.bk - 1) / pl.bk;
-  int64_t S = TARGET_WGS / (pl.nblk * pl.nmat);
+  int64_t S = target_wgs() / (pl.nblk * pl.nmat);
   int64_t smax = steps / MIN_STAGES;
   if (smax < 1) smax = 1;
   if (S > smax) S = smax;
@@ -353,8 +363,8 @@ __global__ __launch_bounds__(NWAVE * 64) void gemm_bf16_decode_kernel(const Gemm
   // nothing), and sums gate and up each in k-range order.  Which sum a slot
   // feeds is fixed at compile time: a run-time choice would put a branch, and
   // so a wait, between the loads.  RCH is sized so that the batch stays within
-  // 128 VGPRs; it covers every k-range of the usual plans in one batch.
-  constexpr int RCH0 = 128 / (NMAT * MB * 4);
+  // 64 VGPRs, which keeps the kernel within 128 (two workgroups per CU).
+  constexpr int RCH0 = 64 / (NMAT * MB * 4);
   constexpr int RCH = RCH0 < 2 ? 2 : (RCH0 > 32 ? 32 : RCH0);
   f32x4 sum[NMAT][MB];
 #pragma unroll

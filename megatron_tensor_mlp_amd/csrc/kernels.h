@@ -104,6 +104,10 @@ hipError_t launch_gemm_bf16_decode(const GemmArgs &a, void *ws, hipStream_t s);
 // MFMA throughput / shader-clock calibration (measurement aid).
 hipError_t launch_calib_mfma(int gaussian, int64_t iters, uint64_t *stats, int nwg,
                              hipStream_t s);
+// Streaming-read calibration: nwg workgroups read `bytes` (a multiple of 16)
+// from `buf` once (measurement aid).
+hipError_t launch_calib_hbm_read(const void *buf, int64_t bytes, uint32_t *sink, int nwg,
+                                 hipStream_t s);
 
 // Attention core of one head shard (bf16): O = softmax(Q K^T / sqrt(dh)) V per
 // query head h, key/value head h / (Hq / Hkv); nseq sequences of S tokens.
