@@ -296,7 +296,7 @@ def hbm_calibration(torch, tp, steps, warmup, rotate_bytes=600 << 20):
     the Infinity Cache: the ceiling a single launch of that size reaches, ramp
     and drain included."""
     dev = "cuda:0"
-    nwg = 256 * 8
+    nwg = 1024
     sink = torch.zeros(nwg, dtype=torch.int32, device=dev)
     out = {}
     for name, nbytes in (("col_117MB", 2 * 8192 * 3584 * 2), ("row_59MB", 3584 * 8192 * 2),
@@ -309,8 +309,9 @@ def hbm_calibration(torch, tp, steps, warmup, rotate_bytes=600 << 20):
                      "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
                      "rotation_copies": copies}
         del bufs, fns
-    out["kernel"] = ("tp_calib_hbm_read: 2048 workgroups x 256 threads, 16-byte nontemporal "
-                     "loads, 4 in flight per thread; HIP-graph replay")
+    out["kernel"] = ("tp_calib_hbm_read: 1024 workgroups x 256 threads, each a contiguous "
+                     "1/1024 of the buffer, 16-byte nontemporal loads, 8 in flight per thread; "
+                     "HIP-graph replay")
     return out
 
 

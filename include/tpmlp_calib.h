@@ -37,9 +37,9 @@ tp_status tp_calib_mfma_bf16(int32_t gaussian, int64_t iters, uint64_t *stats, i
 
 /*
  * Streaming-read rate of HBM: `nwg` workgroups of 256 threads read `bytes`
- * (a multiple of 16) of device memory at `buf` exactly once, 16 bytes per load
- * with the nontemporal hint, the way the few-token kernels stream weights, and
- * write (almost) nothing.  Timing one launch gives the per-launch read ceiling
+ * (a multiple of 16) of device memory at `buf` exactly once, each workgroup a
+ * contiguous 1/nwg of it, 16 bytes per load with the nontemporal hint (as the
+ * few-token kernels stream weights), and write (almost) nothing.  Timing one launch gives the per-launch read ceiling
  * of a kernel that streams that many bytes (ramp and drain included); the
  * caller rotates buffers larger than the 256 MB Infinity Cache to measure HBM.
  *   sink: device buffer of nwg uint32 (caller-owned; written only in the

@@ -1,11 +1,11 @@
 // Calibration kernels (measurement aids, not part of the method): MFMA
 // throughput with the shader clock, and the streaming-read rate of HBM.
 //
-// MFMA throughput and shader-clock calibration.  Each wavefront issues v_mfma_f32_32x32x16_bf16 back to back on
-// four independent accumulators, its A and B operands cycling through eight
-// register sets so that consecutive products see different data; the
-// workgroup records the shader-clock cycles (s_memtime) and the 100 MHz
-// constant-clock ticks (s_memrealtime) it spent.
+// MFMA throughput and shader-clock calibration.  Each wavefront issues
+// v_mfma_f32_32x32x16_bf16 back to back on four independent accumulators, its
+// A and B operands cycling through eight register sets so that consecutive
+// products see different data; the workgroup records the shader-clock cycles
+// (s_memtime) and the 100 MHz constant-clock ticks (s_memrealtime) it spent.
 #include "device_common.hpp"
 #include "kernels.h"
 
@@ -67,28 +67,35 @@ __global__ __launch_bounds__(CAL_THREADS) void calib_mfma_kernel(int gaussian, i
   if (s != s) stats[2 * blockIdx.x] = 0;
 }
 
-// Streaming read of `n16` 16-byte chunks: each thread takes 4 chunks per
-// round, a grid-stride apart, with the nontemporal hint (as the few-token
-// kernels read weights), and folds them into one word; the word is stored
-// only when it equals one particular value, so the loads cannot be dropped
-// and (almost) nothing is written.
+// Streaming read of `n16` 16-byte chunks: workgroup b reads the contiguous
+// range [b c, (b+1) c), c = ceil(n16 / nwg), its 256 threads on consecutive
+// 16-byte chunks, 8 loads in flight per thread, with the nontemporal hint (as
+// the few-token kernels read weights).  The loads are folded into one word,
+// stored only when it equals one particular value, so they cannot be dropped
+// and (almost) nothing is written.  Of the patterns measured (a grid-stride
+// walk over the whole buffer, this per-workgroup range, 2 to 16 loads in
+// flight, 256 to 8192 workgroups, with and without the hint) this one read
+// fastest.
 constexpr int HBM_THREADS = 256;
+constexpr int HBM_UNROLL = 8;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(HBM_THREADS) void calib_hbm_read_kernel(const u32x4 *p, int64_t n16,
                                                                      uint32_t *sink) {
-  const int64_t stride = (int64_t)gridDim.x * HBM_THREADS;
+  const int64_t c = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t beg = (int64_t)blockIdx.x * c;
+  const int64_t end = beg + c < n16 ? beg + c : n16;
   uint32_t acc = 0;
-  int64_t i = (int64_t)blockIdx.x * HBM_THREADS + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    u32x4 v[4];
+  int64_t i = beg + threadIdx.x;
+  for (; i + (HBM_UNROLL - 1) * HBM_THREADS < end; i += HBM_UNROLL * HBM_THREADS) {
+    u32x4 v[HBM_UNROLL];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(p + i + j * stride);
+    for (int j = 0; j < HBM_UNROLL; ++j) v[j] = __builtin_nontemporal_load(p + i + j * HBM_THREADS);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+    for (int j = 0; j < HBM_UNROLL; ++j) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
   }
-  for (; i < n16; i += stride) {
+  for (; i < end; i += HBM_THREADS) {
     const u32x4 v = __builtin_nontemporal_load(p + i);
     acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
