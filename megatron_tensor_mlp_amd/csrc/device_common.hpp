@@ -37,6 +37,34 @@ __device__ __forceinline__ float activate(float x) {
 
 __device__ __forceinline__ float silu(float x) { return activate<ACT_SWIGLU>(x); }
 
+// Epilogue forms of the activations whose result is rounded to bf16 next:
+// the exponential and the reciprocal are single instructions (v_exp_f32,
+// v_rcp_f32, each within about an fp32 ulp), far below bf16's 2^-8.
+//   SiLU:  x / (1 + 2^(-x log2 e))
+//   tanh:  1 - 2 / (1 + 2^(2 z log2 e))   (for the GeLU tanh form)
+__device__ __forceinline__ float silu_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+__device__ __forceinline__ float tanh_fast(float z) {
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(2.8853900817779268f * z));
+}
+template <int ACT>
+__device__ __forceinline__ float activate_fast(float x) {
+  if constexpr (ACT == ACT_GELU_TANH) {
+    const float c = 0.7978845608028654f;  // sqrt(2/pi)
+    return 0.5f * x * (1.0f + tanh_fast(c * (x + 0.044715f * x * x * x)));
+  } else if constexpr (ACT == ACT_SWIGLU) {
+    return silu_fast(x);
+  } else {
+    return activate<ACT>(x);
+  }
+}
+
+// Lanes 2j and 2j+1 exchange a 32-bit value (DPP quad permutation 1,0,3,2).
+__device__ __forceinline__ uint32_t swap_adjacent_lanes(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
 // Derivatives of the activations (for the backward pass), from the
 // definitions above by the chain rule:
 //   GeLU tanh form: with t = tanh(sqrt(2/pi) (x + 0.044715 x^3)),

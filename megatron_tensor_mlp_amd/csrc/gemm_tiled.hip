@@ -444,6 +444,44 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
         }
       }
     }
+  } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_ACT) {
+    // The activation in fp32, rounded to bf16.  Lanes 2j and 2j+1 hold
+    // adjacent columns of the same rows; for each pair of rows they swap one
+    // value, so that each stores two adjacent columns of one row as one 4-byte
+    // word (half the store instructions, 64-byte runs per row).  N is a
+    // multiple of 8, so a column pair is in range or out of range as a whole.
+    bf16 *C = (bf16 *)p.C + g * p.sC;
+    const bool odd = lane & 1;
+    const bf16 *bias = p.bias ? (const bf16 *)p.bias + g * p.sBias : nullptr;
+#pragma unroll
+    for (int f = 0; f < (DUAL ? NB / 2 : NB); ++f) {
+      const int64_t col = n0 + (DUAL ? WN / 2 : WN) * wn + 32 * f + (lane & 31);
+      if (col >= N) continue;
+      const int64_t col0 = col & ~int64_t(1);
+      float bv = 0.0f;
+      if constexpr (EPI == EPI_ACT)
+        if (bias) bv = (float)bias[src_col(p, col)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          float y0, y1;
+          if constexpr (DUAL) {
+            y0 = silu_fast(acc[i][f][v]) * acc[i][f + NB / 2][v];
+            y1 = silu_fast(acc[i][f][v + 1]) * acc[i][f + NB / 2][v + 1];
+          } else {
+            y0 = activate_fast<ACT>(acc[i][f][v] + bv);
+            y1 = activate_fast<ACT>(acc[i][f][v + 1] + bv);
+          }
+          const uint32_t b0 = __builtin_bit_cast(uint16_t, to_bf16(y0));
+          const uint32_t b1 = __builtin_bit_cast(uint16_t, to_bf16(y1));
+          const uint32_t recv = swap_adjacent_lanes(odd ? b0 : b1);
+          // even lane: row of v, columns (col0, col0+1); odd lane: row of v+1.
+          const uint32_t word = odd ? (recv | (b1 << 16)) : (b0 | (recv << 16));
+          const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3) + (odd ? 1 : 0);
+          if (row < M) *(uint32_t *)(C + row * p.ldc + col0) = word;
+        }
+    }
   } else if constexpr (DUAL) {
     bf16 *C = (bf16 *)p.C + g * p.sC;
     bf16 *C2 = (bf16 *)p.C2;
