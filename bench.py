@@ -7,8 +7,10 @@ A step is one forward of one GPU's shard of the Llama-70B SwiGLU MLP at TP = 8
 SiLU(g) * u -> bf16 Y_i) then the row step (Y_i W2_i -> fp32 partial Z_i),
 i.e. the two launches tp_mlp_shard makes.  Inputs are seeded synthetic bf16
 tensors already resident in HBM.  The timed region is bracketed by HIP events
-on the launch stream; per-kernel durations come from HIP-graph replays (events
-only at the ends of a batch of launches).
+on the launch stream; the headline GEMMs' per-launch durations are the
+medians over 50 further steps with an event after each launch (the steady
+state of the timed steps); the secondary sections time HIP-graph replays
+(events only at the ends of a batch of launches).
 
 Prints ONE JSON line.  `value` is the step's algorithmic TFLOP/s (2*T*d*(k/p)
 flops per GEMM, three GEMMs).  Secondary fields report the few-token (decode)
@@ -195,9 +197,9 @@ def ramp(torch, fn_list, seconds=RAMP_S):
 
 def headline(torch, tp, synth, steps, warmup):
     """The timed region: `steps` shard forwards back to back, after the clock
-    ramp and `warmup` untimed steps.  Per-kernel durations come from HIP-graph
-    replays of each launch alone (events only at the ends of a replay batch,
-    so no event sits between two kernels)."""
+    ramp and `warmup` untimed steps.  Per-kernel durations are the medians
+    over 50 more steps with an event on the launch stream after each launch,
+    so the two legs of a step add up to the step."""
     W = synth.WORKLOADS["llama70b_prefill_tp8"]
     dev = "cuda:0"
     Wg, Wu, W2 = (t.to(dev) for t in synth.llama_shard_weights(W.d, W.s))
