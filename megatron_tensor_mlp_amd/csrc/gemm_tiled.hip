@@ -38,6 +38,7 @@
 #include "device_common.hpp"
 #include "kernels.h"
 #include "lds_dma.hpp"
+#include "tiled_geometry.hpp"
 
 namespace tpmlp {
 namespace {
@@ -46,87 +47,41 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-constexpr int BN = 256;               // tile columns (SwiGLU: 128 gate + 128 up)
-constexpr int GROUP_M = 4;            // row-tiles walked together for L2 reuse
-
-// XOR masks on the 16-byte unit index of an LDS row.
-//  A rows (2*BK bytes = BK/8 units): fragment reads touch 8 or 16 consecutive
-//  rows at one logical unit; the mask spreads them over distinct banks.
-template <int BK>
-__device__ __forceinline__ int swz_a(int r) {
-  if constexpr (BK == 64)
-    return ((r >> 1) ^ (r << 2)) & 7;
-  else
-    return ((r >> 1) ^ (r >> 2)) & 3;
-}
-//  B rows (512 or 256 B): a transposing read touches 4 consecutive k rows x
-//  32 or 64 bytes; rows k..k+3 get masks 0, 4, 10, 14 (distinct 64-byte
-//  segments and distinct 32-byte pairs within them).
-__device__ __forceinline__ int swz_b(int k) { return ((k & 3) << 2) ^ (k & 2); }
-
-// Workgroup b runs on XCD b % 8.  Give every XCD a contiguous run of the tile
-// order (a bijection for any total), then walk GROUP_M row-tiles at a time so
-// the tiles resident on one XCD share A and B panels in its L2.
-__device__ __forceinline__ void tile_coords(int bid, int tilesM, int tilesN, int total, int &g,
-                                            int &tm, int &tn) {
-  const int xcd = bid & 7, idx = bid >> 3;
-  const int q = total >> 3, r = total & 7;
-  const int t = xcd * q + (xcd < r ? xcd : r) + idx;
-  const int per = tilesM * tilesN;
-  g = t / per;
-  const int u = t - g * per;
-  const int span = GROUP_M * tilesN;
-  const int grp = u / span;
-  const int first = grp * GROUP_M;
-  const int gsz = (tilesM - first) < GROUP_M ? (tilesM - first) : GROUP_M;
-  const int w = u - grp * span;
-  tm = first + w % gsz;
-  tn = w / gsz;
-}
+using tiled::BN;
+using tiled::swz_a;
+using tiled::swz_b;
+using tiled::tile_coords;
+static_assert(tiled::OOB_OFF == OOB, "one out-of-range offset");
 
 template <int EPI, int ACT, int BK, int NST, int NWAVE, int BM, int LAY>
 __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const GemmArgs p) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE);
-  constexpr bool TA = (LAY == LAY_TN);  // A held as A^T [K,M]: m contiguous
-  constexpr bool TB = (LAY == LAY_NT);  // B held as B^T [N,K]: k contiguous
-  constexpr int NOUT = DUAL ? BN / 2 : BN;       // output columns per tile
+  using G = tiled::Geom<BK, NWAVE, BM, DUAL, LAY>;
+  constexpr bool TA = G::TA, TB = G::TB;
+  constexpr int NOUT = G::NOUT;                  // output columns per tile
   constexpr int KK = BK / 16;                    // 16-k MFMA slices per step
-  constexpr int WMW = BM / 128;                  // waves along M (128 rows each)
-  constexpr int WNW = NWAVE / WMW;               // waves along N
-  constexpr int WN = BN / WNW;                   // accumulator columns per wave
-  constexpr int NB = WN / 32;                    // 32-column B fragments per wave
+  constexpr int WNW = G::WNW;                    // waves along N
+  constexpr int WN = G::WN;                      // accumulator columns per wave
+  constexpr int NB = G::NB;                      // 32-column B fragments per wave
   constexpr int NMF = 4 * NB;                    // MFMAs per slice per wave
   // A fragment is one 16-byte LDS read when its operand is k-contiguous in LDS,
   // two transposing half reads when it is m- (n-) contiguous.
   constexpr int PA = TA ? 2 : 1;                 // LDS reads per A fragment
   constexpr int PB = TB ? 1 : 2;                 // LDS reads per B fragment
   constexpr int NREAD = 4 * PA + NB * PB;        // LDS reads per slice per wave
-  constexpr int A_BYTES = BM * BK * 2;           // [BM rows][BK k]
-  constexpr int B_BYTES = BK * BN * 2;           // [BK k][256 cols] or 2 x [BK][128]
-  constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  constexpr int AUNITS = BK / 8;                 // 16-byte units per k-contiguous row
-  constexpr int AROWS_PER_LOAD = 64 / AUNITS;    // k-contiguous rows one wave-wide 1 KiB load fills
-  constexpr int APITCH = TA ? 2 * BM : 2 * BK;   // bytes per A row in LDS (k rows when TA)
-  constexpr int ATUNITS = BM / 8;                // 16-byte units per k row of A^T
-  constexpr int AKROWS_PER_LOAD = 1024 / APITCH; // k rows of A^T one load fills
-  constexpr int A_LOADS = A_BYTES / 1024 / NWAVE;  // per wave
-  constexpr int BREG = DUAL ? BN / 2 : BN;       // columns per B region
-  constexpr int BPITCH = BREG * 2;               // bytes per B row
-  constexpr int BUNITS = BREG / 8;               // 16-byte units per B row
-  constexpr int BROWS_PER_LOAD = 1024 / BPITCH;  // B rows one wave-wide load fills
-  constexpr int B_LOADS = B_BYTES / 1024 / NWAVE;  // per wave
-  constexpr int B_LOADS_PER_REGION = (B_BYTES / 1024) / (DUAL ? 2 : 1);
-  constexpr int LPS = A_LOADS + B_LOADS;         // loads per wave per stage
+  constexpr int A_BYTES = G::A_BYTES, STAGE_BYTES = G::STAGE_BYTES;
+  constexpr int APITCH = G::APITCH, BPITCH = G::BPITCH;
+  constexpr int A_LOADS = G::A_LOADS, B_LOADS = G::B_LOADS, LPS = G::LPS;
   // Slot (MFMA of a slice) that issues fragment read q of the next slice:
   // R0 + q / RPS, centred in the slice.
   constexpr int RPS = (NREAD + NMF - 1) / NMF;   // reads per slot, at most
   constexpr int NRS = (NREAD + RPS - 1) / RPS;   // slots carrying reads
   constexpr int R0 = (NMF - NRS) / 2;            // first slot carrying a fragment read
   static_assert(NST >= 2 && NST <= 4, "2..4 stages");
-  static_assert((BM == 128 || BM == 256) && NWAVE % WMW == 0, "tile rows");
+  static_assert((BM == 128 || BM == 256) && NWAVE % G::WMW == 0, "tile rows");
   static_assert(NST * STAGE_BYTES <= 160 * 1024, "LDS");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && LPS <= NMF, "load split");
-  static_assert(B_LOADS_PER_REGION % B_LOADS == 0, "a wave's B loads stay in one region");
+  static_assert(G::B_LOADS_PER_REGION % B_LOADS == 0, "a wave's B loads stay in one region");
 
   // One LDS array per stage.
   __shared__ __attribute__((aligned(1024))) char smem0[STAGE_BYTES];
@@ -144,62 +99,20 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
 
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * NOUT;
-  const bf16 *A = (const bf16 *)p.A + g * p.sA + (TA ? m0 : m0 * p.lda);
-  // B offsets are taken from the matrix base: a column map may send a tile's
-  // columns to separate column blocks of B.
-  const bf16 *B = (const bf16 *)p.B + g * p.sB;
-  const bf16 *B2 = DUAL ? (const bf16 *)p.B2 + g * p.sB2 : nullptr;
+  const bf16 *A = G::template a_tile<bf16>(p, g, m0);
+  const bf16 *B = G::template b_group<bf16>(p, g);
+  const bf16 *B2 = G::template b2_group<bf16>(p, g);
 
   // ---- per-lane load offsets (bytes, relative to the k-step's base) -------
-  // A: load j of wave w fills rows (A_LOADS w + j) * AROWS_PER_LOAD + lane/AUNITS,
-  // physical unit lane % AUNITS (logical unit = physical ^ swizzle).
   uint32_t a_off[A_LOADS];
   int a_kof[A_LOADS];
 #pragma unroll
-  for (int j = 0; j < A_LOADS; ++j) {
-    if constexpr (!TA) {
-      const int r = (A_LOADS * wave + j) * AROWS_PER_LOAD + lane / AUNITS;
-      const int lu = (lane % AUNITS) ^ swz_a<BK>(r);
-      a_kof[j] = 8 * lu;
-      a_off[j] = (m0 + r < M) ? (uint32_t)((r * p.lda + 8 * lu) * 2) : OOB;
-    } else {
-      // A^T: load j fills k rows (A_LOADS w + j) * AKROWS_PER_LOAD + lane / ATUNITS
-      // of BM m each; lane -> physical unit lane % ATUNITS.
-      const int k = (A_LOADS * wave + j) * AKROWS_PER_LOAD + lane / ATUNITS;
-      const int lu = (lane % ATUNITS) ^ swz_b(k);
-      a_kof[j] = k;
-      a_off[j] = (m0 + 8 * lu < M) ? (uint32_t)((k * p.lda + 8 * lu) * 2) : OOB;
-    }
-  }
-  // B: load j of wave w is load gi = B_LOADS w + j of the tile, filling 1 KiB
-  // of a B region = BROWS_PER_LOAD rows; lane -> row lane / BUNITS, unit
-  // lane % BUNITS.  With SwiGLU the first half of the loads fill the gate
-  // region and the second half the up region (the first and second half of
-  // the waves).
+  for (int j = 0; j < A_LOADS; ++j) G::a_load(p, m0, wave, lane, j, a_off[j], a_kof[j]);
   uint32_t b_off[B_LOADS];
   int b_k[B_LOADS];
-  const bool b_up = DUAL && (B_LOADS * wave >= B_LOADS_PER_REGION);
+  const bool b_up = G::b_up(wave);
 #pragma unroll
-  for (int j = 0; j < B_LOADS; ++j) {
-    const int gi = B_LOADS * wave + j;
-    const int li = gi % B_LOADS_PER_REGION;
-    const int64_t ld = b_up ? p.ldb2 : p.ldb;
-    if constexpr (!TB) {
-      const int k = li * BROWS_PER_LOAD + lane / BUNITS;
-      const int lu = (lane % BUNITS) ^ swz_b(k);
-      const int64_t col = n0 + 8 * lu;  // output column of this 16-byte unit
-      b_k[j] = k;
-      b_off[j] = (col < N) ? (uint32_t)((k * ld + src_col(p, col)) * 2) : OOB;
-    } else {
-      // B^T: load j fills n rows li * AROWS_PER_LOAD + lane / AUNITS of the
-      // region, BK k each, like the rows of A.
-      const int r = li * AROWS_PER_LOAD + lane / AUNITS;
-      const int lu = (lane % AUNITS) ^ swz_a<BK>(r);
-      const int64_t col = n0 + r;  // output column of this row
-      b_k[j] = 8 * lu;
-      b_off[j] = (col < N) ? (uint32_t)((src_col(p, col) * ld + 8 * lu) * 2) : OOB;
-    }
-  }
+  for (int j = 0; j < B_LOADS; ++j) G::b_load(p, n0, wave, lane, j, b_off[j], b_k[j]);
 
   // This wave's loads of k-step dkt into `stage`, one at a time (q < LPS).
   // Past the last step (dkt >= KT) every lane gets an out-of-range offset: the
@@ -214,23 +127,16 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
     LoadCtx c;
     c.live = dkt < KT;
     c.k0 = (int64_t)(c.live ? dkt : 0) * BK;
-    c.ra = rsrc(TA ? A + c.k0 * p.lda : A + c.k0);
-    if constexpr (TB)  // k past ksplit comes from the second matrix (same ld)
-      c.rb = rsrc(p.ksplit > 0 && c.k0 >= p.ksplit ? (const bf16 *)p.B2 + (c.k0 - p.ksplit)
-                                                    : (b_up ? B2 : B) + c.k0);
-    else
-      c.rb = rsrc(b_up ? B2 + c.k0 * p.ldb2 : B + c.k0 * p.ldb);
+    c.ra = rsrc(G::a_step(p, A, c.k0));
+    c.rb = rsrc(G::b_step(p, B, B2, b_up, c.k0));
     return c;
   };
   auto issue_load = [&](const LoadCtx &c, char *stage, int q) {
     if (q < A_LOADS) {
-      const uint32_t off = (c.live && c.k0 + a_kof[q] < K) ? a_off[q] : OOB;
-      dma16(c.ra, stage + (A_LOADS * wave + q) * 1024, off);
+      dma16(c.ra, stage + G::a_lds(wave, q), G::step_off(c.live, c.k0, a_kof[q], K, a_off[q]));
     } else {
       const int j = q - A_LOADS;
-      const uint32_t off = (c.live && c.k0 + b_k[j] < K) ? b_off[j] : OOB;
-      // regions are consecutive, so tile load gi fills bytes [gi KiB, +1 KiB)
-      dma16(c.rb, stage + A_BYTES + (B_LOADS * wave + j) * 1024, off);
+      dma16(c.rb, stage + G::b_lds(wave, j), G::step_off(c.live, c.k0, b_k[j], K, b_off[j]));
     }
   };
 
@@ -404,18 +310,18 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
   // ---- epilogue ---------------------------------------------------------------
   // 32x32 accumulator layout: lane holds column (lane & 31) and rows
   // 8 (v / 4) + 4 (lane / 32) + (v % 4), v = 0..15.
-  const int64_t rbase = m0 + 128 * wm + 4 * (lane >> 5);
+  const int64_t rbase = G::row_base(m0, wm, lane);
   if constexpr (EPI == EPI_F32) {
     float *C = (float *)p.C + g * p.sC;
 #pragma unroll
     for (int f = 0; f < NB; ++f) {
-      const int64_t col = n0 + WN * wn + 32 * f + (lane & 31);
+      const int64_t col = G::out_col(n0, wn, f, lane);
       if (col >= N) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+          const int64_t row = G::out_row(rbase, i, v);
           if (row < M) C[row * p.ldc + col] = acc[i][f][v];
         }
     }
@@ -426,20 +332,20 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
     float *C = (float *)p.C + g * p.sC;
 #pragma unroll
     for (int f = 0; f < NB; ++f) {
-      const int64_t col = n0 + WN * wn + 32 * f + (lane & 31);
+      const int64_t col = G::out_col(n0, wn, f, lane);
       if (col >= N) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float old[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+          const int64_t row = G::out_row(rbase, i, v);
           old[v] = C[(row < M ? row : M - 1) * p.ldc + col];
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+          const int64_t row = G::out_row(rbase, i, v);
           if (row < M) C[row * p.ldc + col] = old[v] + acc[i][f][v];
         }
       }
@@ -455,7 +361,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
     const bf16 *bias = p.bias ? (const bf16 *)p.bias + g * p.sBias : nullptr;
 #pragma unroll
     for (int f = 0; f < (DUAL ? NB / 2 : NB); ++f) {
-      const int64_t col = n0 + (DUAL ? WN / 2 : WN) * wn + 32 * f + (lane & 31);
+      const int64_t col = G::out_col(n0, wn, f, lane);
       if (col >= N) continue;
       const int64_t col0 = col & ~int64_t(1);
       float bv = 0.0f;
@@ -478,7 +384,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
           const uint32_t recv = swap_adjacent_lanes(odd ? b0 : b1);
           // even lane: row of v, columns (col0, col0+1); odd lane: row of v+1.
           const uint32_t word = odd ? (recv | (b1 << 16)) : (b0 | (recv << 16));
-          const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3) + (odd ? 1 : 0);
+          const int64_t row = G::out_row(rbase, i, v) + (odd ? 1 : 0);
           if (row < M) *(uint32_t *)(C + row * p.ldc + col0) = word;
         }
     }
@@ -487,13 +393,13 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
     bf16 *C2 = (bf16 *)p.C2;
 #pragma unroll
     for (int f = 0; f < NB / 2; ++f) {
-      const int64_t col = n0 + (WN / 2) * wn + 32 * f + (lane & 31);
+      const int64_t col = G::out_col(n0, wn, f, lane);
       if (col >= N) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+          const int64_t row = G::out_row(rbase, i, v);
           if (row < M) {
             const float gv = acc[i][f][v], uv = acc[i][f + NB / 2][v];
             C[row * p.ldc + col] = to_bf16(silu(gv) * uv);
@@ -511,7 +417,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
     const bf16 *H = (const bf16 *)p.aux;
 #pragma unroll
     for (int f = 0; f < NB; ++f) {
-      const int64_t col = n0 + WN * wn + 32 * f + (lane & 31);
+      const int64_t col = G::out_col(n0, wn, f, lane);
       if (col >= N) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -521,7 +427,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
         float hv[NH][16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+          const int64_t row = G::out_row(rbase, i, v);
           const int64_t r = row < M ? row : M - 1;
 #pragma unroll
           for (int q = 0; q < NH; ++q) hv[q][v] = (float)H[r * p.ldaux + q * N + col];
@@ -529,7 +435,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+          const int64_t row = G::out_row(rbase, i, v);
           if (row >= M) continue;
           const float dy = acc[i][f][v];
           if constexpr (EPI == EPI_DACT) {
@@ -548,14 +454,14 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
     const bf16 *bias = p.bias ? (const bf16 *)p.bias + g * p.sBias : nullptr;
 #pragma unroll
     for (int f = 0; f < NB; ++f) {
-      const int64_t col = n0 + WN * wn + 32 * f + (lane & 31);
+      const int64_t col = G::out_col(n0, wn, f, lane);
       if (col >= N) continue;
       const float bv = bias ? (float)bias[src_col(p, col)] : 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+          const int64_t row = G::out_row(rbase, i, v);
           if (row < M) {
             C[row * p.ldc + col] = to_bf16(activate<ACT>(acc[i][f][v] + bv));
             if constexpr (EPI == EPI_ACT_SAVE) C2[row * p.ldc2 + col] = to_bf16(acc[i][f][v] + bv);

@@ -201,7 +201,7 @@ def test_scan_catches_the_descriptor_helper_variant(tmp_path):
     variant = (src[:a] + helper + src[b:]).replace('asm volatile("s_nop 4\\n\\tbuffer_load',
                                                    'asm volatile("buffer_load')
     assert "s_nop 4\\n\\tbuffer_load" not in variant
-    for name in ("gemm_tiled.hip", "device_common.hpp", "kernels.h"):
+    for name in ("gemm_tiled.hip", "device_common.hpp", "kernels.h", "tiled_geometry.hpp"):
         (tmp_path / name).write_text(open(os.path.join(build.CSRC, name)).read())
     (tmp_path / "lds_dma.hpp").write_text(variant)
     out = tmp_path / "variant.s"
