@@ -306,12 +306,14 @@ __global__ __launch_bounds__(NGRP * 256, 1) void attention_kernel(AttnArgs p) {
     issue(0, 0, 1);
     if (my_n > 1) issue(1, 1, 0);
   }
-  for (int it = 0; it < half; ++it) {
+  // One iteration; the score registers alternate between sc and sn (the loop
+  // below is unrolled by two) instead of being copied.
+  auto body = [&](int it, f32x4(&sc)[4], f32x4(&sn)[4]) {
     // V(it) and K(it+1) have landed (this wave's loads; after the barrier,
     // every wave's), and every wave is done with K(it) and V(it-1).
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
     wg_barrier();
-    if (it >= my_n) continue;
+    if (it >= my_n) return;
     if (it + 2 < my_n) issue(it + 2, it & 1, 0);
     if (it + 1 < my_n) {
       issue(it + 1, (it + 1) & 1, 1);
@@ -333,8 +335,10 @@ __global__ __launch_bounds__(NGRP * 256, 1) void attention_kernel(AttnArgs p) {
       cur = blk;
     }
     softmax_pv(sc, smem[grp][it & 1][1], blk, tile_k0(it));
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sc[kb] = sn[kb];
+  };
+  for (int it = 0; it < half; it += 2) {
+    body(it, sc, sn);
+    if (it + 1 < half) body(it + 1, sn, sc);
   }
   // No tile load may still be writing LDS when it is reused below or by the
   // next workgroup.
