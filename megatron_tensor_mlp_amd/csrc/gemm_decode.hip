@@ -35,6 +35,7 @@
 // round trip.
 #include <cstdlib>
 
+#include "decode_geometry.hpp"
 #include "device_common.hpp"
 #include "kernels.h"
 #include "lds_dma.hpp"
@@ -49,9 +50,13 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 // Cache-policy operand of the buffer builtins: sc1, the agent-coherent policy.
 constexpr int CPOL_SC1 = 16;
 
-constexpr int NWAVE = 8;
-constexpr int RC = 16 * NWAVE;  // columns per workgroup
-constexpr int RP = RC * 2;      // bytes per weight row in LDS
+using decode::Geo;
+using decode::NWAVE;
+using decode::RC;
+using decode::RP;
+using decode::swz_w;
+using decode::swz_x;
+static_assert(decode::OOB_OFF == OOB, "one out-of-range offset");
 // The split aims at about one workgroup per CU of a 256-CU device: the
 // streaming rate of a CU is what one workgroup reaches, so a CU given two
 // takes twice as long (measured: 448 or 504 workgroups are slower than 224).
@@ -71,44 +76,6 @@ constexpr int MIN_STAGES = 4;   // fewest k-steps a workgroup streams
 // above it.
 constexpr int64_t MAX_BLOCKS = kWsMaxBlocks;  // column blocks per call
 constexpr size_t CTR_AREA = kWsCounterBytes;
-
-// Geometry of one configuration: a stage holds BK k rows of 128 columns and
-// the matching token rows.
-template <int MB, int BK, int NST>
-struct Geo {
-  static constexpr int KS = BK / 32;             // 32-k MFMA slices per stage
-  static constexpr int WB = BK * RP;             // weight bytes per stage
-  static constexpr int XP = BK * 2;              // bytes per token row
-  static constexpr int XB = 16 * MB * XP;        // token bytes per stage
-  static constexpr int SB = WB + XB;             // stage bytes
-  static constexpr int WL = WB / 1024 / NWAVE;   // 1 KiB weight loads per wave per stage
-  // Token rows: XB / 8 bytes per wave, in 1 KiB loads (16 B per lane) when
-  // there are at least that many, else in 256 B loads (4 B per lane; one
-  // 128 B load from half the lanes for the smallest tile).
-  static constexpr int XW = XB / NWAVE;
-  static constexpr int XLB = XW >= 1024 ? 1024 : 256;
-  static constexpr int XL = XW >= XLB ? XW / XLB : 1;
-  static constexpr int LPS = WL + XL;            // loads per wave per stage
-  static constexpr int PF = NWAVE * MB * 256;    // partial floats per workgroup (one slot)
-  static_assert(BK == 32 || BK == 64, "stage depth");
-  static_assert(WL >= 1, "loads");
-  static_assert(NST >= 3 && NST * SB <= 160 * 1024, "LDS");
-};
-
-// Swizzle mask (XOR on the 16-byte unit index of a row) that spreads the
-// fragment reads over distinct banks: one transposing read takes 8 rows (two
-// runs of 4 consecutive rows, 8 apart) per 32 lanes, and 256 B rows all start
-// at bank 0, so the mask sends those rows to 8 distinct 32-byte bank groups.
-__device__ __forceinline__ int swz_w(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); }
-// Token rows are 128 or 64 B; one fragment read takes 16 consecutive rows per
-// 16 lanes at one logical unit, which the mask sends to 16 distinct units.
-template <int XP>
-__device__ __forceinline__ int swz_x(int r) {
-  if constexpr (XP == 128)
-    return (r >> 1) & 7;
-  else
-    return (r >> 2) & 3;
-}
 
 struct DecodePlan {
   int64_t nblk;  // output column blocks
@@ -171,7 +138,7 @@ __device__ __forceinline__ void store_out(const GemmArgs &p, int64_t col, int la
   for (int m = 0; m < MB; ++m)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int64_t row = 16 * m + 4 * (lane >> 4) + v;
+      const int64_t row = decode::out_row(m, lane, v);
       if (row >= p.M) continue;
       if constexpr (EPI == EPI_SWIGLU)
         ((bf16 *)p.C)[row * p.ldc + col] = to_bf16(silu(acc[m][v]) * up[m][v]);
@@ -195,43 +162,26 @@ __global__ __launch_bounds__(NWAVE * 64) void gemm_bf16_decode_kernel(const Gemm
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Grid order: for each k-range, the gate column blocks, then the up ones.
-  const int64_t wide = blockIdx.x % (NMAT * nblk), s = blockIdx.x / (NMAT * nblk);
-  const bool up = DUAL && wide >= nblk;
-  const int64_t blk = up ? wide - nblk : wide;
+  int64_t blk, s;
+  bool up;
+  decode::wg_coords(blockIdx.x, NMAT, nblk, blk, s, up);
   const bf16 *W = (const bf16 *)(up ? p.B2 : p.B);
   const int64_t ldw = up ? p.ldb2 : p.ldb;
-  const int64_t M = p.M, N = p.N;
-  const int64_t kbeg = s * kc;
-  const int64_t kend = (kbeg + kc < p.K) ? kbeg + kc : p.K;
+  const int64_t M = p.M;
+  int64_t kbeg, kend;
+  decode::k_range(s, kc, p.K, kbeg, kend);
   const int nstages = (int)((kend - kbeg + BK - 1) / BK);
   const int64_t n0 = blk * RC;  // first column of the block
 
   // ---- per-lane load offsets, relative to a stage's k base -----------------
-  // Weight load gi = WL w + j fills 1 KiB = 4 rows of 256 B; lane -> row
-  // 4 gi + lane / 16, physical unit lane % 16.
   uint32_t w_off[G::WL];
   int w_row[G::WL];
 #pragma unroll
-  for (int j = 0; j < G::WL; ++j) {
-    const int r = 4 * (G::WL * wave + j) + lane / 16;
-    const int lu = (lane % 16) ^ swz_w(r);
-    const int64_t col = n0 + 8 * lu;
-    w_row[j] = r;
-    w_off[j] = col < N ? (uint32_t)((r * ldw + src_col(p, col)) * 2) : OOB;
-  }
-  // Token rows: wave w fills bytes [XW w, XW (w+1)) of the token region, load
-  // j the XLB bytes from XW w + XLB j; lane -> physical byte (XLB / 64) lane.
+  for (int j = 0; j < G::WL; ++j) G::w_load(p, ldw, n0, wave, lane, j, w_off[j], w_row[j]);
   uint32_t x_off[G::XL];
   int x_k[G::XL];
 #pragma unroll
-  for (int j = 0; j < G::XL; ++j) {
-    const int pb = G::XW * wave + G::XLB * j + (G::XLB / 64) * lane;  // physical byte
-    const int r = pb / G::XP, b = pb % G::XP;
-    const int k = 8 * ((b >> 4) ^ swz_x<G::XP>(r)) + ((b & 15) >> 1);
-    x_k[j] = k;
-    x_off[j] = (r < M && r < 16 * MB) ? (uint32_t)((r * p.lda + k) * 2) : OOB;
-  }
+  for (int j = 0; j < G::XL; ++j) G::x_load(p, wave, lane, j, x_off[j], x_k[j]);
   const bf16 *X = (const bf16 *)p.A;
 
   // Loads of stage t into its buffer; past the last stage every lane gets an
@@ -243,17 +193,15 @@ __global__ __launch_bounds__(NWAVE * 64) void gemm_bf16_decode_kernel(const Gemm
     const i32x4 rw = rsrc(W + k0 * ldw);
     const i32x4 rx = rsrc(X + k0);
 #pragma unroll
-    for (int j = 0; j < G::WL; ++j) {
-      const uint32_t off = (live && k0 + w_row[j] < kend) ? w_off[j] : OOB;
-      dma16_nt(rw, st + (G::WL * wave + j) * 1024, off);
-    }
+    for (int j = 0; j < G::WL; ++j)
+      dma16_nt(rw, st + G::w_lds(wave, j), G::stage_off(live, k0, w_row[j], kend, w_off[j]));
 #pragma unroll
     for (int j = 0; j < G::XL; ++j) {
-      const uint32_t off = (live && k0 + x_k[j] < kend) ? x_off[j] : OOB;
-      char *dst = st + G::WB + G::XW * wave + G::XLB * j;
+      const uint32_t off = G::stage_off(live, k0, x_k[j], kend, x_off[j]);
+      char *dst = st + G::x_lds(wave, j);
       if constexpr (G::XLB == 1024)
         dma16(rx, dst, off);
-      else if (G::XW >= 256 || lane < G::XW / 4)
+      else if (G::x_lane(lane))
         dma4(rx, dst, off);
     }
   };
@@ -317,7 +265,7 @@ __global__ __launch_bounds__(NWAVE * 64) void gemm_bf16_decode_kernel(const Gemm
   // none may be pending when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 
-  const int64_t col = n0 + 16 * wave + (lane & 15);
+  const int64_t col = decode::out_col(n0, wave, lane);
   const int64_t nparts = NMAT * S;  // workgroups of this column block
   if (nparts == 1) {
     store_out<EPI, ACT, MB>(p, col, lane, acc, acc);
@@ -336,13 +284,12 @@ __global__ __launch_bounds__(NWAVE * 64) void gemm_bf16_decode_kernel(const Gemm
   // their lanes get an offset past the buffer range, which the hardware drops
   // (stores) or reads as zero (loads).
   const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-      parts + blk * nparts * G::PF, 0, 0x7fffffff, RSRC_WORD3);
+      parts + blk * G::block_floats(nparts), 0, 0x7fffffff, RSRC_WORD3);
   uint32_t goff[MB];
 #pragma unroll
-  for (int m = 0; m < MB; ++m)
-    goff[m] = (16 * m + 4 * (lane >> 4) < M) ? (uint32_t)(((wave * MB + m) * 64 + lane) * 16) : OOB;
+  for (int m = 0; m < MB; ++m) goff[m] = G::group_off(M, wave, lane, m);
   {
-    const uint32_t mine = (uint32_t)(((up ? S : 0) + s) * (G::PF * 4));
+    const uint32_t mine = G::slot_off(up ? 1 : 0, S, s);
 #pragma unroll
     for (int m = 0; m < MB; ++m)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, acc[m]), rp,
@@ -380,7 +327,7 @@ __global__ __launch_bounds__(NWAVE * 64) void gemm_bf16_decode_kernel(const Gemm
 #pragma unroll
         for (int m = 0; m < MB; ++m) val[q][c][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if (s2 + c < S) {  // uniform: a scalar branch, no wait
-          const uint32_t slot = (uint32_t)((q * S + s2 + c) * (G::PF * 4));
+          const uint32_t slot = G::slot_off(q, S, s2 + c);
 #pragma unroll
           for (int m = 0; m < MB; ++m)
             val[q][c][m] = __builtin_bit_cast(

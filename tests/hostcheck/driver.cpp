@@ -8,7 +8,7 @@
 // gets a buffer of exactly the bytes its documented shape needs, so that an
 // access past the last element of any operand is a finding.  One output line
 // per case:
-//   CASE <line> | status <s> launches <n> tiled <n> other <n> accesses <n> findings <n>
+//   CASE <line> | status <s> launches <n> tiled <n> decode <n> other <n> accesses <n> findings <n>
 // followed by a FINDING line for each finding.  Exit status 0 when every case
 // returned the expected status and nothing was found.
 #include <stdio.h>
@@ -286,9 +286,10 @@ int main() {
     else
       bad |= st != TP_OK;
     failed += bad;
-    printf("CASE %s | status %d launches %ld tiled %ld other %ld accesses %ld findings %zu%s\n",
-           line.c_str(), (int)st, s.launches, s.tiled, s.checked_other, s.accesses,
-           s.findings.size(), bad ? " FAILED" : "");
+    printf("CASE %s | status %d launches %ld tiled %ld decode %ld other %ld accesses %ld "
+           "findings %zu%s\n",
+           line.c_str(), (int)st, s.launches, s.tiled, s.decode, s.checked_other - s.decode,
+           s.accesses, s.findings.size(), bad ? " FAILED" : "");
     if (st != TP_OK && !expect_error) printf("ERROR %s\n", tp_last_error_message());
     for (const std::string &f : s.findings) printf("FINDING %s\n", f.c_str());
     if (a.o("kernels", 0))

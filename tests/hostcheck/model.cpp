@@ -22,11 +22,13 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <map>
 #include <set>
 #include <string>
 #include <vector>
 
+#include "decode_geometry.hpp"
 #include "kernels.h"  // from the library's csrc/ (include path)
 #include "tiled_geometry.hpp"
 
@@ -372,6 +374,139 @@ void on_tiled(const std::vector<int> &t, const tpmlp::GemmArgs &p, unsigned grid
   if (!ok) finding("no model for tile configuration BK %d NWAVE %d BM %d", BK, NWAVE, BM);
 }
 
+// ---- the few-token GEMM, lane by lane ---------------------------------------------
+template <int MB, int BK, int NST>
+void check_decode(int epi, const tpmlp::GemmArgs &p, int64_t nblk, int64_t S, int64_t kc,
+                  const unsigned *ctr, const float *parts, unsigned grid, unsigned block) {
+  using namespace tpmlp;
+  using G = decode::Geo<MB, BK, NST>;
+  const int nmat = epi == EPI_SWIGLU ? 2 : 1;
+  const int64_t nparts = nmat * S;
+  if (block != (unsigned)(decode::NWAVE * 64)) finding("block %u", block);
+  // LDS: every stage's weight region and token region filled exactly once.
+  {
+    std::vector<int> cover(G::SB, 0);
+    bool bad = false;
+    for (int w = 0; w < decode::NWAVE; ++w) {
+      for (int j = 0; j < G::WL; ++j) {
+        const int o = G::w_lds(w, j);
+        if (o < 0 || o + 1024 > G::WB) bad = true;
+        else for (int b = 0; b < 1024; ++b) ++cover[o + b];
+      }
+      for (int j = 0; j < G::XL; ++j) {
+        const int o = G::x_lds(w, j);
+        for (int lane = 0; lane < 64; ++lane) {
+          if (!G::x_lane(lane)) continue;
+          const int b0 = o + lane * G::X_BYTES;
+          if (b0 < G::WB || b0 + G::X_BYTES > G::SB) bad = true;
+          else for (int b = 0; b < G::X_BYTES; ++b) ++cover[b0 + b];
+        }
+      }
+    }
+    for (int c : cover) bad |= c != 1;
+    if (bad) finding("stage LDS not filled exactly once");
+  }
+  std::vector<char> seen((size_t)(nblk * nmat * S), 0);
+  const uint64_t Xb = (uint64_t)(uintptr_t)p.A, Cb = (uint64_t)(uintptr_t)p.C;
+  const uint64_t Pb = (uint64_t)(uintptr_t)parts;
+  std::vector<std::pair<uint64_t, unsigned>> pstores;  // (16-byte group, workgroup)
+  for (unsigned bid = 0; bid < grid; ++bid) {
+    int64_t blk, s, kbeg, kend;
+    bool up;
+    decode::wg_coords(bid, nmat, nblk, blk, s, up);
+    if (blk < 0 || blk >= nblk || s < 0 || s >= S) {
+      finding("workgroup %u -> block %lld range %lld out of range", bid, (long long)blk, (long long)s);
+      continue;
+    }
+    const int64_t u = (s * nmat + (up ? 1 : 0)) * nblk + blk;
+    if (seen[u]++) finding("block %lld range %lld taken twice", (long long)blk, (long long)s);
+    decode::k_range(s, kc, p.K, kbeg, kend);
+    if (kend <= kbeg) finding("empty k-range %lld", (long long)s);
+    const int64_t nst = (kend - kbeg + BK - 1) / BK;
+    const uint64_t Wb = (uint64_t)(uintptr_t)(up ? p.B2 : p.B);
+    const int64_t ldw = up ? p.ldb2 : p.ldb;
+    const int64_t n0 = blk * decode::RC;
+    // the stages a load with relative k `k` is live in: first and last
+    auto stages = [&](int k, int64_t &t0, int64_t &t1) {
+      t0 = 0;
+      t1 = kend - 1 - kbeg - k >= 0 ? (kend - 1 - kbeg - k) / BK : -1;
+      if (t1 > nst - 1) t1 = nst - 1;
+    };
+    for (int wave = 0; wave < decode::NWAVE; ++wave)
+      for (int lane = 0; lane < 64; ++lane) {
+        for (int j = 0; j < G::WL; ++j) {
+          uint32_t off;
+          int row;
+          G::w_load(p, ldw, n0, wave, lane, j, off, row);
+          if (off != decode::OOB_OFF && off + 16u > 0x7fffffffu) finding("weight offset %u", off);
+          int64_t t0, t1;
+          stages(row, t0, t1);
+          for (int64_t t : {t0, t1}) {
+            if (t < 0 || t > t1) continue;
+            const int64_t k0 = kbeg + t * BK;
+            const uint32_t o = G::stage_off(true, k0, row, kend, off);
+            if (o != decode::OOB_OFF) access(up ? "Wu load" : "W load", Wb, Wb + 2 * k0 * ldw + o, 16);
+          }
+        }
+        for (int j = 0; j < G::XL; ++j) {
+          if (!G::x_lane(lane)) continue;
+          uint32_t off;
+          int k;
+          G::x_load(p, wave, lane, j, off, k);
+          if (off != decode::OOB_OFF && off + 16u > 0x7fffffffu) finding("token offset %u", off);
+          int64_t t0, t1;
+          stages(k, t0, t1);
+          for (int64_t t : {t0, t1}) {
+            if (t < 0 || t > t1) continue;
+            const int64_t k0 = kbeg + t * BK;
+            const uint32_t o = G::stage_off(true, k0, k, kend, off);
+            if (o != decode::OOB_OFF) access("X load", Xb, Xb + 2 * k0 + o, G::X_BYTES);
+          }
+        }
+        const int64_t col = decode::out_col(n0, wave, lane);
+        if (nparts > 1) {
+          const uint64_t blk0 = Pb + 4 * (uint64_t)(blk * G::block_floats(nparts));
+          for (int m = 0; m < MB; ++m) {
+            const uint32_t g = G::group_off(p.M, wave, lane, m);
+            if (g == decode::OOB_OFF) continue;
+            access("partial store", Pb, blk0 + g + G::slot_off(up ? 1 : 0, S, s), 16);
+            pstores.emplace_back(blk0 + g + G::slot_off(up ? 1 : 0, S, s), bid);
+            for (int q = 0; q < nmat; ++q)
+              for (int64_t s2 = 0; s2 < S; ++s2)
+                access("partial load", Pb, blk0 + g + G::slot_off(q, S, s2), 16);
+          }
+          if (wave == 0 && lane == 0)
+            access("counter", (uint64_t)(uintptr_t)ctr, (uint64_t)(uintptr_t)(ctr + blk), 4);
+        }
+        // the output: written by the block's only workgroup, or its last arriver
+        if (col < p.N && (nparts > 1 || !up)) {
+          if (epi == EPI_ACT && p.bias)
+            access("bias", (uint64_t)(uintptr_t)p.bias,
+                   (uint64_t)(uintptr_t)p.bias + 2 * src_col(p, col), 2);
+          const int es = epi == EPI_F32 ? 4 : 2;
+          for (int m = 0; m < MB; ++m)
+            for (int v = 0; v < 4; ++v) {
+              const int64_t row = decode::out_row(m, lane, v);
+              if (row < p.M) access("C store", Cb, Cb + es * (row * p.ldc + col), es);
+            }
+        }
+      }
+  }
+  for (size_t u = 0; u < seen.size(); ++u)
+    if (!seen[u]) {
+      finding("work item %zu never taken", u);
+      break;
+    }
+  // No two workgroups' partial stores may overlap (16-byte aligned groups).
+  std::sort(pstores.begin(), pstores.end());
+  for (size_t i = 1; i < pstores.size(); ++i)
+    if (pstores[i].first < pstores[i - 1].first + 16 && pstores[i].second != pstores[i - 1].second) {
+      finding("partial stores of workgroups %u and %u overlap", pstores[i - 1].second,
+              pstores[i].second);
+      break;
+    }
+}
+
 // ---- argument-level models of the other kernels ------------------------------------
 void on_decode(const std::vector<int> &t, void **args, unsigned grid, unsigned block) {
   // <EPI, ACT, MB, BK, NST>(GemmArgs, nblk, S, kc, ctr, parts)
@@ -384,7 +519,7 @@ void on_decode(const std::vector<int> &t, void **args, unsigned grid, unsigned b
     finding("cannot read the template arguments");
     return;
   }
-  const int MB = t[2];
+  const int MB = t[2], BK = t[3], NST = t[4];
   const int nmat = t[0] == tpmlp::EPI_SWIGLU ? 2 : 1;
   const int nwave = (int)block / 64;
   gemm_extents(p, 2);
@@ -396,6 +531,15 @@ void on_decode(const std::vector<int> &t, void **args, unsigned grid, unsigned b
     extent("counters", ctr, nblk - 1, 4);
     extent("partials", parts, nblk * nmat * S * (int64_t)nwave * MB * 256 - 1, 4);
   }
+  ++g_stats.decode;
+  if (MB == 1 && BK == 32 && NST == 4)
+    check_decode<1, 32, 4>(t[0], p, nblk, S, kc, ctr, parts, grid, block);
+  else if (MB == 2 && BK == 32 && NST == 4)
+    check_decode<2, 32, 4>(t[0], p, nblk, S, kc, ctr, parts, grid, block);
+  else if (MB == 4 && BK == 64 && NST == 3)
+    check_decode<4, 64, 3>(t[0], p, nblk, S, kc, ctr, parts, grid, block);
+  else
+    finding("no model for configuration MB %d BK %d NST %d", MB, BK, NST);
 }
 
 void on_f32(const tpmlp::GemmArgs &p) { gemm_extents(p, 4); }

@@ -24,6 +24,7 @@ void reset();  // forget every buffer, launch and finding
 struct Stats {
   long launches = 0;       // every kernel launch
   long tiled = 0;          // tiled GEMM launches checked lane by lane
+  long decode = 0;         // few-token GEMM launches checked lane by lane
   long checked_other = 0;  // other launches whose extents were checked
   long accesses = 0;       // address ranges checked
   std::vector<std::string> findings;  // violations (first few per launch)

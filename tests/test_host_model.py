@@ -12,9 +12,13 @@ ABI on fake device buffers sized exactly to each operand's documented shape
     every buffer-to-LDS load's bytes at its first and last live k-step (with
     the QKV column map and split B^T operands), offsets inside the descriptor
     range, each stage's LDS filled once, and every epilogue store and read;
-  - every other launch at the level of its arguments (operand extents, the
-    few-token path's counters and partials, attention, reductions, LayerNorm,
-    column sums).
+  - few-token GEMM launches lane by lane (csrc/decode_geometry.hpp): each
+    workgroup's column block and k-range (all exactly once), the weight and
+    token loads at their first and last live stage, each stage's LDS filled
+    once, the split-K partial stores and loads (no two workgroups' stores
+    overlapping), the arrival counter, and the output stores;
+  - every other launch at the level of its arguments (operand extents,
+    attention, reductions, LayerNorm, column sums).
 The cases are the GPU tests' shapes, the full-size workloads, empty inputs,
 padded leading dimensions, and rejected arguments (which must launch nothing).
 A run with every buffer two bytes short must report findings: the model sees
@@ -197,11 +201,12 @@ def test_every_launch_stays_in_bounds(driver):
     assert r.returncode == 0, tail
     done = re.search(r"DONE cases (\d+) failed (\d+)", r.stdout)
     assert done and int(done.group(1)) == len(lines) and done.group(2) == "0", tail
-    stats = [re.search(r"launches (\d+) tiled (\d+) other (\d+) accesses (\d+)", x)
+    stats = [re.search(r"launches (\d+) tiled (\d+) decode (\d+) other (\d+) accesses (\d+)", x)
              for x in r.stdout.splitlines() if x.startswith("CASE")]
     tiled = sum(int(m.group(2)) for m in stats)
-    other = sum(int(m.group(3)) for m in stats)
-    assert tiled >= 100 and other >= 50, (tiled, other)
+    decode = sum(int(m.group(3)) for m in stats)
+    other = sum(int(m.group(4)) for m in stats)
+    assert tiled >= 100 and decode >= 50 and other >= 50, (tiled, decode, other)
 
 
 def test_model_sees_the_last_element(driver):
@@ -218,31 +223,44 @@ def test_model_sees_the_last_element(driver):
 
 
 # Planted mistakes in a copy of the shared addressing code (the bounds model is
-# rebuilt against the copy; the library itself is untouched): a dropped row
-# check on A, a column check that lets one 16-byte unit past N through, and a
-# tile order that is not a bijection.  Each must produce findings.
+# rebuilt against the copy; the library itself is untouched): for the tiled
+# GEMM a dropped row check on A, a column check that lets one 16-byte unit past
+# N through, and a tile order that is not a bijection; for the few-token GEMM
+# a dropped token-row check, a weight column check one unit late, and partial
+# slots of half their size.  Each must produce findings.
 MUTANTS = [
-    ("A rows past M not masked",
+    ("A rows past M not masked", "tiled_geometry.hpp",
      "off = (m0 + r < p.M) ? (uint32_t)((r * p.lda + 8 * lu) * 2) : OOB_OFF;",
      "off = (uint32_t)((r * p.lda + 8 * lu) * 2);",
      ["shard bf16 swiglu 300 264 1024 2 4", "shard bf16 gelu_tanh 1000 520 8504 0 1 bias=1"]),
-    ("B column check off by one unit",
+    ("B column check off by one unit", "tiled_geometry.hpp",
      "off = (col < p.N) ? (uint32_t)((kr * ld + src_col(p, col)) * 2) : OOB_OFF;",
      "off = (col < p.N + 8) ? (uint32_t)((kr * ld + src_col(p, col)) * 2) : OOB_OFF;",
      ["shard bf16 gelu_erf 257 520 768 1 2 bias=1", "qkv bf16 300 264 8 2 64 1 2 bias=1"]),
-    ("tile order not a bijection",
+    ("tile order not a bijection", "tiled_geometry.hpp",
      "const int t = xcd * q + (xcd < r ? xcd : r) + idx;",
      "const int t = xcd * q + idx;",
      ["shard bf16 swiglu 300 264 1024 2 4", "shard bf16 relu 1000 8456 1024 0 1 bias=1"]),
+    ("few-token rows past M not masked", "decode_geometry.hpp",
+     "off = (r < p.M && r < 16 * MB) ? (uint32_t)((r * p.lda + k) * 2) : OOB_OFF;",
+     "off = (r < 16 * MB) ? (uint32_t)((r * p.lda + k) * 2) : OOB_OFF;",
+     ["shard bf16 swiglu 1 264 1024 0 4", "shard bf16 gelu_erf 17 1032 1536 3 4 bias=1"]),
+    ("few-token weight columns past N", "decode_geometry.hpp",
+     "off = col < p.N ? (uint32_t)((r * ldw + src_col(p, col)) * 2) : OOB_OFF;",
+     "off = col < p.N + 8 ? (uint32_t)((r * ldw + src_col(p, col)) * 2) : OOB_OFF;",
+     ["shard bf16 relu 40 520 1000 0 1 bias=1", "qkv bf16 8 520 12 4 40 3 4 bias=1"]),
+    ("few-token partial slots overlap", "decode_geometry.hpp",
+     "return (uint32_t)((q * S + s) * (PF * 4));",
+     "return (uint32_t)((q * S + s) * (PF * 2));",
+     ["shard bf16 swiglu 3 264 16384 0 1", "shard bf16 none 33 264 1024 1 4"]),
 ]
 
 
-@pytest.mark.parametrize("what,old,new,lines", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_model_catches_planted_addressing_mistakes(driver, tmp_path, what, old, new, lines):
-    src = open(os.path.join(build.CSRC, "tiled_geometry.hpp")).read()
+@pytest.mark.parametrize("what,fname,old,new,lines", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_model_catches_planted_addressing_mistakes(driver, tmp_path, what, fname, old, new, lines):
+    src = open(os.path.join(build.CSRC, fname)).read()
     assert src.count(old) == 1, what
-    (tmp_path / "tiled_geometry.hpp").write_text(src.replace(old, new))
-    shutil.copy(os.path.join(build.CSRC, "kernels.h"), tmp_path / "kernels.h")
+    (tmp_path / fname).write_text(src.replace(old, new))  # found before csrc/'s copy
     model = cxx_obj(os.path.join(HC, "model.cpp"), tmp_path, include_first=str(tmp_path))
     objs = [o for o in driver.objs if not o.endswith("model.cpp.o")] + [model]
     exe = str(tmp_path / "driver")
