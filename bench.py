@@ -18,8 +18,10 @@ shard in GB/s of weights streamed, the on-device partial sum in GB/s, the
 simulated TP = 8 block, the GPT-style GeLU shard, the attention projections
 of one head shard (QKV and output projection) and the shard's training step
 (forward that keeps the pre-activation, and the backward pass), and the MFMA
-and HBM calibrations.  `roofline` covers the dominant kernel (the SwiGLU column
-GEMM), `roofline_decode` and `roofline_partial_sum` the HBM-bound steps;
+and HBM calibrations, and the vendor GEMM (hipBLASLt through torch.matmul) on
+the headline's shapes for comparison.  `roofline` covers the dominant kernel
+(the SwiGLU column GEMM), `roofline_decode` and `roofline_partial_sum` the
+HBM-bound steps;
 `cpu_baseline` is the CPU oracle timed on a bounded row sample of the same
 workload, and (`configs`) on a sample of every other configuration next to the
 GPU path's errors against it there.
@@ -563,6 +565,35 @@ def mfma_calibration(torch, tp, iters=20000, nwg=1024):
     return out
 
 
+def library_gemm_reference(torch, synth, steps, warmup):
+    """The vendor GEMM (torch.matmul, i.e. hipBLASLt) on the headline's shapes,
+    timed the same way as the shard's launches, as a check of the harness and
+    a point of comparison only (it is not part of the path): the column step
+    as one GEMM over the concatenated [Wg_i | Wu_i] (no SwiGLU epilogue, so
+    it does less than the path's column launch) and the row step with a bf16
+    output (half the output bytes of the path's fp32 partial)."""
+    W = synth.WORKLOADS["llama70b_prefill_tp8"]
+    dev = "cuda:0"
+    Wg, Wu, W2 = (t.to(dev) for t in synth.llama_shard_weights(W.d, W.s))
+    X = synth.llama_tokens(W.T, W.d).to(dev)
+    Wgu = torch.cat([Wg, Wu], dim=1).contiguous()
+    Y = torch.empty(W.T, W.s, dtype=torch.bfloat16, device=dev).normal_()
+    G = torch.empty(W.T, 2 * W.s, dtype=torch.bfloat16, device=dev)
+    Z = torch.empty(W.T, W.d, dtype=torch.bfloat16, device=dev)
+    col = lambda: torch.matmul(X, Wgu, out=G)  # noqa: E731
+    row = lambda: torch.matmul(Y, W2, out=Z)  # noqa: E731
+    ramp(torch, [col, row])
+    legs, _ = time_legs(torch, [col, row], max(20, steps), warmup)
+    t_col, t_row = median(legs[0]), median(legs[1])
+    f_col = 2.0 * W.T * W.d * 2 * W.s
+    f_row = 2.0 * W.T * W.d * W.s
+    return {"col_us": round(t_col * 1e6, 2), "col_TFLOPs": round(f_col / t_col / 1e12, 1),
+            "row_bf16_out_us": round(t_row * 1e6, 2),
+            "row_bf16_out_TFLOPs": round(f_row / t_row / 1e12, 1),
+            "what": "torch.matmul (hipBLASLt) on X [4096, 8192] x [Wg_i | Wu_i] [8192, 7168] -> bf16, "
+                    "and Y_i [4096, 3584] x W2_i [3584, 8192] -> bf16; events around each launch"}
+
+
 def _errors(np, got, ref):
     got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
     d = got - ref
@@ -714,7 +745,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline only")
     ap.add_argument("--sections",
-                    default="decode,partial_sum,simulated_block,gpt,attention,block,backward,calibration",
+                    default="decode,partial_sum,simulated_block,gpt,attention,block,backward,calibration,"
+                            "library_gemm",
                     help="comma list of the secondary sections to run (without --quick)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 256 MiB device copy (the reference for HBM byte counters)")
@@ -795,6 +827,10 @@ def main():
         result["mfma_calibration"] = mfma_calibration(torch, tp)
         log("bench: hbm calibration")
         result["hbm_calibration"] = hbm_calibration(torch, tp, max(5, args.steps // 2), 2)
+    if "library_gemm" in sections:
+        log("bench: library GEMM reference")
+        result["library_gemm_reference"] = library_gemm_reference(torch, synth,
+                                                                  max(5, args.steps // 2), 3)
     if "decode" in result:
         d1 = result["decode"]["T1"]
         result["roofline_decode"] = {
