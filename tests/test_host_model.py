@@ -256,16 +256,29 @@ MUTANTS = [
 ]
 
 
+@pytest.fixture(scope="module")
+def mutant_outcomes(driver, tmp_path_factory):
+    """Every mutant's bounds model built (in parallel) and run on its cases;
+    what -> (case lines of the output, full output)."""
+    def one(m):
+        what, fname, old, new, lines = m
+        d = tmp_path_factory.mktemp("mutant")
+        src = open(os.path.join(build.CSRC, fname)).read()
+        assert src.count(old) == 1, what
+        (d / fname).write_text(src.replace(old, new))  # found before csrc/'s copy
+        model = cxx_obj(os.path.join(HC, "model.cpp"), d, include_first=str(d))
+        objs = [o for o in driver.objs if not o.endswith("model.cpp.o")] + [model]
+        exe = str(d / "driver")
+        _run([CLANG, *CXX_SAN, "-o", exe, *objs])
+        r = run_driver(exe, lines)
+        return what, ([x for x in r.stdout.splitlines() if x.startswith("CASE")],
+                      r.stdout[-2000:] + r.stderr[-2000:])
+    with ThreadPoolExecutor(len(MUTANTS)) as ex:
+        return dict(ex.map(one, MUTANTS))
+
+
 @pytest.mark.parametrize("what,fname,old,new,lines", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_model_catches_planted_addressing_mistakes(driver, tmp_path, what, fname, old, new, lines):
-    src = open(os.path.join(build.CSRC, fname)).read()
-    assert src.count(old) == 1, what
-    (tmp_path / fname).write_text(src.replace(old, new))  # found before csrc/'s copy
-    model = cxx_obj(os.path.join(HC, "model.cpp"), tmp_path, include_first=str(tmp_path))
-    objs = [o for o in driver.objs if not o.endswith("model.cpp.o")] + [model]
-    exe = str(tmp_path / "driver")
-    _run([CLANG, *CXX_SAN, "-o", exe, *objs])
-    r = run_driver(exe, lines)
-    cases = [x for x in r.stdout.splitlines() if x.startswith("CASE")]
-    assert len(cases) == len(lines), r.stdout[-2000:] + r.stderr[-2000:]
-    assert any(int(re.search(r"findings (\d+)", c).group(1)) > 0 for c in cases), r.stdout
+def test_model_catches_planted_addressing_mistakes(mutant_outcomes, what, fname, old, new, lines):
+    cases, out = mutant_outcomes[what]
+    assert len(cases) == len(lines), out
+    assert any(int(re.search(r"findings (\d+)", c).group(1)) > 0 for c in cases), out

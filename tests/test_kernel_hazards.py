@@ -115,10 +115,37 @@ def violations(asm_lines):
     return found
 
 
-def compile_to_asm(src, outdir):
-    out = os.path.join(outdir, src + ".s")
-    cmd = [build.hipcc(), *build.COMMON, *build.DEVICE_FLAGS, "--offload-device-only", "-S",
-           os.path.join(build.CSRC, src), "-o", out]
+def variant_sources(dirpath):
+    """A variant of the load helpers that was tried and withdrawn: the
+    descriptor's v_readfirstlane and its 5 wait states inside the descriptor
+    helper's own asm statement, and no s_nop in front of the loads; written,
+    with the tiled GEMM and the headers it includes, into dirpath."""
+    src = open(os.path.join(build.CSRC, "lds_dma.hpp")).read()
+    a = src.index("__device__ __forceinline__ i32x4 rsrc(const void *base) {")
+    b = src.index("__device__ __forceinline__ uint32_t lds_addr")
+    helper = (
+        "__device__ __forceinline__ i32x4 rsrc(const void *base) {\n"
+        "  const uint64_t a = (uint64_t)base;\n"
+        "  int lo, hi;\n"
+        '  asm volatile("v_readfirstlane_b32 %0, %2\\n\\tv_readfirstlane_b32 %1, %3\\n\\ts_nop 4"\n'
+        '               : "=s"(lo), "=s"(hi)\n'
+        '               : "v"((int)(uint32_t)a), "v"((int)(uint32_t)(a >> 32) & 0xffff));\n'
+        "  i32x4 r;\n  r[0] = lo;\n  r[1] = hi;\n  r[2] = 0x7fffffff;\n  r[3] = RSRC_WORD3;\n"
+        "  return r;\n}\n\n")
+    variant = (src[:a] + helper + src[b:]).replace('asm volatile("s_nop 4\\n\\tbuffer_load',
+                                                   'asm volatile("buffer_load')
+    assert "s_nop 4\\n\\tbuffer_load" not in variant
+    for name in ("gemm_tiled.hip", "device_common.hpp", "kernels.h", "tiled_geometry.hpp"):
+        with open(os.path.join(dirpath, name), "w") as f:
+            f.write(open(os.path.join(build.CSRC, name)).read())
+    with open(os.path.join(dirpath, "lds_dma.hpp"), "w") as f:
+        f.write(variant)
+    return os.path.join(dirpath, "gemm_tiled.hip")
+
+
+def compile_path_to_asm(path, out):
+    cmd = [build.hipcc(), *build.COMMON, *build.DEVICE_FLAGS, "--offload-device-only", "-S", path,
+           "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     return out
@@ -126,10 +153,17 @@ def compile_to_asm(src, outdir):
 
 @pytest.fixture(scope="module")
 def asm_files():
+    """Assembly of every kernel source, and (key "variant") of the withdrawn
+    descriptor-helper variant of the tiled GEMM, compiled in parallel."""
     with tempfile.TemporaryDirectory() as tmp:
-        with ThreadPoolExecutor(min(8, len(KERNEL_SOURCES))) as ex:
-            paths = list(ex.map(lambda s: compile_to_asm(s, tmp), KERNEL_SOURCES))
-        yield {s: open(p).read().splitlines() for s, p in zip(KERNEL_SOURCES, paths)}
+        vdir = os.path.join(tmp, "variant")
+        os.makedirs(vdir)
+        jobs = [(os.path.join(build.CSRC, s), os.path.join(tmp, s + ".s")) for s in KERNEL_SOURCES]
+        jobs.append((variant_sources(vdir), os.path.join(tmp, "variant.s")))
+        with ThreadPoolExecutor(min(8, len(jobs))) as ex:
+            paths = list(ex.map(lambda j: compile_path_to_asm(*j), jobs))
+        names = KERNEL_SOURCES + ["variant"]
+        yield {n: open(p).read().splitlines() for n, p in zip(names, paths)}
 
 
 def test_checker_finds_a_planted_violation():
@@ -176,40 +210,15 @@ def test_no_valu_sgpr_hazard_before_lds_loads(asm_files, src):
     assert not found, f"{src}: {found[:3]}"
 
 
-def test_scan_catches_the_descriptor_helper_variant(tmp_path):
-    """A variant of the load helpers that was tried and withdrawn: the
-    descriptor's v_readfirstlane and its 5 wait states inside the descriptor
-    helper's own asm statement, and no s_nop in front of the loads.  Built here
-    from the current helpers and compiled with the tiled GEMM, it has the
-    descriptor covered but leaves M0 exposed: the compiler sets M0 for each load
-    with an SALU instruction (s_mov_b32, or s_cselect_b32 choosing the LDS
-    address or -1) right before it, with no wait state, so the load may use the
-    previous M0 - another stage's LDS address, or -1 - for its whole 1 KiB.
-    The scan finds exactly that hazard there, and none in the current helpers."""
-    src = open(os.path.join(build.CSRC, "lds_dma.hpp")).read()
-    a = src.index("__device__ __forceinline__ i32x4 rsrc(const void *base) {")
-    b = src.index("__device__ __forceinline__ uint32_t lds_addr")
-    helper = (
-        "__device__ __forceinline__ i32x4 rsrc(const void *base) {\n"
-        "  const uint64_t a = (uint64_t)base;\n"
-        "  int lo, hi;\n"
-        '  asm volatile("v_readfirstlane_b32 %0, %2\\n\\tv_readfirstlane_b32 %1, %3\\n\\ts_nop 4"\n'
-        '               : "=s"(lo), "=s"(hi)\n'
-        '               : "v"((int)(uint32_t)a), "v"((int)(uint32_t)(a >> 32) & 0xffff));\n'
-        "  i32x4 r;\n  r[0] = lo;\n  r[1] = hi;\n  r[2] = 0x7fffffff;\n  r[3] = RSRC_WORD3;\n"
-        "  return r;\n}\n\n")
-    variant = (src[:a] + helper + src[b:]).replace('asm volatile("s_nop 4\\n\\tbuffer_load',
-                                                   'asm volatile("buffer_load')
-    assert "s_nop 4\\n\\tbuffer_load" not in variant
-    for name in ("gemm_tiled.hip", "device_common.hpp", "kernels.h", "tiled_geometry.hpp"):
-        (tmp_path / name).write_text(open(os.path.join(build.CSRC, name)).read())
-    (tmp_path / "lds_dma.hpp").write_text(variant)
-    out = tmp_path / "variant.s"
-    cmd = [build.hipcc(), *build.COMMON, *build.DEVICE_FLAGS, "--offload-device-only", "-S",
-           str(tmp_path / "gemm_tiled.hip"), "-o", str(out)]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    found = violations(out.read_text().splitlines())
+def test_scan_catches_the_descriptor_helper_variant(asm_files):
+    """The withdrawn variant (see variant_sources), rebuilt from the current
+    helpers and compiled with the tiled GEMM, has the descriptor covered but
+    leaves M0 exposed: the compiler sets M0 for each load with an SALU
+    instruction (s_mov_b32, or s_cselect_b32 choosing the LDS address or -1)
+    right before it, with no wait state, so the load may use the previous M0 -
+    another stage's LDS address, or -1 - for its whole 1 KiB.  The scan finds
+    exactly that hazard there, and none in the current helpers."""
+    found = violations(asm_files["variant"])
     assert found
     for _, writer, _ in found:
         op, dst = writer.split(None, 1)

@@ -7,6 +7,7 @@ import os
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
@@ -108,27 +109,40 @@ def build_mutant(text, old, new, which, out):
                     "-fPIC", "-shared", "-o", out, src, "-lm"], check=True)
 
 
+def run_pins(lib):
+    env = dict(os.environ, TPMLP_ORACLE_LIB=lib, OMP_NUM_THREADS="1")
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
+
+
+CONTROL = ("unmutated copy", "#include <math.h>", "#include <math.h>", 0)
+
+
+@pytest.fixture(scope="module")
+def outcomes():
+    """Every mutant (and an unchanged copy) built and run against the pins, in
+    parallel subprocesses; name -> (return code, tail of the output)."""
+    text = open(SRC).read()
+    with tempfile.TemporaryDirectory() as tmp:
+        def one(m):
+            name, old, new, which = m
+            lib = os.path.join(tmp, "lib%d.so" % abs(hash(name)))
+            build_mutant(text, old, new, which, lib)
+            r = run_pins(lib)
+            return name, (r.returncode, r.stdout[-2000:])
+        workers = max(1, min(8, (os.cpu_count() or 2)))
+        with ThreadPoolExecutor(workers) as ex:
+            return dict(ex.map(one, MUTANTS + [CONTROL]))
+
+
 @pytest.mark.parametrize("name,old,new,which", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_mutant(name, old, new, which):
-    text = open(SRC).read()
-    with tempfile.TemporaryDirectory() as tmp:
-        lib = os.path.join(tmp, "liboracle_mutant.so")
-        build_mutant(text, old, new, which, lib)
-        env = dict(os.environ, TPMLP_ORACLE_LIB=lib, OMP_NUM_THREADS="4")
-        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                            os.path.join(ROOT, "tests", "test_oracle_pins.py")],
-                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    assert r.returncode != 0, f"mutant '{name}' survived the pins:\n{r.stdout[-2000:]}"
+def test_pins_catch_mutant(outcomes, name, old, new, which):
+    rc, out = outcomes[name]
+    assert rc != 0, f"mutant '{name}' survived the pins:\n{out}"
 
 
-def test_unmutated_copy_passes():
+def test_unmutated_copy_passes(outcomes):
     """Control: the same procedure on an unchanged copy passes the pins."""
-    text = open(SRC).read()
-    with tempfile.TemporaryDirectory() as tmp:
-        lib = os.path.join(tmp, "liboracle_copy.so")
-        build_mutant(text, "#include <math.h>", "#include <math.h>", 0, lib)
-        env = dict(os.environ, TPMLP_ORACLE_LIB=lib, OMP_NUM_THREADS="4")
-        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                            os.path.join(ROOT, "tests", "test_oracle_pins.py")],
-                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    assert r.returncode == 0, r.stdout[-2000:]
+    rc, out = outcomes[CONTROL[0]]
+    assert rc == 0, out
