@@ -150,15 +150,19 @@ tp_status tp_mlp_shard(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k,
  * tp_mlp_shard for callers that cannot allocate device memory or pass a
  * workspace: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments (without ws/ws_bytes), results and checks
- * as tp_mlp_shard.  The scratch the few-token (T <= 64, bf16) path needs -- its
+ * as tp_mlp_shard, except that GEMMs with more than 64 tokens never split K
+ * here: where tp_mlp_shard splits one (few output tiles, long K; see
+ * tp_workspace_bytes) the fp32 sums are taken in another order, and the two
+ * results agree within the bf16 tolerance rather than bit for bit.  The scratch
+ * the few-token (T <= 64, bf16) path needs -- its
  * arrival counters and split-K partials -- lives in a library-owned static
  * device array of TP_STATIC_SCRATCH_BYTES on each GPU the library runs on,
  * held until the process ends; its address is looked up, and its counter area
  * cleared by a fill kernel on `stream`, at the first call on each device.  The
  * call allocates nothing (no hipMalloc, hipFree or allocating library call).
- *   - Sizes whose scratch need exceeds TP_STATIC_SCRATCH_BYTES (the need
- *     tp_workspace_bytes reports) return TP_ERR_WORKSPACE, with nothing
- *     launched.
+ *   - Sizes whose few-token scratch need exceeds TP_STATIC_SCRATCH_BYTES (the
+ *     need tp_workspace_bytes reports for T <= 64) return TP_ERR_WORKSPACE,
+ *     with nothing launched.
  *   - Every call on one GPU shares that GPU's array, whose content carries
  *     over from call to call (each call leaves the counters zero again):
  *     calls that overlap on one GPU -- on different streams, or from several
@@ -207,8 +211,11 @@ tp_status tp_mlp_simulated(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_
 /*
  * Bytes of workspace that tp_col_linear / tp_row_linear / tp_mlp_shard /
  * tp_mlp_simulated need for these sizes (0 if none).  The workspace holds
- * the arrival counters (the first 256 KiB) and split-K partial sums (after
- * them) of the few-token (T <= 64) path.  It must be zero-filled before its
+ * arrival counters (the first 256 KiB) and split-K partial sums (after them):
+ * those of the few-token (T <= 64) path, and with more tokens those of a
+ * GEMM with too few output tiles to fill the device (at most 120 tiles of 256
+ * rows) and K of 1536 or more, whose k-range is split over 2 to 8 workgroups
+ * per tile (at most 60 MiB of partials).  It must be zero-filled before its
  * first use; every call leaves its counters zero again, and no entry point
  * writes anything but zeros to the counter area, so one zeroed buffer can be
  * reused by any later call of any entry point on the same stream.  Returns 0

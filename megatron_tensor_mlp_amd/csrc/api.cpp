@@ -199,9 +199,11 @@ GemmArgs row_gemm(const RowCall &r, int groups, int64_t ystride, int64_t zstride
   return a;
 }
 
+// Workspace of one bf16 GEMM: the few-token path's split-K partials, or the
+// tiled path's when it splits K (problems with few tiles).
 size_t gemm_ws_bytes(tp_dtype dt, const GemmArgs &a) {
-  if (dt != TP_BF16 || a.M > kDecodeMaxT || a.M <= 0) return 0;
-  return decode_workspace_bytes(a);
+  if (dt != TP_BF16 || a.M <= 0) return 0;
+  return a.M <= kDecodeMaxT ? decode_workspace_bytes(a) : tiled_workspace_bytes(a);
 }
 
 // The bf16 kernels address memory with 32-bit buffer offsets from a tile's or
@@ -226,7 +228,7 @@ tp_status run_gemm(tp_dtype dt, const GemmArgs &a, void *ws, hipStream_t st) {
   else if (a.M <= kDecodeMaxT)
     e = launch_gemm_bf16_decode(a, ws, st);
   else
-    e = launch_gemm_bf16_tiled(a, st);
+    e = launch_gemm_bf16_tiled(a, ws, st);
   if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return TP_OK;
 }
@@ -368,7 +370,9 @@ tp_status check_tiled(tp_dtype dt, const GemmArgs &a) {
 }
 
 tp_status run_tiled(tp_dtype dt, const GemmArgs &a, hipStream_t st) {
-  const hipError_t e = dt == TP_F32 ? launch_gemm_f32(a, st) : launch_gemm_bf16_tiled(a, st);
+  // (the backward's layouts and epilogues never split K: no workspace)
+  const hipError_t e =
+      dt == TP_F32 ? launch_gemm_f32(a, st) : launch_gemm_bf16_tiled(a, nullptr, st);
   if (e != hipSuccess) return fail(TP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return TP_OK;
 }
@@ -643,8 +647,9 @@ BlockPlan plan_block(tp_dtype dt, tp_act act, int64_t nseq, int64_t S, int64_t d
   P.qw = (int64_t)Hq * dh / p;  // one shard's attention-output columns (W_O rows)
   P.nqkv = ((int64_t)Hq + 2 * (int64_t)Hkv) * dh;  // all shards' QKV columns
   P.s = k / p;
-  // Scratch of the few-token GEMMs (zero with more than 64 tokens): the
-  // largest of the block's four GEMM shapes; buffers are placeholders here.
+  // Scratch of the GEMMs (split-K partials: the few-token path's, or the
+  // tiled path's for shapes with few tiles): the largest of the block's four
+  // GEMM shapes; buffers are placeholders here.
   static const char dummy[16] __attribute__((aligned(16))) = {0};
   const int64_t T = P.T;
   const QkvCall qc = make_qkv(dt, T, d, Hq, Hkv, dh, 0, 1, dummy, d, dummy, P.nqkv, nullptr,
@@ -723,7 +728,10 @@ tp_status tp_mlp_shard_noalloc(tp_dtype dt, tp_act act, int64_t T, int64_t d, in
   const RowCall r = make_row(dt, T, d, k, i, p, Y, ldy, W2, ldw2, Z, ldz);
   TRY(validate_row(r));
   if (T == 0) return ok();
-  const GemmArgs ac = col_gemm(c, 1, 0), ar = row_gemm(r, 1, 0, 0);
+  // The tiled path's split-K partials would not fit the static scratch: the
+  // many-token GEMMs run unsplit here.
+  GemmArgs ac = col_gemm(c, 1, 0), ar = row_gemm(r, 1, 0, 0);
+  ac.splitk = ar.splitk = 1;
   TRY(check_gemm(dt, ac));
   TRY(check_gemm(dt, ar));
   const size_t need = max_sz(gemm_ws_bytes(dt, ac), gemm_ws_bytes(dt, ar));
@@ -820,7 +828,11 @@ size_t tp_workspace_bytes(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t
   ColCall c = make_col(dt, act, T, d, k, 0, p, dummy, d, dummy, k, dummy, k, nullptr,
                        (void *)dummy, s);
   RowCall r = make_row(dt, T, d, k, 0, p, dummy, s, dummy, d, (float *)dummy, d);
-  return max_sz(gemm_ws_bytes(dt, col_gemm(c, 1, 0)), gemm_ws_bytes(dt, row_gemm(r, 1, 0, 0)));
+  // One shard (tp_col_linear, tp_row_linear, tp_mlp_shard) and all p shards
+  // as grouped launches (tp_mlp_simulated): the split may differ.
+  size_t need = max_sz(gemm_ws_bytes(dt, col_gemm(c, 1, 0)), gemm_ws_bytes(dt, row_gemm(r, 1, 0, 0)));
+  need = max_sz(need, gemm_ws_bytes(dt, col_gemm(c, p, T * s)));
+  return max_sz(need, gemm_ws_bytes(dt, row_gemm(r, p, T * s, T * d)));
 }
 
 tp_status tp_col_linear_train(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k, int32_t i,

@@ -33,6 +33,16 @@
 // 16-k slice issues its MFMAs one by one, each followed by at most two memory
 // instructions (the reads of the next slice's fragments, and the loads of a
 // future step), in an order pinned with sched_barrier.
+//
+// Split-K.  A problem with too few tiles to fill the device (at most 120 tiles
+// of 256 rows) splits K into S ranges: S workgroups per tile, each writing
+// its fp32 accumulators to a partial slot of the workspace and bumping the
+// tile's arrival counter; the workgroup that arrives last sums the S partials
+// in k-range order (its own from registers; the order, and so the result, does
+// not depend on which workgroup that is), sets the counter back to zero and
+// runs the epilogue.  Partials are stored and loaded with the agent-coherent
+// cache policy (sc1), as in the few-token GEMM, so no cache write-back or
+// invalidate is needed between the XCDs.
 #include <cstdlib>
 
 #include "device_common.hpp"
@@ -53,8 +63,15 @@ using tiled::swz_b;
 using tiled::tile_coords;
 static_assert(tiled::OOB_OFF == OOB, "one out-of-range offset");
 
-template <int EPI, int ACT, int BK, int NST, int NWAVE, int BM, int LAY>
-__global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const GemmArgs p) {
+// Cache-policy operand of the buffer builtins: sc1, the agent-coherent policy.
+constexpr int CPOL_SC1 = 16;
+
+// SPLIT: the k-ranges of p.splitk (> 1) meet in `ctr` (one arrival counter
+// per tile, zero between launches) and `parts` (the partial slots).
+template <int EPI, int ACT, int BK, int NST, int NWAVE, int BM, int LAY, bool SPLIT>
+__global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const GemmArgs p,
+                                                                        unsigned *ctr,
+                                                                        float *parts) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE);
   using G = tiled::Geom<BK, NWAVE, BM, DUAL, LAY>;
   constexpr bool TA = G::TA, TB = G::TB;
@@ -94,10 +111,16 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int wm = wave / WNW, wn = wave % WNW;
   const int tilesM = (int)((p.M + BM - 1) / BM), tilesN = (int)((p.N + NOUT - 1) / NOUT);
+  const int total = tilesM * tilesN * p.groups;
+  int tile = blockIdx.x, sidx = 0;
+  if constexpr (SPLIT) tiled::split_coords(blockIdx.x, total, tile, sidx);
   int g, tm, tn;
-  tile_coords(blockIdx.x, tilesM, tilesN, tilesM * tilesN * p.groups, g, tm, tn);
+  tile_coords(tile, tilesM, tilesN, total, g, tm, tn);
 
   const int64_t M = p.M, N = p.N, K = p.K;
+  // This workgroup's k-range [kbeg, kend).
+  int64_t kbeg = 0, kend = K;
+  if constexpr (SPLIT) tiled::split_range(K, tiled::split_kc(K, p.splitk, BK), sidx, kbeg, kend);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * NOUT;
   const bf16 *A = G::template a_tile<bf16>(p, g, m0);
   const bf16 *B = G::template b_group<bf16>(p, g);
@@ -114,8 +137,8 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
 #pragma unroll
   for (int j = 0; j < B_LOADS; ++j) G::b_load(p, n0, wave, lane, j, b_off[j], b_k[j]);
 
-  // This wave's loads of k-step dkt into `stage`, one at a time (q < LPS).
-  // Past the last step (dkt >= KT) every lane gets an out-of-range offset: the
+  // This wave's loads of k-step dkt of the range into `stage`, one at a time
+  // (q < LPS).  Past the last step (dkt >= KT) every lane gets an out-of-range offset: the
   // stage, which nothing reads again, is filled with zeros and no memory is
   // touched, so the pipeline needs no branch.
   struct LoadCtx {
@@ -126,17 +149,17 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
   auto load_ctx = [&](int dkt, int KT) {
     LoadCtx c;
     c.live = dkt < KT;
-    c.k0 = (int64_t)(c.live ? dkt : 0) * BK;
+    c.k0 = kbeg + (int64_t)(c.live ? dkt : 0) * BK;
     c.ra = rsrc(G::a_step(p, A, c.k0));
     c.rb = rsrc(G::b_step(p, B, B2, b_up, c.k0));
     return c;
   };
   auto issue_load = [&](const LoadCtx &c, char *stage, int q) {
     if (q < A_LOADS) {
-      dma16(c.ra, stage + G::a_lds(wave, q), G::step_off(c.live, c.k0, a_kof[q], K, a_off[q]));
+      dma16(c.ra, stage + G::a_lds(wave, q), G::step_off(c.live, c.k0, a_kof[q], kend, a_off[q]));
     } else {
       const int j = q - A_LOADS;
-      dma16(c.rb, stage + G::b_lds(wave, j), G::step_off(c.live, c.k0, b_k[j], K, b_off[j]));
+      dma16(c.rb, stage + G::b_lds(wave, j), G::step_off(c.live, c.k0, b_k[j], kend, b_off[j]));
     }
   };
 
@@ -268,7 +291,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
     join_frags(nbuf);
   };
 
-  const int KT = (int)((K + BK - 1) / BK);
+  const int KT = (int)((kend - kbeg + BK - 1) / BK);
   // One k-step on stage s = kt % NST.  Step kt+NST-1 is loaded into the stage
   // read by step kt-1 (free once the barrier that ended step kt-1 passed);
   // past the last step those loads are the zero-filling kind and the
@@ -306,6 +329,84 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
     if (kt + s < KT) step(kt + s, s);
   // No load may still be writing LDS when the workgroup releases it.
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
+
+  if constexpr (SPLIT) {
+    // ---- split-K: publish the partial; the last arriver sums them ----------------
+    __shared__ int s_last;
+    const int S = p.splitk;
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        (char *)parts + (int64_t)tile * S * G::SLOT_BYTES, 0, 0x7fffffff, RSRC_WORD3);
+    const uint32_t mine = (uint32_t)(sidx * G::SLOT_BYTES);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int f = 0; f < NB; ++f)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2],
+                           acc[i][f][4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), rp,
+                                                 mine + G::part_off(wave, lane, i, f, q), 0,
+                                                 CPOL_SC1);
+        }
+    // The stores have completed once vmcnt is zero; the barrier then makes
+    // that true for every wave before the counter moves.
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned prev =
+          __hip_atomic_fetch_add(ctr + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == (unsigned)(S - 1);
+      // Nothing else touches the counter in this launch once the last
+      // arriver has read it: leave it at zero for the next one.
+      if (s_last) __hip_atomic_store(ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // Sum fragment by fragment, SB ranges at a time: every load of a batch is
+    // issued before the first add (this workgroup's own range reads nothing:
+    // an out-of-range offset), and the adds run in k-range order.
+    constexpr int SB = 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int f = 0; f < NB; ++f) {
+        f32x4 sum[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s0 = 0; s0 < S; s0 += SB) {
+          f32x4 val[SB][4];
+#pragma unroll
+          for (int c = 0; c < SB; ++c) {
+            const int s2 = s0 + c;
+            const bool other = s2 < S && s2 != sidx;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              val[c][q] = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                             rp, other ? (uint32_t)(s2 * G::SLOT_BYTES) + G::part_off(wave, lane, i, f, q)
+                                       : OOB,
+                             0, CPOL_SC1));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int c = 0; c < SB; ++c) {
+            const int s2 = s0 + c;
+            if (s2 >= S) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 own = {acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2],
+                                 acc[i][f][4 * q + 3]};
+              sum[q] += s2 == sidx ? own : val[c][q];
+            }
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][f][4 * q + e] = sum[q][e];
+      }
+  }
 
   // ---- epilogue ---------------------------------------------------------------
   // 32x32 accumulator layout: lane holds column (lane & 31) and rows
@@ -486,22 +587,84 @@ template <int EPI, int ACT, int BK, int NST, int NWAVE, int BM, int LAY>
 void launch_cfg(const GemmArgs &a, hipStream_t s) {
   const int nout = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE) ? BN / 2 : BN;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + nout - 1) / nout) * a.groups;
-  hipLaunchKernelGGL((gemm_bf16_tiled_kernel<EPI, ACT, BK, NST, NWAVE, BM, LAY>),
-                     dim3((unsigned)tiles), dim3(NWAVE * 64), 0, s, a);
+  hipLaunchKernelGGL((gemm_bf16_tiled_kernel<EPI, ACT, BK, NST, NWAVE, BM, LAY, false>),
+                     dim3((unsigned)tiles), dim3(NWAVE * 64), 0, s, a, (unsigned *)nullptr,
+                     (float *)nullptr);
+}
+
+// Split-K launch: 256-row tiles of 8 waves, a.splitk > 1 k-ranges each.
+template <int EPI, int ACT, int LAY>
+void launch_split(const GemmArgs &a, void *ws, hipStream_t s) {
+  const int nout = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE) ? BN / 2 : BN;
+  const int64_t tiles = ((a.M + 255) / 256) * ((a.N + nout - 1) / nout) * a.groups;
+  hipLaunchKernelGGL((gemm_bf16_tiled_kernel<EPI, ACT, 32, 4, 8, 256, LAY, true>),
+                     dim3((unsigned)(tiles * a.splitk)), dim3(8 * 64), 0, s, a, (unsigned *)ws,
+                     (float *)((char *)ws + kWsCounterBytes));
 }
 
 // Tiles of 256 rows at most fill half of a 256-CU device: switch to 128-row
 // tiles (4 waves of 128 x 64), twice as many, for problems that small.
 constexpr int64_t SMALL_TILE_MAX = 128;
 
+// Split-K plan for problems of t <= 120 tiles of 256 rows (measured on the
+// Llama-70B shapes at T = 256 .. 4096):
+//  - the last arriver reads S - 1 partials of 256 KiB from the coherent
+//    level at a few microseconds each, so S stays at 4 or below unless the
+//    tiles are very few (t <= 20: up to 8);
+//  - more than ~240 busy CUs buy little (the chip is at its power limit), so
+//    t * S stays at or below 240, and at t > 120 nothing is split;
+//  - S = 2 already beats the 128-row configuration (8 waves per CU instead
+//    of 4, at the same workgroup count);
+//  - every k-range is at least 768 long.
+constexpr int SPLIT_WGS = 240;
+constexpr int SPLIT_MAX = 8;
+constexpr int SPLIT_MAX_MANY = 4;
+constexpr int64_t SPLIT_FEW_TILES = 20;
+constexpr int64_t SPLIT_MIN_K = 768;
+
+bool split_eligible(const GemmArgs &a) {
+  return a.lay == LAY_NN && a.ksplit == 0 &&
+         (a.epi == EPI_F32 || a.epi == EPI_ACT || a.epi == EPI_SWIGLU);
+}
+int64_t tiles256(const GemmArgs &a) {
+  const int nout = (a.epi == EPI_SWIGLU || a.epi == EPI_SWIGLU_SAVE) ? BN / 2 : BN;
+  return ((a.M + 255) / 256) * ((a.N + nout - 1) / nout) * a.groups;
+}
+// TPMLP_TILED_SPLIT (read once) forces the k-ranges of every eligible GEMM
+// (1: none), for sweeps.
+int forced_split() {
+  static int v = [] {
+    const char *e = getenv("TPMLP_TILED_SPLIT");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
+// The k-ranges a launch takes when S are asked for: ceil(K / kc) (S or fewer).
+int effective_split(int64_t K, int S) {
+  if (S <= 1 || K <= 0) return 1;
+  const int64_t kc = tiled::split_kc(K, S, 32);
+  return (int)((K + kc - 1) / kc);
+}
+
 // SWEEP: the configuration variants of the forward epilogues can be forced
 // for sweeps; the other instantiations take the default choice only.
 template <int EPI, int ACT, int LAY, bool SWEEP>
-hipError_t launch_t(const GemmArgs &a, hipStream_t s) {
+hipError_t launch_t(const GemmArgs &a, void *ws, hipStream_t s) {
   const int nout = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE) ? BN / 2 : BN;
   const int64_t tiles = ((a.M + 255) / 256) * ((a.N + nout - 1) / nout) * a.groups;
   if (tiles <= 0) return hipSuccess;
   if (2 * tiles > 0x7fffffff) return hipErrorInvalidValue;
+  if constexpr (SWEEP && LAY == LAY_NN && (EPI == EPI_F32 || EPI == EPI_ACT || EPI == EPI_SWIGLU)) {
+    const int S = tiled_splitk(a);
+    if (S > 1) {
+      if (!ws) return hipErrorInvalidValue;
+      GemmArgs b = a;
+      b.splitk = S;
+      launch_split<EPI, ACT, LAY>(b, ws, s);
+      return hipGetLastError();
+    }
+  }
   int v = SWEEP ? tiled_variant() : 1;
   if (v == 1 && tiles <= SMALL_TILE_MAX) v = 4;
   if constexpr (SWEEP) {
@@ -527,16 +690,16 @@ hipError_t launch_t(const GemmArgs &a, hipStream_t s) {
 }
 
 template <int EPI, int LAY, bool SWEEP>
-hipError_t launch_act(const GemmArgs &a, hipStream_t s) {
+hipError_t launch_act(const GemmArgs &a, void *ws, hipStream_t s) {
   switch (a.act) {
     case ACT_NONE:
-      return launch_t<EPI, ACT_NONE, LAY, SWEEP>(a, s);
+      return launch_t<EPI, ACT_NONE, LAY, SWEEP>(a, ws, s);
     case ACT_RELU:
-      return launch_t<EPI, ACT_RELU, LAY, SWEEP>(a, s);
+      return launch_t<EPI, ACT_RELU, LAY, SWEEP>(a, ws, s);
     case ACT_GELU_TANH:
-      return launch_t<EPI, ACT_GELU_TANH, LAY, SWEEP>(a, s);
+      return launch_t<EPI, ACT_GELU_TANH, LAY, SWEEP>(a, ws, s);
     case ACT_GELU_ERF:
-      return launch_t<EPI, ACT_GELU_ERF, LAY, SWEEP>(a, s);
+      return launch_t<EPI, ACT_GELU_ERF, LAY, SWEEP>(a, ws, s);
   }
   return hipErrorInvalidValue;
 }
@@ -565,34 +728,56 @@ bool gemm_bf16_tiled_supported(const GemmArgs &a) {
   return false;
 }
 
-hipError_t launch_gemm_bf16_tiled(const GemmArgs &a, hipStream_t s) {
+int tiled_splitk(const GemmArgs &a) {
+  if (!split_eligible(a) || a.splitk == 1 || a.M <= 0 || a.N <= 0) return 1;
+  const int64_t t = tiles256(a);
+  if (t > kWsMaxBlocks) return 1;  // one arrival counter per tile
+  const int ask = a.splitk > 1 ? a.splitk : forced_split();
+  if (ask >= 1) return effective_split(a.K, ask < SPLIT_MAX ? ask : SPLIT_MAX);
+  if (t <= 0 || 2 * t > SPLIT_WGS) return 1;
+  int64_t S = SPLIT_WGS / t;
+  const int64_t cap = t <= SPLIT_FEW_TILES ? SPLIT_MAX : SPLIT_MAX_MANY;
+  if (S > cap) S = cap;
+  if (S > a.K / SPLIT_MIN_K) S = a.K / SPLIT_MIN_K;
+  return S >= 2 ? effective_split(a.K, (int)S) : 1;
+}
+
+size_t tiled_workspace_bytes(const GemmArgs &a) {
+  const int S = tiled_splitk(a);
+  if (S <= 1) return 0;
+  using G = tiled::Geom<32, 8, 256, false, LAY_NN>;
+  static_assert(tiled::Geom<32, 8, 256, true, LAY_NN>::SLOT_BYTES == G::SLOT_BYTES, "slot");
+  return kWsCounterBytes + (size_t)tiles256(a) * S * G::SLOT_BYTES;
+}
+
+hipError_t launch_gemm_bf16_tiled(const GemmArgs &a, void *ws, hipStream_t s) {
   if (!gemm_bf16_tiled_supported(a)) return hipErrorInvalidValue;
   if (a.lay == LAY_NN) {
     switch (a.epi) {
       case EPI_F32:
-        return launch_t<EPI_F32, ACT_NONE, LAY_NN, true>(a, s);
+        return launch_t<EPI_F32, ACT_NONE, LAY_NN, true>(a, ws, s);
       case EPI_SWIGLU:
-        return launch_t<EPI_SWIGLU, ACT_SWIGLU, LAY_NN, true>(a, s);
+        return launch_t<EPI_SWIGLU, ACT_SWIGLU, LAY_NN, true>(a, ws, s);
       case EPI_ACT:
-        return launch_act<EPI_ACT, LAY_NN, true>(a, s);
+        return launch_act<EPI_ACT, LAY_NN, true>(a, ws, s);
       case EPI_ACT_SAVE:
-        return launch_act<EPI_ACT_SAVE, LAY_NN, false>(a, s);
+        return launch_act<EPI_ACT_SAVE, LAY_NN, false>(a, ws, s);
       case EPI_SWIGLU_SAVE:
-        return launch_t<EPI_SWIGLU_SAVE, ACT_SWIGLU, LAY_NN, false>(a, s);
+        return launch_t<EPI_SWIGLU_SAVE, ACT_SWIGLU, LAY_NN, false>(a, ws, s);
     }
   } else if (a.lay == LAY_NT) {
     switch (a.epi) {
       case EPI_F32:
-        return launch_t<EPI_F32, ACT_NONE, LAY_NT, false>(a, s);
+        return launch_t<EPI_F32, ACT_NONE, LAY_NT, false>(a, ws, s);
       case EPI_F32_ACC:
-        return launch_t<EPI_F32_ACC, ACT_NONE, LAY_NT, false>(a, s);
+        return launch_t<EPI_F32_ACC, ACT_NONE, LAY_NT, false>(a, ws, s);
       case EPI_DACT:
-        return launch_act<EPI_DACT, LAY_NT, false>(a, s);
+        return launch_act<EPI_DACT, LAY_NT, false>(a, ws, s);
       case EPI_DSWIGLU:
-        return launch_t<EPI_DSWIGLU, ACT_SWIGLU, LAY_NT, false>(a, s);
+        return launch_t<EPI_DSWIGLU, ACT_SWIGLU, LAY_NT, false>(a, ws, s);
     }
   } else if (a.lay == LAY_TN) {
-    if (a.epi == EPI_F32) return launch_t<EPI_F32, ACT_NONE, LAY_TN, false>(a, s);
+    if (a.epi == EPI_F32) return launch_t<EPI_F32, ACT_NONE, LAY_TN, false>(a, ws, s);
   }
   return hipErrorInvalidValue;
 }

@@ -63,6 +63,10 @@ struct GemmArgs {
   // A [M, K] times them sums two products in one GEMM; 0 = off.  ksplit is a
   // multiple of 32 (a k-step never straddles the two).
   int64_t ksplit;
+  // Tiled path: k-ranges per output tile (split-K), 0 = the launcher's choice
+  // (tiled_splitk), 1 = none.  Split tiles meet in the workspace passed to
+  // the launch (the shared layout: the counter area, then the partials).
+  int splitk;
 };
 
 // Weight / bias column read for output column c.
@@ -75,8 +79,14 @@ __host__ __device__ inline int64_t src_col(const GemmArgs &p, int64_t c) {
 
 // Large-T path: MFMA tiles staged through LDS (every epilogue and layout).
 // _supported: the shape fits the kernels' 32-bit buffer offsets.
+// tiled_splitk: the k-ranges per tile the launch uses (a.splitk, or for 0
+// the launcher's choice: more than one only for plain layouts with the
+// forward epilogues, at most 120 tiles of 256 rows, and k of 1536 or more);
+// tiled_workspace_bytes: the workspace that needs (0 without split-K).
 bool gemm_bf16_tiled_supported(const GemmArgs &a);
-hipError_t launch_gemm_bf16_tiled(const GemmArgs &a, hipStream_t s);
+int tiled_splitk(const GemmArgs &a);
+size_t tiled_workspace_bytes(const GemmArgs &a);
+hipError_t launch_gemm_bf16_tiled(const GemmArgs &a, void *ws, hipStream_t s);
 
 // Every entry point that takes a workspace lays it out the same way, so that
 // one buffer can serve them all: a counter area of kWsCounterBytes (arrival

@@ -51,6 +51,25 @@ __host__ __device__ __forceinline__ void tile_coords(int bid, int tilesM, int ti
   tn = w / gsz;
 }
 
+// Split-K: workgroup b of a launch of `total` tiles times S k-ranges takes
+// tile b % total (in the order above; with total a multiple of 8 the tile's
+// XCD is still b % 8) and k-range b / total.  The ranges are kc long, kc =
+// ceil(K / S) rounded up to a whole k-step, the last one ragged; a launch
+// takes S = ceil(K / kc) ranges, for which the same formula gives back kc.
+__host__ __device__ __forceinline__ void split_coords(int bid, int total, int &tile, int &sidx) {
+  tile = bid % total;
+  sidx = bid / total;
+}
+__host__ __device__ __forceinline__ int64_t split_kc(int64_t K, int S, int BK) {
+  const int64_t per = (K + S - 1) / S;
+  return (per + BK - 1) / BK * BK;
+}
+__host__ __device__ __forceinline__ void split_range(int64_t K, int64_t kc, int sidx,
+                                                     int64_t &kbeg, int64_t &kend) {
+  kbeg = (int64_t)sidx * kc;
+  kend = kbeg + kc < K ? kbeg + kc : K;
+}
+
 // Geometry of one kernel configuration: BK k per step, NWAVE waves, BM tile
 // rows, DUAL (SwiGLU: gate and up regions), LAY (operand layout).
 template <int BK, int NWAVE, int BM, bool DUAL, int LAY>
@@ -191,6 +210,16 @@ struct Geom {
   __host__ __device__ static __forceinline__ int64_t out_col(int64_t n0, int wn, int f, int lane) {
     return n0 + (DUAL ? WN / 2 : WN) * wn + 32 * f + (lane & 31);
   }
+  // Split-K partial slots: one per (tile, k-range), tile-major, each holding
+  // every wave's accumulators as 16-byte groups [wave][i][f][quarter q][lane]
+  // (q: accumulator elements 4q..4q+3), so one store or load instruction of a
+  // wave covers 1 KiB.  part_off: a group's byte offset within its slot.
+  static constexpr int64_t SLOT_BYTES = (int64_t)NWAVE * 4 * NB * 4 * 64 * 16;
+  __host__ __device__ static __forceinline__ uint32_t part_off(int wave, int lane, int i, int f,
+                                                               int q) {
+    return (uint32_t)(((((wave * 4 + i) * NB + f) * 4 + q) * 64 + lane) * 16);
+  }
+
   __host__ __device__ static __forceinline__ int64_t row_base(int64_t m0, int wm, int lane) {
     return m0 + 128 * wm + 4 * (lane >> 5);
   }

@@ -110,7 +110,8 @@ std::vector<int> template_ints(const std::string &name, const char *kernel) {
   at += strlen(kernel);
   if (at >= name.size() || name[at] != 'I') return v;
   ++at;
-  while (at + 1 < name.size() && name[at] == 'L' && name[at + 1] == 'i') {
+  // integer (Li<n>E) and bool (Lb<0|1>E) arguments
+  while (at + 1 < name.size() && name[at] == 'L' && (name[at + 1] == 'i' || name[at + 1] == 'b')) {
     at += 2;
     const bool neg = name[at] == 'n';
     if (neg) ++at;
@@ -166,8 +167,11 @@ void gemm_extents(const tpmlp::GemmArgs &p, int es) {
 }
 
 // ---- the tiled GEMM, lane by lane ------------------------------------------------
+// split: the split-K instantiation (S = p.splitk k-ranges per tile, meeting
+// in ctr and parts).
 template <int BK, int NWAVE, int BM, bool DUAL, int LAY>
-void check_tiled(int epi, const tpmlp::GemmArgs &p, unsigned grid, unsigned block) {
+void check_tiled(int epi, const tpmlp::GemmArgs &p, unsigned grid, unsigned block, bool split,
+                 const unsigned *ctr, const float *parts) {
   using namespace tpmlp;
   using G = tiled::Geom<BK, NWAVE, BM, DUAL, LAY>;
   typedef uint16_t E;  // bf16 storage
@@ -175,7 +179,35 @@ void check_tiled(int epi, const tpmlp::GemmArgs &p, unsigned grid, unsigned bloc
   if (block != (unsigned)(NWAVE * 64)) finding("block %u, want %d", block, NWAVE * 64);
   const int tilesM = (int)((p.M + BM - 1) / BM), tilesN = (int)((p.N + G::NOUT - 1) / G::NOUT);
   const int64_t total = (int64_t)tilesM * tilesN * p.groups;
-  if ((int64_t)grid != total) finding("grid %u, want %lld tiles", grid, (long long)total);
+  const int S = split ? p.splitk : 1;
+  if (split && S < 2) finding("split launch with %d k-ranges", S);
+  if (S < 1) return;
+  if ((int64_t)grid != total * S)
+    finding("grid %u, want %lld tiles x %d k-ranges", grid, (long long)total, S);
+  const int64_t kc = split ? tiled::split_kc(p.K, S, BK) : p.K;
+  if (split) {
+    if (kc % BK || (int64_t)S * kc < p.K || (int64_t)(S - 1) * kc >= p.K)
+      finding("k-ranges %d x %lld do not tile K %lld", S, (long long)kc, (long long)p.K);
+    if (total > (int64_t)kWsMaxBlocks) finding("%lld tiles exceed the counter area", (long long)total);
+    // the counters lie in the counter area below the partials
+    if ((uint64_t)(uintptr_t)(ctr + total) > (uint64_t)(uintptr_t)parts)
+      finding("counters overlap the partials");
+    extent("counters", ctr, total - 1, 4);
+    extent("partials", parts, total * S * G::SLOT_BYTES / 4 - 1, 4);
+    // a slot's groups: a bijection onto its SLOT_BYTES / 16 groups
+    std::vector<char> cov((size_t)(G::SLOT_BYTES / 16), 0);
+    bool bad = false;
+    for (int w = 0; w < NWAVE; ++w)
+      for (int lane = 0; lane < 64; ++lane)
+        for (int i = 0; i < 4; ++i)
+          for (int f = 0; f < G::NB; ++f)
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t o = G::part_off(w, lane, i, f, q);
+              if (o % 16 || o / 16 >= cov.size()) bad = true;
+              else if (cov[o / 16]++) bad = true;
+            }
+    if (bad) finding("partial slot groups are not a bijection");
+  }
 
   // LDS: the loads of all waves fill each stage exactly once, in 1 KiB pieces.
   {
@@ -197,19 +229,26 @@ void check_tiled(int epi, const tpmlp::GemmArgs &p, unsigned grid, unsigned bloc
     if (bad) finding("stage LDS not filled exactly once");
   }
 
-  std::vector<char> seen((size_t)total, 0);
-  const int64_t KT = (p.K + BK - 1) / BK;
+  std::vector<char> seen((size_t)(total * S), 0);
   const uint64_t Abase = (uint64_t)(uintptr_t)p.A, Bbase = (uint64_t)(uintptr_t)p.B,
                  B2base = (uint64_t)(uintptr_t)p.B2;
+  const uint64_t Pb = (uint64_t)(uintptr_t)parts;
   for (unsigned bid = 0; bid < grid; ++bid) {
+    int tile = (int)bid, sidx = 0;
+    if (split) tiled::split_coords((int)bid, (int)total, tile, sidx);
     int g, tm, tn;
-    tiled::tile_coords((int)bid, tilesM, tilesN, (int)total, g, tm, tn);
-    if (g < 0 || g >= p.groups || tm < 0 || tm >= tilesM || tn < 0 || tn >= tilesN) {
-      finding("block %u -> tile (%d, %d, %d) out of range", bid, g, tm, tn);
+    tiled::tile_coords(tile, tilesM, tilesN, (int)total, g, tm, tn);
+    if (g < 0 || g >= p.groups || tm < 0 || tm >= tilesM || tn < 0 || tn >= tilesN || sidx < 0 ||
+        sidx >= S) {
+      finding("block %u -> tile (%d, %d, %d) range %d out of range", bid, g, tm, tn, sidx);
       continue;
     }
     const int64_t t = ((int64_t)g * tilesM + tm) * tilesN + tn;
-    if (seen[t]++) finding("tile (%d, %d, %d) taken twice", g, tm, tn);
+    if (seen[t * S + sidx]++) finding("tile (%d, %d, %d) range %d taken twice", g, tm, tn, sidx);
+    int64_t kbeg = 0, kend = p.K;
+    if (split) tiled::split_range(p.K, kc, sidx, kbeg, kend);
+    if (split && kend <= kbeg) finding("empty k-range %d", sidx);
+    const int64_t KT = (kend - kbeg + BK - 1) / BK;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * G::NOUT;
     const E *A = G::template a_tile<E>(p, g, m0);
     const E *B = G::template b_group<E>(p, g);
@@ -223,13 +262,14 @@ void check_tiled(int epi, const tpmlp::GemmArgs &p, unsigned grid, unsigned bloc
           G::a_load(p, m0, wave, lane, j, off, kof);
           if (off != tiled::OOB_OFF && off + 16u > 0x7fffffffu)
             finding("A load offset %u past the descriptor range", off);
-          // live steps: k0 = kt * BK with k0 + kof < K
-          const int64_t last = p.K - 1 - kof >= 0 ? (p.K - 1 - kof) / BK : -1;
+          // live steps: k0 = kbeg + kt * BK with k0 + kof < kend
+          const int64_t last = kend - 1 - kof - kbeg >= 0 ? (kend - 1 - kof - kbeg) / BK : -1;
           for (int64_t kt : {(int64_t)0, last}) {
             if (kt < 0 || kt >= KT) continue;
-            const uint32_t o = G::step_off(kt < KT, kt * BK, kof, p.K, off);
+            const int64_t k0 = kbeg + kt * BK;
+            const uint32_t o = G::step_off(kt < KT, k0, kof, kend, off);
             if (o == tiled::OOB_OFF) continue;
-            const uint64_t base = (uint64_t)(uintptr_t)G::a_step(p, A, kt * BK);
+            const uint64_t base = (uint64_t)(uintptr_t)G::a_step(p, A, k0);
             access("A load", Abase, base + o, 16);
           }
         }
@@ -240,15 +280,15 @@ void check_tiled(int epi, const tpmlp::GemmArgs &p, unsigned grid, unsigned bloc
           if (off != tiled::OOB_OFF && off + 16u > 0x7fffffffu)
             finding("B load offset %u past the descriptor range", off);
           std::set<int64_t> steps = {0};
-          steps.insert(p.K - 1 - kr >= 0 ? (p.K - 1 - kr) / BK : -1);
+          steps.insert(kend - 1 - kr - kbeg >= 0 ? (kend - 1 - kr - kbeg) / BK : -1);
           if (G::TB && p.ksplit > 0) {
-            steps.insert(p.ksplit / BK - 1);
-            steps.insert(p.ksplit / BK);
+            steps.insert((p.ksplit - kbeg) / BK - 1);
+            steps.insert((p.ksplit - kbeg) / BK);
           }
           for (int64_t kt : steps) {
             if (kt < 0 || kt >= KT) continue;
-            const int64_t k0 = kt * BK;
-            const uint32_t o = G::step_off(true, k0, kr, p.K, off);
+            const int64_t k0 = kbeg + kt * BK;
+            const uint32_t o = G::step_off(true, k0, kr, kend, off);
             if (o == tiled::OOB_OFF) continue;
             const uint64_t base = (uint64_t)(uintptr_t)G::b_step(p, B, B2, up, k0);
             const bool second = G::TB ? (p.ksplit > 0 && k0 >= p.ksplit) : up;
@@ -256,6 +296,25 @@ void check_tiled(int epi, const tpmlp::GemmArgs &p, unsigned grid, unsigned bloc
           }
         }
       }
+    }
+
+    // Split-K: this workgroup's partial slot (stores), every other slot of
+    // the tile (the last arriver's loads), the tile's counter.
+    if (split) {
+      const uint64_t tile0 = Pb + (uint64_t)t * S * G::SLOT_BYTES;
+      for (int wave = 0; wave < NWAVE; ++wave)
+        for (int lane = 0; lane < 64; ++lane)
+          for (int i = 0; i < 4; ++i)
+            for (int f = 0; f < G::NB; ++f)
+              for (int q = 0; q < 4; ++q) {
+                const uint32_t o = G::part_off(wave, lane, i, f, q);
+                for (int s2 = 0; s2 < S; ++s2)
+                  if (s2 == sidx || (wave == 0 && lane == 0) || (i == 3 && f == G::NB - 1 && q == 3))
+                    access(s2 == sidx ? "partial store" : "partial load", Pb,
+                           tile0 + (uint64_t)s2 * G::SLOT_BYTES + o, 16);
+              }
+      if ((int64_t)S * G::SLOT_BYTES > 0x7fffffffLL) finding("slots beyond the descriptor range");
+      access("counter", (uint64_t)(uintptr_t)ctr, (uint64_t)(uintptr_t)(ctr + t), 4);
     }
 
     // Epilogue.  Fragments f of a wave cover its accumulator columns (the
@@ -338,39 +397,45 @@ void check_tiled(int epi, const tpmlp::GemmArgs &p, unsigned grid, unsigned bloc
       }
     }
   }
-  for (int64_t t = 0; t < total; ++t)
+  for (int64_t t = 0; t < total * S; ++t)
     if (!seen[t]) {
-      finding("tile %lld never taken", (long long)t);
+      finding("tile %lld range %lld never taken", (long long)(t / S), (long long)(t % S));
       break;
     }
 }
 
 template <int BK, int NWAVE, int BM>
-bool dispatch_lay(int epi, int lay, const tpmlp::GemmArgs &p, unsigned grid, unsigned block) {
+bool dispatch_lay(int epi, int lay, const tpmlp::GemmArgs &p, unsigned grid, unsigned block,
+                  bool split, const unsigned *ctr, const float *parts) {
   const bool dual = dual_epi(epi);
   switch (lay * 2 + (dual ? 1 : 0)) {
-    case 0: check_tiled<BK, NWAVE, BM, false, 0>(epi, p, grid, block); return true;
-    case 1: check_tiled<BK, NWAVE, BM, true, 0>(epi, p, grid, block); return true;
-    case 2: check_tiled<BK, NWAVE, BM, false, 1>(epi, p, grid, block); return true;
-    case 4: check_tiled<BK, NWAVE, BM, false, 2>(epi, p, grid, block); return true;
+    case 0: check_tiled<BK, NWAVE, BM, false, 0>(epi, p, grid, block, split, ctr, parts); return true;
+    case 1: check_tiled<BK, NWAVE, BM, true, 0>(epi, p, grid, block, split, ctr, parts); return true;
+    case 2: check_tiled<BK, NWAVE, BM, false, 1>(epi, p, grid, block, split, ctr, parts); return true;
+    case 4: check_tiled<BK, NWAVE, BM, false, 2>(epi, p, grid, block, split, ctr, parts); return true;
   }
   return false;
 }
 
-void on_tiled(const std::vector<int> &t, const tpmlp::GemmArgs &p, unsigned grid, unsigned block) {
-  // <EPI, ACT, BK, NST, NWAVE, BM, LAY>
-  if (t.size() != 7) {
+void on_tiled(const std::vector<int> &t, void **args, unsigned grid, unsigned block) {
+  // <EPI, ACT, BK, NST, NWAVE, BM, LAY, SPLIT>(GemmArgs, ctr, parts)
+  const tpmlp::GemmArgs &p = *(const tpmlp::GemmArgs *)args[0];
+  const unsigned *ctr = *(unsigned *const *)args[1];
+  const float *parts = *(float *const *)args[2];
+  if (t.size() != 8) {
     finding("cannot read the template arguments");
     return;
   }
   const int epi = t[0], BK = t[2], NWAVE = t[4], BM = t[5], LAY = t[6];
+  const bool split = t[7] != 0;
   if (epi != p.epi || LAY != p.lay) finding("kernel <epi %d, lay %d> launched with args epi %d lay %d", epi, LAY, p.epi, p.lay);
+  if (!split && (ctr || parts)) finding("unsplit launch given a workspace");
   gemm_extents(p, 2);
   bool ok = false;
-  if (BK == 32 && NWAVE == 8 && BM == 256) ok = dispatch_lay<32, 8, 256>(epi, LAY, p, grid, block);
-  else if (BK == 32 && NWAVE == 4 && BM == 256) ok = dispatch_lay<32, 4, 256>(epi, LAY, p, grid, block);
-  else if (BK == 32 && NWAVE == 4 && BM == 128) ok = dispatch_lay<32, 4, 128>(epi, LAY, p, grid, block);
-  else if (BK == 64 && NWAVE == 8 && BM == 256) ok = dispatch_lay<64, 8, 256>(epi, LAY, p, grid, block);
+  if (BK == 32 && NWAVE == 8 && BM == 256) ok = dispatch_lay<32, 8, 256>(epi, LAY, p, grid, block, split, ctr, parts);
+  else if (BK == 32 && NWAVE == 4 && BM == 256) ok = dispatch_lay<32, 4, 256>(epi, LAY, p, grid, block, split, ctr, parts);
+  else if (BK == 32 && NWAVE == 4 && BM == 128) ok = dispatch_lay<32, 4, 128>(epi, LAY, p, grid, block, split, ctr, parts);
+  else if (BK == 64 && NWAVE == 8 && BM == 256) ok = dispatch_lay<64, 8, 256>(epi, LAY, p, grid, block, split, ctr, parts);
   if (!ok) finding("no model for tile configuration BK %d NWAVE %d BM %d", BK, NWAVE, BM);
 }
 
@@ -631,7 +696,7 @@ void on_launch(const char *name, unsigned gx, unsigned gy, unsigned gz, unsigned
   if (by != 1 || bz != 1) finding("block is not one-dimensional");
   if (n.find("gemm_bf16_tiled_kernel") != std::string::npos) {
     if (gy != 1 || gz != 1) finding("grid is not one-dimensional");
-    on_tiled(template_ints(n, "gemm_bf16_tiled_kernel"), *(const tpmlp::GemmArgs *)args[0], gx, bx);
+    on_tiled(template_ints(n, "gemm_bf16_tiled_kernel"), args, gx, bx);
     return;
   }
   ++g_stats.checked_other;

@@ -91,7 +91,7 @@ def test_shard_bounds_errors():
 
 def test_workspace_bytes():
     bf16 = torch.bfloat16
-    # many tokens: tiled path, no workspace
+    # many tokens, many tiles: tiled path, no workspace
     assert tp.tp_workspace_bytes(bf16, "swiglu", 4096, 8192, 28672, 8) == 0
     assert tp.tp_workspace_bytes(torch.float32, "gelu_tanh", 4, 512, 2048, 4) == 0
     # decode shapes split K and need partial sums + arrival counters
@@ -272,9 +272,48 @@ def test_qkv_zero_tokens_and_fp32_alignment():
     assert status_name(qkv(dt=0, T=0, dh=12, ldw=144, ldo=72)) == "TP_OK"
 
 
+# The tiled path's split-K plan, seen through the workspace it needs: the
+# counter area, then one 256 x 256 fp32 partial slot per tile and k-range.
+CTR = 256 << 10
+SLOT = 256 * 256 * 4
+
+
+def test_tiled_split_k_plan():
+    """A many-token GEMM of t <= 120 tiles of 256 rows splits K into
+    S = min(240 // t, 4 (8 when t <= 20), K // 768) k-ranges per tile, if
+    that is 2 or more."""
+    bf16 = torch.bfloat16
+    qkv = lambda *a: tp.tp_qkv_workspace_bytes(bf16, *a)  # noqa: E731
+    # Llama-70B QKV shard, T = 4096: 16 x 5 tiles, 3 k-ranges of d = 8192
+    assert qkv(4096, 8192, 64, 8, 128, 8) == CTR + 80 * 3 * SLOT
+    # T = 2048: 8 x 5 tiles, 4 ranges (6 would fit: at most 4 above 20 tiles)
+    assert qkv(2048, 8192, 64, 8, 128, 8) == CTR + 40 * 4 * SLOT
+    # 4 x 5 tiles: 12 would fit, 8 at most
+    assert qkv(1000, 8192, 8, 1, 128, 1) == CTR + 20 * 8 * SLOT
+    # 120 tiles (4 x 30) split in 2; 121 (11 x 11) not at all
+    assert qkv(1024, 8192, 58, 1, 128, 1) == CTR + 120 * 2 * SLOT
+    assert qkv(2816, 8192, 20, 1, 128, 1) == 0
+    # K: 2 ranges need K >= 1536
+    assert qkv(4096, 3072, 64, 8, 128, 8) == CTR + 80 * 3 * SLOT
+    assert qkv(4096, 1528, 64, 8, 128, 8) == 0
+    assert tp.tp_qkv_workspace_bytes(torch.float32, 4096, 8192, 64, 8, 128, 8) == 0
+    # MLP shard, T = 300, Llama-70B width: column 2 x 28 tiles in 4 ranges,
+    # row 2 x 32 tiles in 3 (K = 3584); the larger of the two
+    mlp = lambda *a: tp.tp_workspace_bytes(bf16, *a)  # noqa: E731
+    assert mlp("swiglu", 300, 8192, 3584, 1) == CTR + 56 * 4 * SLOT
+    # the same shard as one of p = 8 (the simulated launches group 8 x 56
+    # tiles and do not split)
+    assert mlp("swiglu", 300, 8192, 28672, 8) == CTR + 56 * 4 * SLOT
+    # one tile, K = 12296: 8 ranges; the simulated launch groups the 4 shards'
+    # tiles (4 x 8 slots)
+    assert mlp("none", 65, 12296, 1024, 4) == CTR + 4 * 8 * SLOT
+    # the headline shard: 448 and 512 tiles, no split
+    assert mlp("swiglu", 4096, 8192, 28672, 8) == 0
+
+
 def test_qkv_workspace_bytes():
     bf16 = torch.bfloat16
-    assert tp.tp_qkv_workspace_bytes(bf16, 4096, 8192, 64, 8, 128, 8) == 0
+    assert tp.tp_qkv_workspace_bytes(bf16, 4096, 4096, 32, 32, 128, 4) == 0  # 16 x 12 tiles
     for T in (1, 8, 64):
         assert tp.tp_qkv_workspace_bytes(bf16, T, 8192, 64, 8, 128, 8) > 0
     assert tp.tp_qkv_workspace_bytes(torch.float32, 8, 8192, 64, 8, 128, 8) == 0

@@ -67,6 +67,20 @@ def test_qkv_bf16_small(T, d, Hq, Hkv, dh, p, bias, what):
         assert_bf16_close(out, ref, f"QKV shard {i}")
 
 
+def test_qkv_split_k():
+    """Tiled QKV projection with split K: 4 x 5 tiles of 256 rows, d = 8192 in 8
+    k-ranges (rows sampled)."""
+    T, d, Hq, Hkv, dh, p = 1000, 8192, 8, 1, 128, 1
+    X, W, b = small_inputs(T, d, Hq, Hkv, dh, 1300, True)
+    say(f"qkv split-K case T={T} d={d} Hq={Hq} Hkv={Hkv} dh={dh}")
+    out = run_qkv(X, W, Hq, Hkv, dh, 0, p, bqkv=b)
+    rows = sampled_rows(T, 16)
+    ref = oracle.qkv_shard(f64(X[rows]), f64(W), Hq, Hkv, dh, 0, p, bqkv=f64(b))
+    assert_bf16_close(out[rows], ref, "QKV")
+    again = run_qkv(X, W, Hq, Hkv, dh, 0, p, bqkv=b)
+    assert torch.equal(out, again)
+
+
 @pytest.mark.parametrize("T", [5, 64, 300])
 def test_qkv_padded_leading_dimensions(T):
     """Output view with a leading dimension above its width (padding is NaN and

@@ -302,6 +302,61 @@ def test_tiled_256_rows_ragged(T, d, k, act, what):
     assert_bf16_close(Z[rows], Zr, "Z")
 
 
+# Tiled path with split K (few output tiles, long K): S k-ranges per tile meet
+# in the workspace, where the last arriving workgroup sums them in order.
+SPLIT_CASES = [
+    # (T, d, k, p, act, what)
+    (300, 8192, 3584, 1, "swiglu", "column 2 x 28 tiles, 4 k-ranges; row 2 x 32 tiles, 3 k-ranges"),
+    (257, 4104, 2048, 1, "gelu_tanh",
+     "column 2 x 8 tiles, 5 k-ranges (last 776 of 832); row 2 x 17 tiles, 2 k-ranges; bias"),
+    (100, 3080, 512, 1, "relu", "column 1 x 2 tiles, 4 k-ranges (last 680 of 800), bias"),
+    (65, 12296, 1024, 4, "none", "column one tile, 8 k-ranges (last 1320), bias"),
+]
+
+
+@pytest.mark.parametrize("T,d,k,p,act,what", SPLIT_CASES)
+def test_tiled_split_k(T, d, k, p, act, what):
+    sw = act == "swiglu"
+    X, W1, Wu, b1, W2 = synth.small_case(T, d, k, 700 + T, sw, bias=not sw)
+    i = p - 1
+    say(f"split-K case T={T} d={d} k={k} p={p} act={act} i={i}: {what}")
+    Y, Z = run_shard(X, W1, W2, i, p, act, Wu=Wu, b1=b1)
+    rows = sampled_rows(T, 24)
+    Yr, Zr = oracle.mlp_shard(f64(X[rows]), f64(W1), f64(W2), i, p, act,
+                              b1=f64(b1) if b1 is not None else None,
+                              Wu=f64(Wu) if Wu is not None else None)
+    assert_bf16_close(Y[rows], Yr, "Y")
+    assert_bf16_close(Z[rows], Zr, "Z")
+    assert bool(torch.isfinite(Y).all()) and bool(torch.isfinite(Z).all())
+
+
+def test_split_k_workspace_reuse_and_determinism():
+    """One zeroed workspace serves split-K tiled calls of two shapes and a
+    few-token call in between; every call leaves the arrival counters zero, and
+    the same call gives the same bits again."""
+    ws = torch.zeros(96 << 20, dtype=torch.uint8, device=DEV)
+    seq = [(300, 8192, 3584, 1, "swiglu"), (65, 12296, 1024, 4, "none"),
+           (8, 1032, 4096, 2, "swiglu"), (300, 8192, 3584, 1, "swiglu")]
+    data = {}
+    outs = []
+    for T, d, k, p, act in seq:
+        sw = act == "swiglu"
+        if (T, d, k) not in data:
+            data[(T, d, k)] = synth.small_case(T, d, k, 900 + T, sw, bias=not sw)
+        X, W1, Wu, b1, W2 = data[(T, d, k)]
+        need = tp.tp_workspace_bytes(torch.bfloat16, act, T, d, k, p)
+        assert 0 < need <= ws.numel()
+        say(f"split-K reuse T={T} d={d} k={k} p={p} act={act}")
+        Y = torch.empty(T, k // p, dtype=torch.bfloat16, device=DEV)
+        Z = torch.empty(T, d, device=DEV)
+        tp.tp_mlp_shard(dev(X), dev(W1), dev(W2), p - 1, p, Y, Z, act=act, Wu=dev(Wu),
+                        b1=dev(b1), ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:256 << 10].count_nonzero()) == 0
+        outs.append((Y.cpu(), Z.cpu()))
+    assert torch.equal(outs[0][0], outs[3][0]) and torch.equal(outs[0][1], outs[3][1])
+
+
 def test_gpt_gelu_shard_full_size():
     """GPT-style GeLU shard at d = 4096, k/p = 4096 (compact shard), T = 2048."""
     W = synth.WORKLOADS["gpt_gelu_p4"]

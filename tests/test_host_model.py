@@ -125,6 +125,9 @@ def gpu_test_cases():
             out.append(f"shard bf16 {act} {T} {d} {k} {i} {p}" + ("" if act == "swiglu" else " bias=1"))
     for T, d, k, act, _ in gp.TILE256_CASES:
         out.append(f"shard bf16 {act} {T} {d} {k} 0 1" + ("" if act == "swiglu" else " bias=1"))
+    for T, d, k, p, act, _ in gp.SPLIT_CASES:
+        out.append(f"shard bf16 {act} {T} {d} {k} {p - 1} {p}" + ("" if act == "swiglu" else " bias=1"))
+    out.append("qkv bf16 1000 8192 8 1 128 0 1 bias=1")
     for T1, T2, d, k, p, act in gz.CASES:
         for T in (T1, T2):
             out.append(f"noalloc bf16 {act} {T} {d} {k} {p - 1} {p}"
@@ -209,6 +212,22 @@ def test_every_launch_stays_in_bounds(driver):
     assert tiled >= 100 and decode >= 50 and other >= 50, (tiled, decode, other)
 
 
+def test_split_k_launches_are_modelled(driver):
+    """The shapes that split K launch the split instantiation (bool template
+    argument 1), and the model checks them without findings."""
+    from tests import test_gpu_parity as gp
+    lines = [f"shard bf16 {act} {T} {d} {k} {p - 1} {p}" + ("" if act == "swiglu" else " bias=1")
+             for T, d, k, p, act, _ in gp.SPLIT_CASES]
+    lines.append("qkv bf16 4096 8192 64 8 128 5 8")
+    r = run_driver(driver, [x + " kernels=1" for x in lines])
+    out = r.stdout
+    assert re.search(r"DONE cases \d+ failed 0", out), out[-3000:] + r.stderr[-2000:]
+    split = [x for x in out.splitlines()
+             if x.startswith("KERNEL") and "gemm_bf16_tiled_kernel" in x and "Lb1E" in x]
+    # every case has at least one split launch (the column step, or the QKV)
+    assert len(split) >= len(lines), out[-3000:]
+
+
 def test_model_sees_the_last_element(driver):
     """Every buffer two bytes short of its operand's extent: each case must
     report a finding (so an access to an operand's last element is seen)."""
@@ -225,7 +244,8 @@ def test_model_sees_the_last_element(driver):
 # Planted mistakes in a copy of the shared addressing code (the bounds model is
 # rebuilt against the copy; the library itself is untouched): for the tiled
 # GEMM a dropped row check on A, a column check that lets one 16-byte unit past
-# N through, and a tile order that is not a bijection; for the few-token GEMM
+# N through, a tile order that is not a bijection, split-K partial groups that
+# overlap and k-ranges that are not whole k-steps; for the few-token GEMM
 # a dropped token-row check, a weight column check one unit late, and partial
 # slots of half their size.  Each must produce findings.
 MUTANTS = [
@@ -241,6 +261,14 @@ MUTANTS = [
      "const int t = xcd * q + (xcd < r ? xcd : r) + idx;",
      "const int t = xcd * q + idx;",
      ["shard bf16 swiglu 300 264 1024 2 4", "shard bf16 relu 1000 8456 1024 0 1 bias=1"]),
+    ("split-K slot groups overlap", "tiled_geometry.hpp",
+     "* 64 + lane) * 16);",
+     "* 64 + lane) * 8);",
+     ["qkv bf16 1000 8192 8 1 128 0 1 bias=1", "shard bf16 none 65 12296 1024 3 4 bias=1"]),
+    ("split-K k-range not whole steps", "tiled_geometry.hpp",
+     "return (per + BK - 1) / BK * BK;",
+     "return per;",
+     ["shard bf16 none 65 12296 1024 3 4 bias=1", "shard bf16 gelu_tanh 257 4104 2048 0 1 bias=1"]),
     ("few-token rows past M not masked", "decode_geometry.hpp",
      "off = (r < p.M && r < 16 * MB) ? (uint32_t)((r * p.lda + k) * 2) : OOB_OFF;",
      "off = (r < 16 * MB) ? (uint32_t)((r * p.lda + k) * 2) : OOB_OFF;",
