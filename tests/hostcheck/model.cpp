@@ -435,6 +435,7 @@ void on_tiled(const std::vector<int> &t, void **args, unsigned grid, unsigned bl
   if (BK == 32 && NWAVE == 8 && BM == 256) ok = dispatch_lay<32, 8, 256>(epi, LAY, p, grid, block, split, ctr, parts);
   else if (BK == 32 && NWAVE == 4 && BM == 256) ok = dispatch_lay<32, 4, 256>(epi, LAY, p, grid, block, split, ctr, parts);
   else if (BK == 32 && NWAVE == 4 && BM == 128) ok = dispatch_lay<32, 4, 128>(epi, LAY, p, grid, block, split, ctr, parts);
+  else if (BK == 32 && NWAVE == 8 && BM == 128) ok = dispatch_lay<32, 8, 128>(epi, LAY, p, grid, block, split, ctr, parts);
   else if (BK == 64 && NWAVE == 8 && BM == 256) ok = dispatch_lay<64, 8, 256>(epi, LAY, p, grid, block, split, ctr, parts);
   if (!ok) finding("no model for tile configuration BK %d NWAVE %d BM %d", BK, NWAVE, BM);
 }
