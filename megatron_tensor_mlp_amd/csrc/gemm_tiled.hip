@@ -414,6 +414,12 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
   // 8 (v / 4) + 4 (lane / 32) + (v % 4), v = 0..15.
   const int64_t rbase = G::row_base(m0, wm, lane);
   if constexpr (EPI == EPI_F32) {
+    // fp32 outputs that no later GEMM of the path reads back (the row step's
+    // partial, the weight gradients) are stored with the nontemporal hint, so
+    // that they do not displace operands from the caches (measured: row step
+    // 207 -> 203 us, and the next step's column GEMM faster too, its operands
+    // still cached).  The backward's dX, which the next launch accumulates
+    // into, is stored normally.
     float *C = (float *)p.C + g * p.sC;
 #pragma unroll
     for (int f = 0; f < NB; ++f) {
@@ -424,7 +430,12 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_bf16_tiled_kernel(const Ge
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int64_t row = G::out_row(rbase, i, v);
-          if (row < M) C[row * p.ldc + col] = acc[i][f][v];
+          if (row < M) {
+            if constexpr (LAY != LAY_NT)
+              __builtin_nontemporal_store(acc[i][f][v], &C[row * p.ldc + col]);
+            else
+              C[row * p.ldc + col] = acc[i][f][v];
+          }
         }
     }
   } else if constexpr (EPI == EPI_F32_ACC) {
