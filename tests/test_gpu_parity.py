@@ -416,6 +416,38 @@ def test_llama_block_simulated_tp8():
     assert np.array_equal(Z.cpu().numpy(), ref)
 
 
+# Simulated mode whose grouped column launch splits K: (T, d, k, p, act, what)
+SIM_SPLIT_CASES = [
+    (300, 8192, 1024, 4, "gelu_tanh", "4 groups x 2 tiles, 8 k-ranges, bias"),
+    (300, 8192, 2048, 4, "swiglu", "4 groups x 2 x 4 tiles, 4 k-ranges"),
+]
+
+
+@pytest.mark.parametrize("T,d,k,p,act,what", SIM_SPLIT_CASES)
+def test_simulated_split_k(T, d, k, p, act, what):
+    """All p shards as grouped launches whose column step splits K, then the
+    reduction: each shard's Y and the summed Z against the oracle on sampled
+    rows, and Z bit for bit against the left-to-right sum of the partials."""
+    sw = act == "swiglu"
+    X, W1, Wu, b1, W2 = synth.small_case(T, d, k, 1100 + k, sw, bias=not sw)
+    s = k // p
+    say(f"simulated split-K case T={T} d={d} k={k} p={p} act={act}: {what}")
+    Y = torch.empty(p, T, s, dtype=torch.bfloat16, device=DEV)
+    Zp = torch.empty(p, T, d, device=DEV)
+    Z = torch.empty(T, d, device=DEV)
+    tp.tp_mlp_simulated(dev(X), dev(W1), dev(W2), p, Y, Zp, Z, act=act, Wu=dev(Wu), b1=dev(b1))
+    torch.cuda.synchronize()
+    rows = sampled_rows(T, 12)
+    for i in range(p):
+        Yr, Zr = oracle.mlp_shard(f64(X[rows]), f64(W1), f64(W2), i, p, act,
+                                  b1=f64(b1) if b1 is not None else None,
+                                  Wu=f64(Wu) if Wu is not None else None)
+        assert_bf16_close(Y[i][rows], Yr, f"Y_{i}")
+        assert_bf16_close(Zp[i][rows], Zr, f"Z_{i}")
+    ref = oracle.partial_sum_f32([Zp[i].cpu().numpy() for i in range(p)])
+    assert np.array_equal(Z.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("T,ldx", [(300, (1 << 21) - 8), (17, (1 << 23) - 8)])
 def test_largest_supported_leading_dimension(T, ldx):
     """X as a view of a buffer with the largest leading dimension each path

@@ -127,6 +127,8 @@ def gpu_test_cases():
         out.append(f"shard bf16 {act} {T} {d} {k} 0 1" + ("" if act == "swiglu" else " bias=1"))
     for T, d, k, p, act, _ in gp.SPLIT_CASES:
         out.append(f"shard bf16 {act} {T} {d} {k} {p - 1} {p}" + ("" if act == "swiglu" else " bias=1"))
+    for T, d, k, p, act, _ in gp.SIM_SPLIT_CASES:
+        out.append(f"sim bf16 {act} {T} {d} {k} {p}" + ("" if act == "swiglu" else " bias=1"))
     out.append("qkv bf16 1000 8192 8 1 128 0 1 bias=1")
     for T1, T2, d, k, p, act in gz.CASES:
         for T in (T1, T2):
