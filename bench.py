@@ -752,8 +752,8 @@ def main():
                     help="also run one 256 MiB device copy (the reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's shard; runs on more than one GPU are not part of "
-              "this build (the cross-GPU reduction is out of scope).", file=sys.stderr)
+        print("bench.py measures one GPU's shard and runs on one GPU only: the cross-GPU "
+              "reduction is out of scope, so there is nothing to time on more.", file=sys.stderr)
         sys.exit(2)
 
     import torch
