@@ -67,3 +67,21 @@ def test_noalloc_llama_decode_shard():
         say(f"noalloc llama decode T={T}")
         (Yw, Zw), (Yn, Zn) = both(X[:T].contiguous(), Wg, W2, 0, 1, "swiglu", Wu=Wu)
         assert torch.equal(Yn, Yw) and torch.equal(Zn, Zw)
+
+
+def test_noalloc_where_the_workspace_entry_point_splits_k():
+    """A shape whose tiled GEMMs tp_mlp_shard splits K (2 x 28 and 2 x 32 tiles,
+    K = 8192 and 3584): the no-alloc entry point runs them unsplit, so the two
+    agree within the bf16 tolerance, and each matches the oracle (sampled rows)."""
+    T, d, k = 300, 8192, 3584
+    assert tp.tp_workspace_bytes(torch.bfloat16, "swiglu", T, d, k, 1) > 0
+    X, W1, Wu, _, W2 = synth.small_case(T, d, k, 1900, True, False)
+    say(f"noalloc split-K shape T={T} d={d} k={k}")
+    (Yw, Zw), (Yn, Zn) = both(X, W1, W2, 0, 1, "swiglu", Wu=Wu)
+    assert_bf16_close(Yn, Yw, "Y vs workspace entry point")
+    assert_bf16_close(Zn, Zw, "Z vs workspace entry point")
+    rows = [0, 1, 127, 128, 255, 256, 299]
+    Yr, Zr = oracle.mlp_shard(f64(X[rows]), f64(W1), f64(W2), 0, 1, "swiglu", Wu=f64(Wu))
+    for Y, Z in ((Yw, Zw), (Yn, Zn)):
+        assert_bf16_close(Y[rows], Yr, "Y")
+        assert_bf16_close(Z[rows], Zr, "Z")
