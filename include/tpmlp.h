@@ -215,7 +215,12 @@ tp_status tp_mlp_simulated(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_
  * those of the few-token (T <= 64) path, and with more tokens those of a
  * GEMM with too few output tiles to fill the device (at most 120 tiles of 256
  * rows) and K of 1536 or more, whose k-range is split over 2 to 8 workgroups
- * per tile (at most 60 MiB of partials).  It must be zero-filled before its
+ * per tile (at most 60 MiB of partials).  With more than 64 tokens the
+ * workspace is optional: given none (NULL), or fewer bytes than this, those
+ * GEMMs run unsplit -- slower, and their fp32 sums taken in another order, so
+ * the results agree with the split ones within the bf16 tolerance rather than
+ * bit for bit.  With 64 or fewer tokens it is required (TP_ERR_WORKSPACE
+ * otherwise).  It must be zero-filled before its
  * first use; every call leaves its counters zero again, and no entry point
  * writes anything but zeros to the counter area, so one zeroed buffer can be
  * reused by any later call of any entry point on the same stream.  Returns 0

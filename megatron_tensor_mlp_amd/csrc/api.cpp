@@ -233,6 +233,19 @@ tp_status run_gemm(tp_dtype dt, const GemmArgs &a, void *ws, hipStream_t st) {
   return TP_OK;
 }
 
+// The workspace a GEMM needs given the caller's buffer.  The tiled path
+// (more than 64 tokens) splits K only when the buffer holds the partials; with
+// no buffer, or a smaller one, it runs unsplit (a.splitk = 1) and needs none.
+// The few-token path has no unsplit form: its need stands.
+size_t fit_gemm_ws(tp_dtype dt, GemmArgs &a, const void *ws, size_t ws_bytes) {
+  const size_t need = gemm_ws_bytes(dt, a);
+  if (need > 0 && dt == TP_BF16 && a.M > kDecodeMaxT && (!ws || ws_bytes < need)) {
+    a.splitk = 1;
+    return gemm_ws_bytes(dt, a);
+  }
+  return need;
+}
+
 tp_status check_ws(size_t need, void *ws, size_t ws_bytes) {
   if (need == 0) return TP_OK;
   if (!ws || ws_bytes < need)
@@ -678,9 +691,9 @@ tp_status tp_col_linear(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k
   const ColCall c = make_col(dt, act, T, d, k, i, p, X, ldx, W1, ldw1, Wu, ldwu, b1, Y, ldy);
   TRY(validate_col(c));
   if (T == 0) return ok();
-  const GemmArgs a = col_gemm(c, 1, 0);
+  GemmArgs a = col_gemm(c, 1, 0);
   TRY(check_gemm(dt, a));
-  TRY(check_ws(gemm_ws_bytes(dt, a), ws, ws_bytes));
+  TRY(check_ws(fit_gemm_ws(dt, a, ws, ws_bytes), ws, ws_bytes));
   TRY(run_gemm(dt, a, ws, (hipStream_t)stream));
   return ok();
 }
@@ -691,9 +704,9 @@ tp_status tp_row_linear(tp_dtype dt, int64_t T, int64_t d, int64_t k, int32_t i,
   const RowCall r = make_row(dt, T, d, k, i, p, Y, ldy, W2, ldw2, Z, ldz);
   TRY(validate_row(r));
   if (T == 0) return ok();
-  const GemmArgs a = row_gemm(r, 1, 0, 0);
+  GemmArgs a = row_gemm(r, 1, 0, 0);
   TRY(check_gemm(dt, a));
-  TRY(check_ws(gemm_ws_bytes(dt, a), ws, ws_bytes));
+  TRY(check_ws(fit_gemm_ws(dt, a, ws, ws_bytes), ws, ws_bytes));
   TRY(run_gemm(dt, a, ws, (hipStream_t)stream));
   return ok();
 }
@@ -708,10 +721,11 @@ tp_status tp_mlp_shard(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_t k,
   const RowCall r = make_row(dt, T, d, k, i, p, Y, ldy, W2, ldw2, Z, ldz);
   TRY(validate_row(r));
   if (T == 0) return ok();
-  const GemmArgs ac = col_gemm(c, 1, 0), ar = row_gemm(r, 1, 0, 0);
+  GemmArgs ac = col_gemm(c, 1, 0), ar = row_gemm(r, 1, 0, 0);
   TRY(check_gemm(dt, ac));
   TRY(check_gemm(dt, ar));
-  TRY(check_ws(max_sz(gemm_ws_bytes(dt, ac), gemm_ws_bytes(dt, ar)), ws, ws_bytes));
+  TRY(check_ws(max_sz(fit_gemm_ws(dt, ac, ws, ws_bytes), fit_gemm_ws(dt, ar, ws, ws_bytes)), ws,
+               ws_bytes));
   TRY(run_gemm(dt, ac, ws, (hipStream_t)stream));
   TRY(run_gemm(dt, ar, ws, (hipStream_t)stream));
   return ok();
@@ -799,10 +813,11 @@ tp_status tp_mlp_simulated(tp_dtype dt, tp_act act, int64_t T, int64_t d, int64_
   TRY(check_ld("ldz", ldz, d, TP_F32));
   if (b2) TRY(check_ptr("b2", b2));
   if (T == 0) return ok();
-  const GemmArgs ac = col_gemm(c, p, T * s), ar = row_gemm(r, p, T * s, T * d);
+  GemmArgs ac = col_gemm(c, p, T * s), ar = row_gemm(r, p, T * s, T * d);
   TRY(check_gemm(dt, ac));
   TRY(check_gemm(dt, ar));
-  TRY(check_ws(max_sz(gemm_ws_bytes(dt, ac), gemm_ws_bytes(dt, ar)), ws, ws_bytes));
+  TRY(check_ws(max_sz(fit_gemm_ws(dt, ac, ws, ws_bytes), fit_gemm_ws(dt, ar, ws, ws_bytes)), ws,
+               ws_bytes));
   TRY(run_gemm(dt, ac, ws, (hipStream_t)stream));
   TRY(run_gemm(dt, ar, ws, (hipStream_t)stream));
   PartSumArgs ps{};
@@ -933,9 +948,9 @@ tp_status tp_qkv_linear(tp_dtype dt, int64_t T, int64_t d, int32_t Hq, int32_t H
   const QkvCall c = make_qkv(dt, T, d, Hq, Hkv, dh, i, p, X, ldx, Wqkv, ldw, bqkv, QKV, ldo);
   TRY(validate_qkv(c));
   if (T == 0) return ok();
-  const GemmArgs a = qkv_gemm(c);
+  GemmArgs a = qkv_gemm(c);
   TRY(check_gemm(dt, a));
-  TRY(check_ws(gemm_ws_bytes(dt, a), ws, ws_bytes));
+  TRY(check_ws(fit_gemm_ws(dt, a, ws, ws_bytes), ws, ws_bytes));
   TRY(run_gemm(dt, a, ws, (hipStream_t)stream));
   return ok();
 }

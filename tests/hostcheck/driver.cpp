@@ -67,6 +67,7 @@ struct Args {
 
 tp_status run_case(const std::string &op, const Args &a) {
   const int64_t pad = a.o("pad", 0);  // extra elements in every leading dimension
+  const bool nows = a.o("nows", 0) != 0;  // pass no workspace (NULL, 0 bytes)
   if (op == "col" || op == "shard" || op == "noalloc" || op == "train") {
     // <dt> <act> T d k i p
     const tp_dtype dt = parse_dt(a.pos[0]);
@@ -82,7 +83,7 @@ tp_status run_case(const std::string &op, const Args &a) {
     void *b1 = bias ? buf(k * es, "b1") : nullptr;
     void *Y = buf(mat(T, s, ldy, es), "Y");
     if (op == "col") {
-      const size_t wsb = tp_workspace_bytes(dt, act, T, d, k, p);
+      const size_t wsb = nows ? 0 : tp_workspace_bytes(dt, act, T, d, k, p);
       void *ws = wsb ? buf(wsb, "workspace") : nullptr;
       return tp_col_linear(dt, act, T, d, k, i, p, X, ldx, W1, ldw, Wu, ldw, b1, Y, ldy, ws, wsb,
                            nullptr);
@@ -98,7 +99,7 @@ tp_status run_case(const std::string &op, const Args &a) {
     if (op == "noalloc")
       return tp_mlp_shard_noalloc(dt, act, T, d, k, i, p, X, ldx, W1, ldw, Wu, ldw, b1, W2,
                                   d + pad, Y, ldy, Z, ldz, nullptr);
-    const size_t wsb = tp_workspace_bytes(dt, act, T, d, k, p);
+    const size_t wsb = nows ? 0 : tp_workspace_bytes(dt, act, T, d, k, p);
     void *ws = wsb ? buf(wsb, "workspace") : nullptr;
     return tp_mlp_shard(dt, act, T, d, k, i, p, X, ldx, W1, ldw, Wu, ldw, b1, W2, d + pad, Y, ldy,
                         Z, ldz, ws, wsb, nullptr);
@@ -111,7 +112,7 @@ tp_status run_case(const std::string &op, const Args &a) {
     void *Y = buf(mat(T, s, s + pad, es), "Y");
     void *W2 = buf(mat(k, d, d + pad, es), "W2");
     float *Z = (float *)buf(mat(T, d, d + pad, 4), "Z");
-    const size_t wsb = tp_workspace_bytes(dt, TP_ACT_NONE, T, d, k, p);
+    const size_t wsb = nows ? 0 : tp_workspace_bytes(dt, TP_ACT_NONE, T, d, k, p);
     void *ws = wsb ? buf(wsb, "workspace") : nullptr;
     return tp_row_linear(dt, T, d, k, i, p, Y, s + pad, W2, d + pad, Z, d + pad, ws, wsb, nullptr);
   }
@@ -131,7 +132,7 @@ tp_status run_case(const std::string &op, const Args &a) {
     void *Y = buf((size_t)(T * k * es), "Y blocks");
     float *Zp = (float *)buf((size_t)(p * T * d * 4), "Z partials");
     float *Z = (float *)buf(mat(T, d, d + pad, 4), "Z");
-    const size_t wsb = tp_workspace_bytes(dt, act, T, d, k, p);
+    const size_t wsb = nows ? 0 : tp_workspace_bytes(dt, act, T, d, k, p);
     void *ws = wsb ? buf(wsb, "workspace") : nullptr;
     return tp_mlp_simulated(dt, act, T, d, k, p, X, d + pad, W1, k + pad, Wu, k + pad, b1, W2,
                             d + pad, b2, Y, Zp, Z, d + pad, ws, wsb, nullptr);
@@ -148,7 +149,7 @@ tp_status run_case(const std::string &op, const Args &a) {
     void *W = buf(mat(d, n, n + pad, es), "Wqkv");
     void *b = a.o("bias", 0) ? buf(n * es, "bqkv") : nullptr;
     void *O = buf(mat(T, w, w + pad, es), "QKV");
-    const size_t wsb = tp_qkv_workspace_bytes(dt, T, d, Hq, Hkv, dh, p);
+    const size_t wsb = nows ? 0 : tp_qkv_workspace_bytes(dt, T, d, Hq, Hkv, dh, p);
     void *ws = wsb ? buf(wsb, "workspace") : nullptr;
     return tp_qkv_linear(dt, T, d, Hq, Hkv, dh, i, p, X, d + pad, W, n + pad, b, O, w + pad, ws,
                          wsb, nullptr);

@@ -330,6 +330,40 @@ def test_tiled_split_k(T, d, k, p, act, what):
     assert bool(torch.isfinite(Y).all()) and bool(torch.isfinite(Z).all())
 
 
+def test_tiled_without_workspace_runs_unsplit():
+    """With more than 64 tokens the split-K workspace is optional: given too
+    little, the tiled GEMMs run unsplit and still match the oracle (and the
+    split result within the bf16 tolerance); with 64 or fewer tokens a missing
+    workspace is an error and nothing is written."""
+    T, d, k = 300, 8192, 3584
+    X, W1, Wu, _, W2 = synth.small_case(T, d, k, 1700, True, False)
+    tiny = torch.zeros(16, dtype=torch.uint8, device=DEV)
+    outs = []
+    for ws in (tiny, None):  # unsplit, then split (the binding sizes the workspace)
+        say(f"tiled T={T} d={d} k={k} with {'a 16-byte' if ws is not None else 'a full'} workspace")
+        Y = torch.full((T, k), float("nan"), dtype=torch.bfloat16, device=DEV)
+        Z = torch.full((T, d), float("nan"), device=DEV)
+        tp.tp_mlp_shard(dev(X), dev(W1), dev(W2), 0, 1, Y, Z, act="swiglu", Wu=dev(Wu), ws=ws)
+        torch.cuda.synchronize()
+        outs.append((Y, Z))
+    rows = sampled_rows(T, 16)
+    Yr, Zr = oracle.mlp_shard(f64(X[rows]), f64(W1), f64(W2), 0, 1, "swiglu", Wu=f64(Wu))
+    for Y, Z in outs:
+        assert_bf16_close(Y[rows], Yr, "Y")
+        assert_bf16_close(Z[rows], Zr, "Z")
+    assert_bf16_close(outs[0][0], outs[1][0], "Y unsplit vs split")
+    assert_bf16_close(outs[0][1], outs[1][1], "Z unsplit vs split")
+
+    Xs, W1s, Wus, _, W2s = synth.small_case(8, 1032, 4096, 1701, True, False)
+    Y = torch.full((8, 2048), 7.0, dtype=torch.bfloat16, device=DEV)
+    Z = torch.full((8, 1032), 7.0, device=DEV)
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_mlp_shard(dev(Xs), dev(W1s), dev(W2s), 1, 2, Y, Z, act="swiglu", Wu=dev(Wus), ws=tiny)
+    assert e.value.name == "TP_ERR_WORKSPACE"
+    torch.cuda.synchronize()
+    assert bool((Y == 7.0).all()) and bool((Z == 7.0).all())
+
+
 def test_split_k_workspace_reuse_and_determinism():
     """One zeroed workspace serves split-K tiled calls of two shapes and a
     few-token call in between; every call leaves the arrival counters zero, and

@@ -173,6 +173,11 @@ EXTRA = [
     "bwd bf16 swiglu 4096 8192 28672 7 8",
     "bwd bf16 gelu_tanh 300 264 1024 3 4 db1=1 pad=8",
     "block swiglu 1 512 8192 64 8 128 28672 8 1 inplace=1",
+    "shard bf16 swiglu 300 8192 3584 0 1 nows=1",     # no workspace: the tiled GEMMs run unsplit
+    "col bf16 gelu_tanh 257 4104 2048 0 1 bias=1 nows=1",
+    "row bf16 300 8192 3584 0 1 nows=1",
+    "qkv bf16 1000 8192 8 1 128 0 1 bias=1 nows=1",
+    "sim bf16 swiglu 300 8192 2048 4 nows=1",
     "shard bf16 swiglu 300 264 1024 2 4 pad=8",       # padded leading dimensions
     "shard bf16 gelu_erf 17 264 1024 0 4 bias=1 pad=16",
     "qkv bf16 300 264 8 2 64 1 2 bias=1 pad=8",
@@ -196,6 +201,7 @@ EXTRA = [
     "! qkv bf16 10 264 8 3 64 0 2",                   # Hkv % p != 0
     "! block swiglu 1 16 24 4 2 96 64 2 1",           # dh neither 64 nor 128
     "! noalloc bf16 swiglu 64 8192 65536 0 1",        # partials beyond the static scratch
+    "! shard bf16 swiglu 64 8192 28672 0 8 nows=1",   # few tokens: the workspace is required
 ]
 
 
